@@ -1,0 +1,298 @@
+"""Benchmark of the WTConv layer on one MI355X: forward + input gradient + weight
+gradients per step, on synthetic WTConvNeXt-shaped tensors.
+
+    python bench.py [--steps K] [--warmup W] [--workload stage1] [--gpus 1]
+
+Prints one JSON line.  `value` is the step's algorithmic HBM bytes (the sum over
+its kernel launches, see memory_bound_depthwise_amd/traffic.py) divided by the
+measured step time, in GB/s; `ms_per_step` is the time of one forward + backward.
+Inputs are resident in device memory before the timed region; `--rotate` buffer
+sets (default 3) are cycled so consecutive steps do not find their inputs in the
+256 MB last-level cache.
+
+The `roofline` object covers the kernel family with the largest share of the step
+time, timed with hipEvents the library records around each launch on its launch
+stream; `cpu_baseline` times the float64 CPU oracle on a bounded sample.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+METRIC = "WTConv layer fwd+bwd ms and achieved HBM GB/s (% of 8 TB/s), 1 GPU"
+HBM_PEAK_GBS = 8000.0
+# Single-issue v_fma_f32: 256 CUs x 4 SIMDs x 16 lanes x 2 FLOP x 2.4 GHz.  The
+# 157.3 TFLOP/s vector figure counts packed FP32, which this library does not use.
+ALU_PEAK_TFLOPS = 78.6
+
+WORKLOADS = {
+    "stage1": ["stage1"], "stage2": ["stage2"], "stage3": ["stage3"],
+    "hires_L1": ["hires_L1"], "hires_L2": ["hires_L2"], "hires_L3": ["hires_L3"],
+    "hires_L4": ["hires_L4"], "hires_L5": ["hires_L5"],
+    "stack": ["stack_1", "stack_2", "stack_3", "stack_4"],
+    "tiny": ["tiny"],
+}
+
+
+def describe(cases):
+    parts = [f"x[{c.n},{c.c},{c.h},{c.w}] {c.dtype} k={c.k} L={c.levels}" for c in cases]
+    return "; ".join(parts)
+
+
+def source_digest():
+    h = hashlib.sha256()
+    csrc = os.path.join(ROOT, "memory_bound_depthwise_amd", "csrc")
+    for name in sorted(os.listdir(csrc)):
+        with open(os.path.join(csrc, name), "rb") as f:
+            h.update(name.encode() + f.read())
+    return h.hexdigest()[:16]
+
+
+class Layer:
+    """Device tensors of one layer: `rotate` sets of (x, dy, y, dx) plus parameters,
+    gradient outputs and one workspace, all allocated before timing."""
+
+    def __init__(self, case, rotate, torch, wt):
+        from synthetic import normal
+        self.case = case
+        dt = torch.bfloat16 if case.dtype == "bf16" else torch.float32
+        dev = "cuda"
+        self.sets = []
+        for r in range(rotate):
+            if r == 0:
+                x, dy = case.x(), case.dy()
+            else:  # distinct data per set, same distribution
+                x = normal(case.seed + r, f"{case.name}/x", (case.n, case.c, case.h, case.w), case.x_std)
+                dy = normal(case.seed + r, f"{case.name}/dy", (case.n, case.c, case.h, case.w), case.dy_std)
+            tx = torch.from_numpy(x).to(dev).to(dt)
+            tdy = torch.from_numpy(dy).to(dev).to(dt)
+            self.sets.append((tx, tdy, torch.empty_like(tx), torch.empty_like(tx)))
+        self.p = {k: torch.from_numpy(v).to(dev) for k, v in case.params().items()}
+        C, k, L = case.c, case.k, case.levels
+        f32 = torch.float32
+        self.grads = {"dw0": torch.empty((C, k, k), dtype=f32, device=dev),
+                      "db0": torch.empty((C,), dtype=f32, device=dev),
+                      "ds0": torch.empty((C,), dtype=f32, device=dev),
+                      "dwl": torch.empty((L, C, 4, k, k), dtype=f32, device=dev),
+                      "dsl": torch.empty((L, C, 4), dtype=f32, device=dev)}
+        desc = wt.make_desc(case.n, case.c, case.h, case.w, k, L, wt.BF16 if case.dtype == "bf16" else wt.F32)
+        nbytes = max(wt.wtconv_workspace_size(desc, op) for op in range(3))
+        self.ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
+
+    def forward(self, i, wt):
+        x, _, y, _ = self.sets[i % len(self.sets)]
+        p, L = self.p, self.case.levels
+        wt.wtconv_forward(x, p["w0"], p["b0"], p["s0"], p["wl"], p["sl"], L, out=y, workspace=self.ws)
+
+    def backward(self, i, wt):
+        x, dy, _, dx = self.sets[i % len(self.sets)]
+        p, L = self.p, self.case.levels
+        wt.wtconv_backward_input(dy, p["w0"], p["s0"], p["wl"], p["sl"], L, out=dx, workspace=self.ws)
+        wt.wtconv_backward_weight(x, dy, p["w0"], p["b0"], p["s0"], p["wl"], p["sl"], L, out=self.grads,
+                                  workspace=self.ws)
+
+
+def run_step(layers, i, wt):
+    for layer in layers:
+        layer.forward(i, wt)
+    for layer in reversed(layers):
+        layer.backward(i, wt)
+
+
+def cpu_baseline(cases, budget_s, model_bytes_fn):
+    """Time the float64 CPU oracle (forward + backward) on the first planes of each
+    layer's batch, growing the sample until it takes about budget_s / 4 seconds or
+    covers the whole batch.  Returns the oracle's rate in the same units as the GPU
+    value (algorithmic bytes of the sampled work per second)."""
+    import oracle
+    from synthetic import Case
+    total_s, total_bytes, samples, frac_full = 0.0, 0.0, [], []
+    for case in cases:
+        ns = 1
+        while True:
+            sub = Case(ns, case.c, case.h, case.w, case.k, case.levels, case.dtype, case.seed,
+                       case.x_std, case.dy_std, case.w_std, case.b_std, case.s_low, case.s_high, case.name)
+            x, dy, p = sub.x(), sub.dy(), sub.params()
+            q = {k: v.astype("float64") for k, v in p.items()}
+            t0 = time.perf_counter()
+            oracle.forward(x.astype("float64"), q, case.levels, case.k)
+            oracle.backward(x.astype("float64"), dy.astype("float64"), q, case.levels, case.k)
+            dt = time.perf_counter() - t0
+            if dt * 2 > budget_s / (4 * len(cases)) or ns >= case.n or ns >= 64:
+                break
+            ns *= 2
+        total_s += dt
+        total_bytes += model_bytes_fn(sub)
+        samples.append(f"{case.name}: n={ns} of {case.n}")
+        frac_full.append(dt * case.n / ns)
+    return {
+        "value": round(total_bytes / total_s / 1e9, 4),
+        "unit": "GB/s",
+        "cores": oracle.threads(),
+        "kind": "oracle",
+        "sample": "; ".join(samples) + " (all channels; forward + backward in float64)",
+        "ms_per_step_extrapolated": round(1e3 * sum(frac_full), 1),
+        "seconds": round(total_s, 2),
+    }
+
+
+def load_traffic(kernel, workload, digest):
+    """HBM bytes per launch from rocprofv3 counters, if measured on this source."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
+    if not os.path.exists(path):
+        return None
+    with open(path) as f:
+        rec = json.load(f)
+    if rec.get("source_digest") != digest:
+        return None
+    return rec.get("bytes_per_launch")
+
+
+def main():
+    ap = argparse.ArgumentParser(description=__doc__)
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="stage1", choices=sorted(WORKLOADS))
+    ap.add_argument("--rotate", type=int, default=3)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-budget", type=float, default=40.0, help="seconds for the oracle leg")
+    ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
+                    help="only run a plain device copy of this many MiB (counter calibration)")
+    args = ap.parse_args()
+
+    if args.gpus != 1:
+        print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
+              f"(the layer has no multi-GPU path in this build)", file=sys.stderr)
+        sys.exit(2)
+
+    import torch
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    torch.cuda.set_device(0)
+
+    if args.copy_probe:
+        n = args.copy_probe * (1 << 20) // 4
+        a = torch.ones(n, dtype=torch.float32, device="cuda")
+        b = torch.empty_like(a)
+        for _ in range(5):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        print(json.dumps({"copy_probe_bytes": 4 * n, "dispatches": 5}), flush=True)
+        return
+
+    import memory_bound_depthwise_amd as wt
+    from memory_bound_depthwise_amd import traffic
+    from synthetic import baseline_cases
+
+    allc = baseline_cases()
+    cases = [allc[name] for name in WORKLOADS[args.workload]]
+    print(f"# bench: {args.workload}: {describe(cases)}", file=sys.stderr, flush=True)
+    layers = [Layer(c, args.rotate, torch, wt) for c in cases]
+    es = lambda c: 2 if c.dtype == "bf16" else 4
+    step_bytes = sum(traffic.step_totals(c.n, c.c, c.h, c.w, c.k, c.levels, es(c))[0] for c in cases)
+    step_flops = sum(traffic.step_totals(c.n, c.c, c.h, c.w, c.k, c.levels, es(c))[1] for c in cases)
+
+    for i in range(args.warmup):
+        run_step(layers, i, wt)
+    torch.cuda.synchronize()
+
+    # timed region: exactly `steps` steps, synchronised on both sides
+    stream = torch.cuda.current_stream()
+    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    ev0.record(stream)
+    for i in range(args.steps):
+        run_step(layers, i, wt)
+    ev1.record(stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3
+    gpu_ms = ev0.elapsed_time(ev1)
+    ms_per_step = max(wall_ms, gpu_ms) / args.steps
+    print(f"# timed {args.steps} steps: {ms_per_step:.4f} ms/step", file=sys.stderr, flush=True)
+
+    # per-kernel durations: the same steps again with the library's event pairs
+    wt.profile_begin()
+    for i in range(args.steps):
+        run_step(layers, i, wt)
+    torch.cuda.synchronize()
+    kstats = wt.profile_end()
+
+    # algorithmic bytes / flops per kernel family (summed over layers and passes)
+    fam = {}
+    for c in cases:
+        for name, _pass, b, f in traffic.launches(c.n, c.c, c.h, c.w, c.k, c.levels, es(c)):
+            key = f"{name}<{c.k},{c.dtype}>"
+            d = fam.setdefault(key, {"bytes": 0, "flops": 0, "launches": 0})
+            d["bytes"] += b
+            d["flops"] += f
+            d["launches"] += 1
+    kernels = []
+    for s in kstats:
+        d = fam.get(s["name"], {"bytes": 0, "flops": 0, "launches": 1})
+        per_step_launches = d["launches"]
+        avg_ms = s["total_ms"] / s["count"]
+        per_launch_bytes = d["bytes"] / per_step_launches
+        per_launch_flops = d["flops"] / per_step_launches
+        kernels.append({
+            "kernel": s["name"], "launches_per_step": per_step_launches,
+            "avg_ms": round(avg_ms, 5), "ms_per_step": round(s["total_ms"] / args.steps, 5),
+            "bytes_per_launch": per_launch_bytes, "flops_per_launch": per_launch_flops,
+            "gbs": round(per_launch_bytes / (avg_ms * 1e-3) / 1e9, 1) if avg_ms > 0 else None,
+            "tflops": round(per_launch_flops / (avg_ms * 1e-3) / 1e12, 2) if avg_ms > 0 else None,
+        })
+    kernels.sort(key=lambda k: -k["ms_per_step"])
+    dom = kernels[0]
+    t_hbm = dom["bytes_per_launch"] / (HBM_PEAK_GBS * 1e9)
+    t_alu = dom["flops_per_launch"] / (ALU_PEAK_TFLOPS * 1e12)
+    digest = source_digest()
+    if t_hbm >= t_alu:
+        roof = {"bound": "hbm", "achieved": dom["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                "frac": round(dom["gbs"] / HBM_PEAK_GBS, 4)}
+    else:
+        roof = {"bound": "alu", "achieved": dom["tflops"], "peak": ALU_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(dom["tflops"] / ALU_PEAK_TFLOPS, 4)}
+    roof["kernel"] = dom["kernel"]
+    roof["avg_launch_ms"] = dom["avg_ms"]
+    roof["traffic"] = load_traffic(dom["kernel"].split("<")[0], args.workload, digest)
+
+    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": cases[0].dtype,
+        "data": "synthetic",
+        "config": {"workload": args.workload, "shapes": describe(cases), "pass": "forward + dx + dW",
+                   "rotate_buffer_sets": args.rotate, "step_bytes": step_bytes, "step_flops": step_flops},
+        "hbm_frac": round(value / HBM_PEAK_GBS, 4),
+        "source_digest": digest,
+        "kernels": kernels,
+        "roofline": roof,
+    }
+    if not args.no_cpu_baseline:
+        def sample_bytes(c):
+            return traffic.step_totals(c.n, c.c, c.h, c.w, c.k, c.levels, es(c))[0]
+        print("# cpu baseline (oracle) ...", file=sys.stderr, flush=True)
+        result["cpu_baseline"] = cpu_baseline(cases, args.cpu_budget, sample_bytes)
+    print(json.dumps(result), flush=True)
+
+
+if __name__ == "__main__":
+    main()
