@@ -19,8 +19,10 @@ def test_table1_and_eq3(golden_dir):
     assert traffic.paper_macs(5, 1) == pytest.approx(g["k5_L1_macs_per_n"], abs=1e-9)
     assert 2 * traffic.paper_macs(5, 5) == pytest.approx(g["k5_L5_flops_per_n"], abs=0.05)
     assert 4 * traffic.paper_q_ref(5) == pytest.approx(g["k5_L5_ref_bytes_per_n_fp32"], abs=0.05)
+    # Eq. 4 divides the printed 137.9N FLOP by 85.3N bytes (= 1.617) and states the
+    # result as "about 1.63"; the pin allows for that rounding.
     assert 2 * traffic.paper_macs(5, 5) / (4 * traffic.paper_q_ref(5)) == pytest.approx(
-        g["ref_intensity_fp32"], abs=0.005)
+        g["ref_intensity_fp32"], abs=0.015)
 
 
 def test_launch_model_counts():
