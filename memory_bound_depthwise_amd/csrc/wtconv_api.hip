@@ -138,12 +138,16 @@ Tiling pick_tiling(Kind kind, int K, int n, int C, int Ho, int Wo) {
     t.tiles_x = cdiv(Wo, 64);
     t.TX = cdiv(Wo, t.tiles_x);
     t.SP = cdiv(t.TX, S);
-    const int ty_max = std::max(1, kTargetItems / t.SP);
-    const int tiles_y = cdiv(Ho, ty_max);
-    t.TY = cdiv(Ho, tiles_y);
-    t.tiles = tiles_y * t.tiles_x;
-    t.PB = std::max(1, std::min(n, kTargetItems / std::max(1, t.TY * t.SP)));
-    while (t.PB > 1 && lds_bytes(kind, K, t.PB, t.TY, t.SP) > kLdsBudget) --t.PB;
+    int ty_max = std::max(1, kTargetItems / t.SP);
+    for (;;) {
+        const int tiles_y = cdiv(Ho, ty_max);
+        t.TY = cdiv(Ho, tiles_y);
+        t.tiles = tiles_y * t.tiles_x;
+        t.PB = std::max(1, std::min(n, kTargetItems / std::max(1, t.TY * t.SP)));
+        while (t.PB > 1 && lds_bytes(kind, K, t.PB, t.TY, t.SP) > kLdsBudget) --t.PB;
+        if (ty_max == 1 || lds_bytes(kind, K, t.PB, t.TY, t.SP) <= kLdsBudget) break;
+        ty_max = std::max(1, ty_max / 2);  // one plane's tile is still too tall
+    }
     if (kind == Kind::LevelFwd || kind == Kind::Synth) {
         t.NB = t.PB;
     } else {
