@@ -107,38 +107,47 @@ def run_step(layers, i, wt):
 
 
 def cpu_baseline(cases, budget_s, model_bytes_fn):
-    """Time the float64 CPU oracle (forward + backward) on the first planes of each
-    layer's batch, growing the sample until it takes about budget_s / 4 seconds or
-    covers the whole batch.  Returns the oracle's rate in the same units as the GPU
-    value (algorithmic bytes of the sampled work per second)."""
+    """Time the float64 CPU oracle (forward + backward) on a bounded sample of the
+    workload: the first planes of each layer's batch (all channels), grown by
+    doubling until one pass takes about budget_s / 8 or covers the whole batch,
+    then repeated until about budget_s / 2 has run.  Returns the oracle's rate in
+    the GPU value's units (algorithmic bytes of the sampled work per second)."""
     import oracle
     from synthetic import Case
-    total_s, total_bytes, samples, frac_full = 0.0, 0.0, [], []
+    total_s, total_bytes, samples, full_ms = 0.0, 0.0, [], 0.0
+    per_layer = budget_s / len(cases)
     for case in cases:
         ns = 1
         while True:
             sub = Case(ns, case.c, case.h, case.w, case.k, case.levels, case.dtype, case.seed,
                        case.x_std, case.dy_std, case.w_std, case.b_std, case.s_low, case.s_high, case.name)
-            x, dy, p = sub.x(), sub.dy(), sub.params()
+            x, dy, p = sub.x().astype("float64"), sub.dy().astype("float64"), sub.params()
             q = {k: v.astype("float64") for k, v in p.items()}
             t0 = time.perf_counter()
-            oracle.forward(x.astype("float64"), q, case.levels, case.k)
-            oracle.backward(x.astype("float64"), dy.astype("float64"), q, case.levels, case.k)
+            oracle.forward(x, q, case.levels, case.k)
+            oracle.backward(x, dy, q, case.levels, case.k)
             dt = time.perf_counter() - t0
-            if dt * 2 > budget_s / (4 * len(cases)) or ns >= case.n or ns >= 64:
+            if dt > per_layer / 8 or ns >= case.n:
                 break
-            ns *= 2
-        total_s += dt
-        total_bytes += model_bytes_fn(sub)
-        samples.append(f"{case.name}: n={ns} of {case.n}")
-        frac_full.append(dt * case.n / ns)
+            ns = min(case.n, 2 * ns)
+        reps, spent = 1, dt
+        while spent < per_layer / 2:
+            t0 = time.perf_counter()
+            oracle.forward(x, q, case.levels, case.k)
+            oracle.backward(x, dy, q, case.levels, case.k)
+            spent += time.perf_counter() - t0
+            reps += 1
+        total_s += spent
+        total_bytes += reps * model_bytes_fn(sub)
+        samples.append(f"{case.name}: n={ns} of {case.n}, {reps} passes")
+        full_ms += 1e3 * spent / reps * case.n / ns
     return {
         "value": round(total_bytes / total_s / 1e9, 4),
         "unit": "GB/s",
         "cores": oracle.threads(),
         "kind": "oracle",
         "sample": "; ".join(samples) + " (all channels; forward + backward in float64)",
-        "ms_per_step_extrapolated": round(1e3 * sum(frac_full), 1),
+        "ms_per_step_extrapolated": round(full_ms, 1),
         "seconds": round(total_s, 2),
     }
 
@@ -163,7 +172,7 @@ def main():
     ap.add_argument("--workload", default="stage1", choices=sorted(WORKLOADS))
     ap.add_argument("--rotate", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-budget", type=float, default=40.0, help="seconds for the oracle leg")
+    ap.add_argument("--cpu-budget", type=float, default=30.0, help="seconds for the oracle leg")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
                     help="only run a plain device copy of this many MiB (counter calibration)")
     args = ap.parse_args()
