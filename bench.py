@@ -153,15 +153,16 @@ def cpu_baseline(cases, budget_s, model_bytes_fn):
 
 
 def load_traffic(kernel, workload, digest):
-    """HBM bytes per launch from rocprofv3 counters, if measured on this source."""
-    path = os.path.join(ROOT, "profiles", f"traffic_{kernel}_{workload}.json")
+    """HBM bytes per launch (fetch + write) of `kernel` from the rocprofv3 counter
+    record of this workload, if the counters were taken on this kernel source."""
+    path = os.path.join(ROOT, "profiles", f"traffic_{workload}.txt")
     if not os.path.exists(path):
         return None
     with open(path) as f:
         rec = json.load(f)
     if rec.get("source_digest") != digest:
         return None
-    return rec.get("bytes_per_launch")
+    return rec.get("kernels", {}).get(kernel)
 
 
 def main():
@@ -240,7 +241,8 @@ def main():
     fam = {}
     for c in cases:
         for name, _pass, b, f in traffic.launches(c.n, c.c, c.h, c.w, c.k, c.levels, es(c)):
-            key = f"{name}<{c.k},{c.dtype}>"
+            fam_name, _, lvl = name.partition("#")
+            key = f"{fam_name}<{c.k},{c.dtype}>" + (f"#{lvl}" if lvl else "")
             d = fam.setdefault(key, {"bytes": 0, "flops": 0, "launches": 0})
             d["bytes"] += b
             d["flops"] += f
@@ -272,7 +274,7 @@ def main():
                 "frac": round(dom["tflops"] / ALU_PEAK_TFLOPS, 4)}
     roof["kernel"] = dom["kernel"]
     roof["avg_launch_ms"] = dom["avg_ms"]
-    roof["traffic"] = load_traffic(dom["kernel"].split("<")[0], args.workload, digest)
+    roof["traffic"] = load_traffic(dom["kernel"], args.workload, digest)
 
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     result = {

@@ -135,7 +135,7 @@ int wtconv_version(void);
  * count written to *n_entries) and switches profiling off.  Not meant to be
  * used from several threads at once. */
 typedef struct wtconv_kernel_time {
-    char name[64];   /* kernel family, k and dtype, e.g. "level_fwd<5,bf16>" */
+    char name[64];   /* kernel family, k, dtype and level, e.g. "level_fwd<5,bf16>#1" */
     int32_t count;   /* launches recorded */
     double total_ms; /* sum of event-to-event durations */
     double min_ms, max_ms;

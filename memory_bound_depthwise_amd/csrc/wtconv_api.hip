@@ -20,6 +20,7 @@
 #include <vector>
 
 #include "wtconv.h"
+#include "wtconv_fused.hpp"
 #include "wtconv_kernels.hpp"
 
 namespace wtc {
@@ -27,7 +28,6 @@ namespace {
 
 constexpr int kThreads = 256;
 constexpr size_t kLdsBudget = 64 * 1024;   // bytes of LDS per workgroup we allow
-constexpr int kTargetItems = 256;          // strips per workgroup pass
 constexpr int kDwTargetBlocks = 2048;      // workgroups wanted for the gradient kernels
 constexpr size_t kAlign = 256;
 
@@ -60,7 +60,7 @@ hipEvent_t pooled_event() {
 }
 
 template <typename Kern, typename Args>
-int launch(const char *family, int K, int is_bf16, Kern kern, dim3 grid, dim3 block, size_t shmem,
+int launch(const char *family, int K, int is_bf16, int level, Kern kern, dim3 grid, dim3 block, size_t shmem,
            hipStream_t stream, const Args &args) {
     if (grid.x == 0 || grid.y == 0) return WTCONV_OK;
     hipEvent_t ev0 = nullptr, ev1 = nullptr;
@@ -79,7 +79,10 @@ int launch(const char *family, int K, int is_bf16, Kern kern, dim3 grid, dim3 bl
     if (prof) {
         (void)hipEventRecord(ev1, stream);
         char name[64];
-        snprintf(name, sizeof(name), "%s<%d,%s>", family, K, is_bf16 ? "bf16" : "f32");
+        if (level > 0)
+            snprintf(name, sizeof(name), "%s<%d,%s>#%d", family, K, is_bf16 ? "bf16" : "f32", level);
+        else
+            snprintf(name, sizeof(name), "%s<%d,%s>", family, K, is_bf16 ? "bf16" : "f32");
         std::lock_guard<std::mutex> lock(g_prof_mu);
         g_prof.push_back({name, ev0, ev1});
     }
@@ -105,49 +108,70 @@ LevelDims level_dims(const wtconv_desc &d) {
     return ld;
 }
 
-// Bytes of LDS a kernel needs for a tiling, as a function of (PB, TY, SP).
+// Bytes of LDS a kernel needs for a tiling (HY rows staged per 8-row strip set
+// plus the K - 1 halo; see the kernels for the layouts).
 enum class Kind { LevelFwd, Synth, DwLevel, DwBase };
 
-int strip_of(Kind k) { return k == Kind::LevelFwd ? 4 : 8; }
-
-size_t lds_bytes(Kind kind, int K, int PB, int TY, int SP) {
-    const int S = strip_of(kind), KK = K * K;
-    const size_t HY = TY + K - 1, HXP = (size_t)SP * S + K - 1, GW = (size_t)SP * S;
+size_t lds_bytes(Kind kind, int K, const Tiling &t) {
+    const int R = (K - 1) / 2, KK = K * K;
+    const size_t PB = t.PB, HY = (size_t)t.SP * kRH + K - 1, HXP = t.TX + K - 1, GY = (size_t)t.SP * kRH;
+    const size_t HXW = stage_width(t.TX, R, t.VW), GW = stage_width(t.TX, 0, t.VW);
     switch (kind) {
-        case Kind::LevelFwd: return (4 * KK + (size_t)PB * 4 * HY * HXP) * sizeof(float);
-        case Kind::Synth: return (KK + (size_t)PB * HY * HXP) * sizeof(float);
-        case Kind::DwLevel:
-            return ((size_t)PB * 4 * HY * HXP + (size_t)PB * 4 * TY * GW + (kThreads / 256) * 4 * KK) * sizeof(float);
-        case Kind::DwBase:
-            return ((size_t)PB * HY * HXP + (size_t)PB * TY * GW + (kThreads / 64) * (KK + 1)) * sizeof(float);
+        case Kind::LevelFwd: return (PB * 4 * HY * HXP + 4 * PB * t.TY * t.TX) * sizeof(float);
+        case Kind::Synth: return (PB * HY * HXW) * sizeof(float);
+        case Kind::DwLevel: return (PB * 4 * HY * HXP + PB * 4 * GY * t.TX + 4 * KK) * sizeof(float);
+        case Kind::DwBase: return (PB * HY * HXW + PB * GY * GW + (kThreads / kWave) * (KK + 1)) * sizeof(float);
     }
     return 0;
 }
 
-// Tile an Ho x Wo output grid: rows of at most 64 columns, about kTargetItems
-// strips per pass, as many planes stacked per pass as that leaves room for (small
-// planes), within the LDS budget.
-Tiling pick_tiling(Kind kind, int K, int n, int C, int Ho, int Wo) {
-    const int S = strip_of(kind);
+// Lanes that work on one item stream: a wavefront per band for the level kernels,
+// the whole workgroup otherwise.
+int lane_group(Kind kind) { return (kind == Kind::LevelFwd || kind == Kind::DwLevel) ? kWave : kThreads; }
+
+// Tile an Ho x Wo output grid.  Tiles are at most 64 columns wide (a full row for
+// the small planes of the WTConvNeXt stages) and as tall as needed for about 4
+// strips per lane group; then as many planes are stacked per pass as give the
+// best lane occupancy within the LDS budget, keeping at least ~2 workgroups per
+// compute unit when the problem allows.
+Tiling pick_tiling(Kind kind, int K, int n, int C, int Ho, int Wo, int VW) {
     Tiling t{};
+    t.VW = VW;
     if (n <= 0 || Ho <= 0 || Wo <= 0) {
         t.TY = t.TX = t.SP = t.tiles_x = t.PB = t.NB = 1;
         t.tiles = t.nblk = 0;
         return t;
     }
+    const int U = lane_group(kind);
     t.tiles_x = cdiv(Wo, 64);
     t.TX = cdiv(Wo, t.tiles_x);
-    t.SP = cdiv(t.TX, S);
-    int ty_max = std::max(1, kTargetItems / t.SP);
+    int sp_max = std::max(1, cdiv(4 * U, t.TX));
     for (;;) {
-        const int tiles_y = cdiv(Ho, ty_max);
+        const int tiles_y = cdiv(Ho, sp_max * kRH);
         t.TY = cdiv(Ho, tiles_y);
+        t.SP = cdiv(t.TY, kRH);
         t.tiles = tiles_y * t.tiles_x;
-        t.PB = std::max(1, std::min(n, kTargetItems / std::max(1, t.TY * t.SP)));
-        while (t.PB > 1 && lds_bytes(kind, K, t.PB, t.TY, t.SP) > kLdsBudget) --t.PB;
-        if (ty_max == 1 || lds_bytes(kind, K, t.PB, t.TY, t.SP) <= kLdsBudget) break;
-        ty_max = std::max(1, ty_max / 2);  // one plane's tile is still too tall
+        t.PB = 1;
+        if (sp_max == 1 || lds_bytes(kind, K, t) <= kLdsBudget) break;
+        sp_max = std::max(1, sp_max / 2);
     }
+    // plane stacking: best lane occupancy, then the smaller PB
+    const long long min_blocks = 512;
+    double best = -1.0;
+    int best_pb = 1;
+    for (int pb = 1; pb <= std::min(n, 64); ++pb) {
+        Tiling c = t;
+        c.PB = pb;
+        if (lds_bytes(kind, K, c) > kLdsBudget) break;
+        if (pb > 1 && (long long)t.tiles * C * cdiv(n, pb) < min_blocks) break;
+        const long long items = (long long)pb * t.SP * t.TX;
+        const double occ = (double)items / (double)(cdiv(items, U) * (long long)U);
+        if (occ > best + 1e-9) {
+            best = occ;
+            best_pb = pb;
+        }
+    }
+    t.PB = best_pb;
     if (kind == Kind::LevelFwd || kind == Kind::Synth) {
         t.NB = t.PB;
     } else {
@@ -163,11 +187,123 @@ Tiling pick_tiling(Kind kind, int K, int n, int C, int Ho, int Wo) {
     return t;
 }
 
-bool tiling_fits(Kind kind, int K, const Tiling &t) {
-    return lds_bytes(kind, K, t.PB, t.TY, t.SP) <= kLdsBudget;
+bool tiling_fits(Kind kind, int K, const Tiling &t) { return lds_bytes(kind, K, t) <= kLdsBudget; }
+
+// Widest vector (elements) for staging rows of length W at pointer p.
+int vec_width(int W, int dtype, const void *p) {
+    int vw = dtype == WTCONV_BF16 ? 8 : 4;
+    const size_t es = dtype == WTCONV_BF16 ? 2 : 4;
+    while (vw > 1 && (W % vw != 0 || ((uintptr_t)p % (vw * es)) != 0)) vw /= 2;
+    return vw;
 }
+int max_vec_width(int dtype) { return dtype == WTCONV_BF16 ? 8 : 4; }
 
 long long grid_of(const Tiling &t, int C) { return (long long)t.tiles * C * t.nblk; }
+
+// ---------------------------------------------------------------------------
+// Plane-resident forward (small planes): LDS layout and plane stacking
+// ---------------------------------------------------------------------------
+
+constexpr int kFusedMaxSide = 64;
+constexpr int kFusedTargetBlocks = 768;  // ~3 workgroups per compute unit
+
+// Layout of one plane block; fills everything but PB / NB / nblk / VE.  The weight
+// table comes first, then the plane blocks, then a tail so that the synthesis
+// reads of rows past the plane (values that are discarded) stay in the allocation.
+bool fused_layout(const wtconv_desc &d, FusedArgs &a) {
+    const int K = d.k, KK = K * K, KKP = (KK + 3) & ~3;
+    if (d.h > kFusedMaxSide || d.w > kFusedMaxSide) return false;
+    a.H = d.h;
+    a.W = d.w;
+    a.L = d.levels;
+    a.hl[0] = d.h;
+    a.wl_[0] = d.w;
+    for (int l = 1; l <= d.levels; ++l) {
+        a.hl[l] = (a.hl[l - 1] + 1) / 2;
+        a.wl_[l] = (a.wl_[l - 1] + 1) / 2;
+    }
+    for (int l = 0; l <= d.levels; ++l) a.sp[l] = cdiv(a.hl[l], kRH);
+    const int wtab_floats = (d.levels * 4 * KKP + 3) & ~3;
+    a.wtab = 0;
+    int off = wtab_floats;
+    a.xoff = off;
+    a.xs = d.w + K - 1;
+    off += (a.sp[0] * kRH + K - 1) * a.xs;
+    int items = 0;
+    for (int l = 0; l < d.levels; ++l) {
+        off = (off + 3) & ~3;
+        a.yb[l] = off;
+        a.sy[l] = a.wl_[l + 1] + K - 1;
+        a.bs[l] = (a.sp[l + 1] * kRH + K - 1) * a.sy[l];
+        off += 4 * a.bs[l];
+        items += 4 * a.sp[l + 1] * a.wl_[l + 1];
+        a.items_end[l] = items;
+    }
+    a.conv_items = items;
+    off = (off + 3) & ~3;
+    a.plane_floats = off - wtab_floats;
+    return true;
+}
+
+int fused_tail_floats(const FusedArgs &a) {
+    const int widest = a.L > 0 ? std::max(a.xs, a.sy[0]) : a.xs;
+    return 4 * widest + 64;
+}
+
+int fused_prefetch_capacity(int dtype, int VE) {
+    // 16 prefetch words per thread, 256 threads
+    const int es = dtype == WTCONV_BF16 ? 2 : 4;
+    const int words_per_vec = (VE * es + 3) / 4;
+    return (16 / words_per_vec) * kThreads * VE;
+}
+
+// Choose PB (planes per pass) and NB (planes per workgroup).  False when the plane
+// is too large for the plane-resident kernel.
+bool plan_fused(const wtconv_desc &d, int VE, FusedArgs &a) {
+    if (d.n <= 0 || d.c <= 0 || d.h <= 0 || d.w <= 0) return false;
+    FusedArgs base{};
+    if (!fused_layout(d, base)) return false;
+    const int wtab_floats = base.xoff;
+    const int tail = fused_tail_floats(base);
+    const long long HW = (long long)d.h * d.w;
+    const int fin = base.sp[0] * d.w;
+    int haar = 0;
+    for (int l = 1; l <= d.levels; ++l) haar += base.hl[l] * base.wl_[l];
+    double best = 1e30;
+    int best_pb = 0;
+    for (int pb = 1; pb <= std::min(d.n, 64); ++pb) {
+        const long long lds = (long long)wtab_floats + (long long)pb * base.plane_floats + tail;
+        if (lds * 4 > (long long)kLdsBudget) break;
+        if ((long long)pb * base.conv_items > (long long)kFusedMaxItems * kThreads) break;
+        if ((long long)pb * fin > (long long)kFusedMaxFinal * kThreads) break;
+        if (pb * HW > fused_prefetch_capacity(d.dtype, VE)) break;
+        // estimated wave-instructions per pass: a conv or final item is 8 K^2 FMAs
+        // (+ synthesis for the final ones), Haar / combine ~15 per position, ~300 fixed
+        const double per_item = 8.0 * d.k * d.k;
+        const double cost = cdiv((long long)pb * base.conv_items, kThreads) * per_item +
+                            cdiv((long long)pb * fin, kThreads) * (per_item + 10.0 * d.levels + 20.0) +
+                            2.0 * cdiv((long long)pb * haar, kThreads) * 15.0 + 300.0;
+        if (cost / pb < best - 1e-9) {
+            best = cost / pb;
+            best_pb = pb;
+        }
+    }
+    if (best_pb == 0) return false;
+    a = base;
+    a.PB = best_pb;
+    a.lds_floats = wtab_floats + best_pb * base.plane_floats + tail;
+    a.VE = VE;
+    // planes per workgroup: a multiple of PB, about kFusedTargetBlocks workgroups
+    const long long passes = cdiv(d.n, a.PB);
+    const long long want_per_chan = std::max<long long>(1, cdiv(kFusedTargetBlocks, d.c));
+    const long long passes_per_wg = std::max<long long>(1, cdiv(passes, want_per_chan));
+    a.NB = (int)(passes_per_wg * a.PB);
+    a.nblk = cdiv(d.n, a.NB);
+    a.n = d.n;
+    a.C = d.c;
+    return true;
+}
+
 
 struct FwdPlan {
     LevelDims ld;
@@ -201,8 +337,9 @@ FwdPlan plan_forward(const wtconv_desc &d) {
         p.c_off[l - 1] = off;
         off = align_up(off + planes * p.ld.H[l] * p.ld.W[l] * es);
     }
-    for (int l = 1; l <= d.levels; ++l) p.lvl[l - 1] = pick_tiling(Kind::LevelFwd, d.k, d.n, d.c, p.ld.H[l], p.ld.W[l]);
-    p.syn = pick_tiling(Kind::Synth, d.k, d.n, d.c, d.h, d.w);
+    for (int l = 1; l <= d.levels; ++l)
+        p.lvl[l - 1] = pick_tiling(Kind::LevelFwd, d.k, d.n, d.c, p.ld.H[l], p.ld.W[l], 1);
+    p.syn = pick_tiling(Kind::Synth, d.k, d.n, d.c, d.h, d.w, max_vec_width(d.dtype));
     p.bytes = off;
     return p;
 }
@@ -220,13 +357,13 @@ DwPlan plan_backward_weight(const wtconv_desc &d) {
     }
     p.part_off = off;
     const int KK = d.k * d.k;
-    p.base = pick_tiling(Kind::DwBase, d.k, d.n, d.c, d.h, d.w);
+    p.base = pick_tiling(Kind::DwBase, d.k, d.n, d.c, d.h, d.w, max_vec_width(d.dtype));
     long long floats = 0;
     p.region[0] = 0;
     p.G[0] = (d.n > 0 && d.h > 0 && d.w > 0) ? p.base.nblk * p.base.tiles : 0;
     floats += (long long)d.c * p.G[0] * (KK + 1);
     for (int l = 1; l <= d.levels; ++l) {
-        p.lvl[l - 1] = pick_tiling(Kind::DwLevel, d.k, d.n, d.c, p.ld.H[l], p.ld.W[l]);
+        p.lvl[l - 1] = pick_tiling(Kind::DwLevel, d.k, d.n, d.c, p.ld.H[l], p.ld.W[l], 1);
         p.region[l] = floats;
         p.G[l] = (d.n > 0 && d.h > 0 && d.w > 0) ? p.lvl[l - 1].nblk * p.lvl[l - 1].tiles : 0;
         floats += (long long)d.c * p.G[l] * 4 * KK;
@@ -274,10 +411,41 @@ bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
 // ---------------------------------------------------------------------------
 
 template <int K, typename T>
+int run_fused_forward(const wtconv_desc &d, FusedArgs a, const void *x, const float *w0, const float *b0,
+                      const float *s0, const float *wl, const float *sl, void *y, hipStream_t st, int rotate) {
+    const int bf = std::is_same<T, uint16_t>::value;
+    a.x = x;
+    a.y = y;
+    a.w0 = w0;
+    a.b0 = b0;
+    a.s0 = s0;
+    a.wl = wl;
+    a.sl = sl;
+    a.rotate = rotate;
+    const dim3 grid((unsigned)((long long)d.c * a.nblk)), block(kThreads);
+    const size_t shm = (size_t)a.lds_floats * sizeof(float);
+    switch (a.VE) {
+        case 8:
+            if constexpr (sizeof(T) == 2)
+                return launch("fused_fwd", K, bf, 0, fused_fwd_kernel<K, T, 8>, grid, block, shm, st, a);
+            return WTCONV_ERR_HIP;
+        case 4: return launch("fused_fwd", K, bf, 0, fused_fwd_kernel<K, T, 4>, grid, block, shm, st, a);
+        case 2: return launch("fused_fwd", K, bf, 0, fused_fwd_kernel<K, T, 2>, grid, block, shm, st, a);
+        default: return launch("fused_fwd", K, bf, 0, fused_fwd_kernel<K, T, 1>, grid, block, shm, st, a);
+    }
+}
+
+template <int K, typename T>
 int run_forward(const wtconv_desc &d, const void *x, const float *w0, const float *b0, const float *s0,
                 const float *wl, const float *sl, void *y, char *ws, hipStream_t st, int rotate) {
+    {
+        FusedArgs fa{};
+        if (plan_fused(d, vec_width(d.w, d.dtype, x), fa))
+            return run_fused_forward<K, T>(d, fa, x, w0, b0, s0, wl, sl, y, st, rotate);
+    }
     const FwdPlan p = plan_forward(d);
     const int bf = std::is_same<T, uint16_t>::value;
+
     const int L = d.levels;
     for (int l = 1; l <= L; ++l) {
         LevelArgs a{};
@@ -294,9 +462,10 @@ int run_forward(const wtconv_desc &d, const void *x, const float *w0, const floa
         a.Wo = p.ld.W[l];
         a.wscale = std::ldexp(1.0f, -(l + 1));
         a.rotate = rotate;
+        a.pairs = (a.Wi % 2 == 0) && ((uintptr_t)a.in % (2 * sizeof(T)) == 0);
         a.t = p.lvl[l - 1];
-        const size_t shm = lds_bytes(Kind::LevelFwd, K, a.t.PB, a.t.TY, a.t.SP);
-        int rc = launch("level_fwd", K, bf, level_fwd_kernel<K, T>, dim3((unsigned)grid_of(a.t, d.c)),
+        const size_t shm = lds_bytes(Kind::LevelFwd, K, a.t);
+        int rc = launch("level_fwd", K, bf, l, level_fwd_kernel<K, T>, dim3((unsigned)grid_of(a.t, d.c)),
                         dim3(kThreads), shm, st, a);
         if (rc) return rc;
     }
@@ -318,8 +487,9 @@ int run_forward(const wtconv_desc &d, const void *x, const float *w0, const floa
     s.L = L;
     s.rotate = rotate;
     s.t = p.syn;
-    const size_t shm = lds_bytes(Kind::Synth, K, s.t.PB, s.t.TY, s.t.SP);
-    return launch("synth", K, bf, synth_kernel<K, T>, dim3((unsigned)grid_of(s.t, d.c)), dim3(kThreads), shm, st,
+    s.t.VW = vec_width(d.w, d.dtype, x);
+    const size_t shm = lds_bytes(Kind::Synth, K, s.t);
+    return launch("synth", K, bf, 0, synth_kernel<K, T>, dim3((unsigned)grid_of(s.t, d.c)), dim3(kThreads), shm, st,
                   s);
 }
 
@@ -345,9 +515,11 @@ int run_backward_weight(const wtconv_desc &d, const void *x, const void *dy, con
             a.Wi = p.ld.W[l - 1];
             a.Ho = p.ld.H[l];
             a.Wo = p.ld.W[l];
+            a.pairs = (a.Wi % 2 == 0) && ((uintptr_t)a.xin % (2 * sizeof(T)) == 0) &&
+                      ((uintptr_t)a.gin % (2 * sizeof(T)) == 0);
             a.t = p.lvl[l - 1];
-            const size_t shm = lds_bytes(Kind::DwLevel, K, a.t.PB, a.t.TY, a.t.SP);
-            int rc = launch("dw_level", K, bf, dw_level_kernel<K, T>, dim3((unsigned)grid_of(a.t, d.c)),
+            const size_t shm = lds_bytes(Kind::DwLevel, K, a.t);
+            int rc = launch("dw_level", K, bf, l, dw_level_kernel<K, T>, dim3((unsigned)grid_of(a.t, d.c)),
                             dim3(kThreads), shm, st, a);
             if (rc) return rc;
         }
@@ -360,8 +532,9 @@ int run_backward_weight(const wtconv_desc &d, const void *x, const void *dy, con
         b.H = d.h;
         b.W = d.w;
         b.t = p.base;
-        const size_t shm = lds_bytes(Kind::DwBase, K, b.t.PB, b.t.TY, b.t.SP);
-        int rc = launch("dw_base", K, bf, dw_base_kernel<K, T>, dim3((unsigned)grid_of(b.t, d.c)), dim3(kThreads),
+        b.t.VW = std::min(vec_width(d.w, d.dtype, x), vec_width(d.w, d.dtype, dy));
+        const size_t shm = lds_bytes(Kind::DwBase, K, b.t);
+        int rc = launch("dw_base", K, bf, 0, dw_base_kernel<K, T>, dim3((unsigned)grid_of(b.t, d.c)), dim3(kThreads),
                         shm, st, b);
         if (rc) return rc;
     }
@@ -383,7 +556,7 @@ int run_backward_weight(const wtconv_desc &d, const void *x, const void *dy, con
     f.ds0 = ds0;
     f.dwl = dwl;
     f.dsl = dsl;
-    return launch("dw_finalize", K, bf, dw_finalize_kernel<K>, dim3((unsigned)d.c, (unsigned)(L + 1)), dim3(128), 0,
+    return launch("dw_finalize", K, bf, 0, dw_finalize_kernel<K>, dim3((unsigned)d.c, (unsigned)(L + 1)), dim3(128), 0,
                   st, f);
 }
 

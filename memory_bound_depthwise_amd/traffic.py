@@ -32,8 +32,9 @@ def level_sizes(h, w, levels):
 
 
 def launches(n, c, h, w, k, levels, elem_bytes):
-    """List of (family, pass, bytes, flops) for one forward + input-gradient +
-    weight-gradient step of one layer, in launch order."""
+    """List of (name, pass, bytes, flops) for one forward + input-gradient +
+    weight-gradient step of one layer, in launch order; per-level kernels are
+    named family#level, as the library's profiling records name them."""
     P = n * c
     N = P * h * w
     E = elem_bytes
@@ -43,13 +44,13 @@ def launches(n, c, h, w, k, levels, elem_bytes):
         for l in range(1, levels + 1):
             blocks = P * hs[l] * ws[l]
             elems = P * hs[l - 1] * ws[l - 1] + 4 * blocks + (blocks if l < levels else 0)
-            out.append(("level_fwd", pass_name, E * elems, blocks * (8 * k * k + 20)))
+            out.append((f"level_fwd#{l}", pass_name, E * elems, blocks * (8 * k * k + 20)))
         q = sum(4 * P * hs[l] * ws[l] for l in range(1, levels + 1))
         out.append(("synth", pass_name, E * (2 * N + q), N * (2 * k * k + levels)))
     for l in range(1, levels + 1):
         blocks = P * hs[l] * ws[l]
         elems = 2 * P * hs[l - 1] * ws[l - 1] + (2 * blocks if l < levels else 0)
-        out.append(("dw_level", "backward_weight", E * elems, blocks * (8 * k * k + 16)))
+        out.append((f"dw_level#{l}", "backward_weight", E * elems, blocks * (8 * k * k + 16)))
     out.append(("dw_base", "backward_weight", E * 2 * N, N * (2 * k * k + 1)))
     out.append(("dw_finalize", "backward_weight", 0, 0))
     return out

@@ -29,7 +29,7 @@ def test_launch_model_counts():
     n, c, h, w, k, L, E = 2, 3, 7, 9, 5, 2, 2
     ls = traffic.launches(n, c, h, w, k, L, E)
     names = [x[0] for x in ls]
-    assert names == ["level_fwd", "level_fwd", "synth"] * 2 + ["dw_level", "dw_level", "dw_base", "dw_finalize"]
+    assert names == ["level_fwd#1", "level_fwd#2", "synth"] * 2 + ["dw_level#1", "dw_level#2", "dw_base", "dw_finalize"]
     P = n * c
     # level 1: reads 7x9, coefficient grid 4x5; writes Q 4*4*5 and carrier 4*5
     assert ls[0][2] == E * P * (7 * 9 + 4 * 20 + 20)
