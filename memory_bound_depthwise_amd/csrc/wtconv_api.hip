@@ -21,6 +21,7 @@
 
 #include "wtconv.h"
 #include "wtconv_fused.hpp"
+#include "wtconv_fused_dw.hpp"
 #include "wtconv_kernels.hpp"
 
 namespace wtc {
@@ -32,6 +33,9 @@ constexpr int kDwTargetBlocks = 2048;      // workgroups wanted for the gradient
 constexpr size_t kAlign = 256;
 
 inline size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
+
+// Multiply-high reciprocal for fdiv (divisor and dividends below 2^16); 0 encodes 1.
+inline uint32_t magic_of(int d) { return d <= 1 ? 0u : (uint32_t)((0x100000000ULL + (uint64_t)d - 1) / (uint64_t)d); }
 inline int cdiv(long long a, long long b) { return (int)((a + b - 1) / b); }
 
 // ---------------------------------------------------------------------------
@@ -226,15 +230,18 @@ bool fused_layout(const wtconv_desc &d, FusedArgs &a) {
     const int wtab_floats = (d.levels * 4 * KKP + 3) & ~3;
     a.wtab = 0;
     int off = wtab_floats;
+    // regions hold the grid plus its halo; the extra rows that the last 8-row strip
+    // reads (only for outputs past the grid, which are discarded) fall in the next
+    // region or in the tail of the allocation
     a.xoff = off;
     a.xs = d.w + K - 1;
-    off += (a.sp[0] * kRH + K - 1) * a.xs;
+    off += (d.h + K - 1) * a.xs;
     int items = 0;
     for (int l = 0; l < d.levels; ++l) {
         off = (off + 3) & ~3;
         a.yb[l] = off;
         a.sy[l] = a.wl_[l + 1] + K - 1;
-        a.bs[l] = (a.sp[l + 1] * kRH + K - 1) * a.sy[l];
+        a.bs[l] = (a.hl[l + 1] + K - 1) * a.sy[l];
         off += 4 * a.bs[l];
         items += 4 * a.sp[l + 1] * a.wl_[l + 1];
         a.items_end[l] = items;
@@ -246,15 +253,19 @@ bool fused_layout(const wtconv_desc &d, FusedArgs &a) {
 }
 
 int fused_tail_floats(const FusedArgs &a) {
-    const int widest = a.L > 0 ? std::max(a.xs, a.sy[0]) : a.xs;
-    return 4 * widest + 64;
+    // Reads for discarded outputs run past a region by at most 8 rows (the last
+    // 8-row strip) or 4 block rows (synthesis); past every region but the last they
+    // land in the next region, past the last one in this tail.
+    const int last = a.L > 0 ? a.sy[a.L - 1] : a.xs;
+    return (kRH + 4) * last + 64;
 }
 
 int fused_prefetch_capacity(int dtype, int VE) {
-    // 16 prefetch words per thread, 256 threads
+    // prefetch words per thread (8 for bf16, 16 for f32), 256 threads
     const int es = dtype == WTCONV_BF16 ? 2 : 4;
+    const int words = dtype == WTCONV_BF16 ? 8 : 16;
     const int words_per_vec = (VE * es + 3) / 4;
-    return (16 / words_per_vec) * kThreads * VE;
+    return (words / words_per_vec) * kThreads * VE;
 }
 
 // Choose PB (planes per pass) and NB (planes per workgroup).  False when the plane
@@ -277,6 +288,7 @@ bool plan_fused(const wtconv_desc &d, int VE, FusedArgs &a) {
         if ((long long)pb * base.conv_items > (long long)kFusedMaxItems * kThreads) break;
         if ((long long)pb * fin > (long long)kFusedMaxFinal * kThreads) break;
         if (pb * HW > fused_prefetch_capacity(d.dtype, VE)) break;
+        if ((long long)pb * d.c * HW >= (1LL << 30)) break;  // 32-bit offsets from a plane base
         // estimated wave-instructions per pass: a conv or final item is 8 K^2 FMAs
         // (+ synthesis for the final ones), Haar / combine ~15 per position, ~300 fixed
         const double per_item = 8.0 * d.k * d.k;
@@ -301,9 +313,114 @@ bool plan_fused(const wtconv_desc &d, int VE, FusedArgs &a) {
     a.nblk = cdiv(d.n, a.NB);
     a.n = d.n;
     a.C = d.c;
+    a.m_hw = magic_of((int)HW);
+    a.m_w = magic_of(d.w);
+    a.m_conv = magic_of(std::max(1, a.conv_items));
+    a.m_fin = magic_of(fin);
+    for (int l = 0; l < d.levels; ++l) {
+        a.m_per[l] = magic_of(a.hl[l + 1] * a.wl_[l + 1]);
+        a.m_wl[l] = magic_of(a.wl_[l + 1]);
+    }
     return true;
 }
 
+
+
+// ---------------------------------------------------------------------------
+// Plane-resident weight gradient of the levels (small planes)
+// ---------------------------------------------------------------------------
+
+constexpr int kFusedDwTargetBlocks = 1024;
+
+// Layout and lane allocation from the shape alone (the prefetch capacity does not
+// depend on the vector width), so that the workspace size is shape-determined.
+bool plan_fused_dw(const wtconv_desc &d, FusedDwArgs &a) {
+    if (d.levels < 1 || d.n <= 0 || d.c <= 0 || d.h <= 0 || d.w <= 0) return false;
+    if (d.h > kFusedMaxSide || d.w > kFusedMaxSide) return false;
+    const int K = d.k, L = d.levels;
+    FusedDwArgs b{};
+    b.H = d.h;
+    b.W = d.w;
+    b.L = L;
+    b.hl[0] = d.h;
+    b.wl_[0] = d.w;
+    for (int l = 1; l <= L; ++l) {
+        b.hl[l] = (b.hl[l - 1] + 1) / 2;
+        b.wl_[l] = (b.wl_[l - 1] + 1) / 2;
+    }
+    for (int l = 0; l <= L; ++l) b.sp[l] = cdiv(b.hl[l], kRH);
+    // regions: x pyramid (halo R, rows trimmed to the grid), then dy pyramid (centre)
+    int off = 0;
+    for (int l = 0; l < L; ++l) {
+        off = (off + 3) & ~3;
+        b.yb[l] = off;
+        b.ys[l] = b.wl_[l + 1] + K - 1;
+        b.ybs[l] = (b.hl[l + 1] + K - 1) * b.ys[l];
+        off += 4 * b.ybs[l];
+    }
+    for (int l = 0; l < L; ++l) {
+        off = (off + 3) & ~3;
+        b.gb[l] = off;
+        b.gbs[l] = b.hl[l + 1] * b.wl_[l + 1];
+        off += 4 * b.gbs[l];
+    }
+    b.plane_floats = (off + 3) & ~3;
+    // reads for discarded rows run up to 8 (+4) rows past the last region
+    const int tail = (kRH + 4) * std::max(b.wl_[L], b.ys[L - 1]) + 64;
+    b.blocks = b.hl[1] * b.wl_[1];
+    const int capacity = d.dtype == WTCONV_BF16 ? 2048 : 1024;  // level-1 blocks prefetched per pass
+    long long per_pair[kMaxLevels];
+    for (int l = 0; l < L; ++l) per_pair[l] = (long long)b.sp[l + 1] * b.wl_[l + 1];
+    const int KK = K * K;
+    double best = 1e30;
+    int best_pb = 0, best_r = 0;
+    for (int pb = 1; pb <= std::min(d.n, 16); ++pb) {
+        const long long lds = std::max<long long>((long long)pb * b.plane_floats + tail, 256LL * 9);
+        if (lds * 4 > (long long)kLdsBudget) break;
+        if ((long long)pb * b.blocks > capacity) break;
+        if ((long long)pb * d.c * d.h * d.w >= (1LL << 30)) break;
+        int r = 1;
+        for (; r <= kDwMaxRounds; ++r) {
+            long long lanes = 0;
+            for (int l = 0; l < L; ++l) lanes += 4 * cdiv(pb * per_pair[l], r);
+            if (lanes <= kThreads) break;
+        }
+        if (r > kDwMaxRounds) continue;
+        // wave-instructions per pass: r rounds of 8 K^2 FMAs (+ ~40), Haar ~300, fixed ~300
+        const double cost = r * (8.0 * KK + 40.0) + 300.0 + 300.0;
+        if (cost / pb < best - 1e-9) {
+            best = cost / pb;
+            best_pb = pb;
+            best_r = r;
+        }
+    }
+    if (best_pb == 0) return false;
+    a = b;
+    a.PB = best_pb;
+    a.rounds = best_r;
+    int lane = 0;
+    for (int l = 0; l < L; ++l)
+        for (int bd = 0; bd < 4; ++bd) {
+            a.lane0[4 * l + bd] = lane;
+            a.lanes[4 * l + bd] = cdiv(best_pb * per_pair[l], best_r);
+            lane += a.lanes[4 * l + bd];
+        }
+    a.lds_floats = (int)std::max<long long>((long long)best_pb * b.plane_floats + tail, 256LL * 9);
+    const long long passes = cdiv(d.n, a.PB);
+    const long long want_per_chan = std::max<long long>(1, cdiv(kFusedDwTargetBlocks, d.c));
+    const long long passes_per_wg = std::max<long long>(1, cdiv(passes, want_per_chan));
+    a.NB = (int)(passes_per_wg * a.PB);
+    a.nblk = cdiv(d.n, a.NB);
+    a.n = d.n;
+    a.C = d.c;
+    a.m_w1 = magic_of(a.wl_[1]);
+    a.m_blocks = magic_of(a.blocks);
+    for (int l = 0; l < L; ++l) {
+        a.m_per[l] = magic_of(a.hl[l + 1] * a.wl_[l + 1]);
+        a.m_wl[l] = magic_of(a.wl_[l + 1]);
+    }
+    return true;
+}
 
 struct FwdPlan {
     LevelDims ld;
@@ -313,6 +430,8 @@ struct FwdPlan {
 };
 
 struct DwPlan {
+    bool fused;          // levels by the plane-resident kernel (no carriers)
+    FusedDwArgs fa;
     LevelDims ld;
     size_t xc_off[kMaxLevels], gc_off[kMaxLevels];
     size_t part_off;                 // byte offset of the partials
@@ -347,13 +466,16 @@ FwdPlan plan_forward(const wtconv_desc &d) {
 DwPlan plan_backward_weight(const wtconv_desc &d) {
     DwPlan p{};
     p.ld = level_dims(d);
+    p.fused = plan_fused_dw(d, p.fa);
     const size_t es = elem_size(d.dtype), planes = (size_t)d.n * d.c;
     size_t off = 0;
-    for (int l = 1; l < d.levels; ++l) {
-        p.xc_off[l - 1] = off;
-        off = align_up(off + planes * p.ld.H[l] * p.ld.W[l] * es);
-        p.gc_off[l - 1] = off;
-        off = align_up(off + planes * p.ld.H[l] * p.ld.W[l] * es);
+    if (!p.fused) {
+        for (int l = 1; l < d.levels; ++l) {
+            p.xc_off[l - 1] = off;
+            off = align_up(off + planes * p.ld.H[l] * p.ld.W[l] * es);
+            p.gc_off[l - 1] = off;
+            off = align_up(off + planes * p.ld.H[l] * p.ld.W[l] * es);
+        }
     }
     p.part_off = off;
     const int KK = d.k * d.k;
@@ -365,7 +487,10 @@ DwPlan plan_backward_weight(const wtconv_desc &d) {
     for (int l = 1; l <= d.levels; ++l) {
         p.lvl[l - 1] = pick_tiling(Kind::DwLevel, d.k, d.n, d.c, p.ld.H[l], p.ld.W[l], 1);
         p.region[l] = floats;
-        p.G[l] = (d.n > 0 && d.h > 0 && d.w > 0) ? p.lvl[l - 1].nblk * p.lvl[l - 1].tiles : 0;
+        if (p.fused)
+            p.G[l] = p.fa.nblk;
+        else
+            p.G[l] = (d.n > 0 && d.h > 0 && d.w > 0) ? p.lvl[l - 1].nblk * p.lvl[l - 1].tiles : 0;
         floats += (long long)d.c * p.G[l] * 4 * KK;
     }
     p.bytes = align_up(off + (size_t)floats * sizeof(float));
@@ -501,8 +626,32 @@ int run_backward_weight(const wtconv_desc &d, const void *x, const void *dy, con
     const int bf = std::is_same<T, uint16_t>::value;
     const int L = d.levels;
     float *partial = reinterpret_cast<float *>(ws + p.part_off);
+    if (!empty(d) && p.fused && L > 0) {
+        FusedDwArgs a = p.fa;
+        a.x = x;
+        a.dy = dy;
+        a.partial = partial;
+        for (int l = 0; l < L; ++l) a.off[l] = p.region[l + 1];
+        const int ve = std::min(vec_width(d.w, d.dtype, x), vec_width(d.w, d.dtype, dy));
+        a.VE = ve >= 2 ? ve : 1;
+        const dim3 grid((unsigned)((long long)d.c * a.nblk)), block(kThreads);
+        const size_t shm = (size_t)a.lds_floats * sizeof(float);
+        int rc;
+        switch (a.VE) {
+            case 8:
+                if constexpr (sizeof(T) == 2) {
+                    rc = launch("fused_dw", K, bf, 0, fused_dw_kernel<K, T, 8>, grid, block, shm, st, a);
+                    break;
+                }
+                return WTCONV_ERR_HIP;
+            case 4: rc = launch("fused_dw", K, bf, 0, fused_dw_kernel<K, T, 4>, grid, block, shm, st, a); break;
+            case 2: rc = launch("fused_dw", K, bf, 0, fused_dw_kernel<K, T, 2>, grid, block, shm, st, a); break;
+            default: rc = launch("fused_dw", K, bf, 0, fused_dw_kernel<K, T, 1>, grid, block, shm, st, a); break;
+        }
+        if (rc) return rc;
+    }
     if (!empty(d)) {
-        for (int l = 1; l <= L; ++l) {
+        for (int l = 1; l <= L && !p.fused; ++l) {
             DwLevelArgs a{};
             a.xin = l == 1 ? x : (const void *)(ws + p.xc_off[l - 2]);
             a.gin = l == 1 ? dy : (const void *)(ws + p.gc_off[l - 2]);

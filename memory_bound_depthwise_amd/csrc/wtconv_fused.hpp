@@ -35,9 +35,24 @@
 
 namespace wtc {
 
-constexpr int kFusedMaxItems = 4;   // conv items per thread per pass
-constexpr int kFusedMaxFinal = 2;   // final-pass items per thread per pass
-constexpr int kFusedRawWords = 16;  // prefetch buffer per thread (32-bit words)
+constexpr int kFusedMaxItems = 3;  // conv items per thread per pass
+constexpr int kFusedMaxFinal = 2;  // final-pass items per thread per pass
+// prefetch buffer per thread (32-bit words)
+template <typename T>
+constexpr int fused_raw_words() { return sizeof(T) == 2 ? 8 : 16; }
+
+// Balanced item-to-thread map: item round k covers items [256 k, 256 k + r_k) and
+// gives each of the four wavefronts a contiguous chunk of ceil(r_k / 4) items, so no
+// wavefront (and no SIMD) carries a whole extra round.  Returns -1 when the thread
+// has no item in round k.
+__device__ __forceinline__ int balanced_item(int total, int k, int tid) {
+    const int first = k * 256, r = min(256, total - first);
+    if (r <= 0) return -1;
+    const int chunk = (r + 3) >> 2, w = tid >> 6, lane = tid & 63;
+    if (lane >= chunk) return -1;
+    const int li = w * chunk + lane;
+    return li < r ? first + li : -1;
+}
 
 struct FusedArgs {
     const void *x;
@@ -58,6 +73,9 @@ struct FusedArgs {
     int items_end[kMaxLevels];  // cumulative conv items per plane, by level (4 bands each)
     int conv_items;             // per plane
     int lds_floats;             // total
+    // multiply-high reciprocals (see fdiv) of the divisors used per element
+    uint32_t m_hw, m_w, m_conv, m_fin;
+    uint32_t m_per[kMaxLevels], m_wl[kMaxLevels];  // level l+1: Hl*Wl and Wl
 };
 
 template <int K>
@@ -75,22 +93,24 @@ __device__ __forceinline__ void conv_strip_dyn(const float *src, int stride, con
 }
 
 // Prefetch of PB planes of x into registers: vector v of the pass covers elements
-// [v VE, v VE + VE) of the concatenated planes; slots are v = tid + k 256.
+// [v VE, v VE + VE) of the concatenated planes; slots are v = tid + k 256.  Global
+// offsets are 32-bit from the uniform base of plane (n0, c); PB C H W < 2^30.
 template <typename T, int VE>
 struct XPrefetch {
+    static constexpr int kRawWords = fused_raw_words<T>();
     static constexpr int kWordsPerVec = (VE * (int)sizeof(T) + 3) / 4;
-    static constexpr int kSlots = kFusedRawWords / kWordsPerVec;
+    static constexpr int kSlots = kRawWords / kWordsPerVec;
 
-    __device__ __forceinline__ static void load(uint32_t *raw, const T *x, int n0, int n_end, int c, int C,
-                                                int HW, int PB, int tid) {
+    __device__ __forceinline__ static void load(uint32_t *raw, const T *xbase, int live_planes, int CHW, int HW,
+                                                uint32_t m_hw, int PB, int tid) {
         const int total = PB * HW / VE;
 #pragma unroll
         for (int k = 0; k < kSlots; ++k) {
             const int v = tid + k * 256;
             if (v >= total) continue;
-            const int e = v * VE, p = e / HW, off = e - p * HW;
-            if (n0 + p >= n_end) continue;
-            const T *src = x + ((size_t)(n0 + p) * C + c) * HW + off;
+            const int e = v * VE, p = fdiv(e, m_hw), off = e - p * HW;
+            if (p >= live_planes) continue;
+            const T *src = xbase + (p * CHW + off);
             uint32_t *r = raw + k * kWordsPerVec;
             if constexpr (sizeof(T) == 2) {
                 if constexpr (VE == 8) {
@@ -131,17 +151,18 @@ struct XPrefetch {
     }
 
     // Write the slots into the x regions of LDS (centre of each plane's region).
-    __device__ __forceinline__ static void commit(const uint32_t *raw, float *smem, int n0, int n_end, int HW,
-                                                  int W, int PB, int plane_floats, int xoff, int xs, int R, int tid) {
+    __device__ __forceinline__ static void commit(const uint32_t *raw, float *smem, int live_planes, int HW,
+                                                  uint32_t m_hw, int W, uint32_t m_w, int PB, int plane_floats,
+                                                  int xoff, int xs, int R, int tid) {
         const int total = PB * HW / VE;
 #pragma unroll
         for (int k = 0; k < kSlots; ++k) {
             const int v = tid + k * 256;
             if (v >= total) continue;
-            const int e = v * VE, p = e / HW, off = e - p * HW;
-            const int row = off / W, col = off - row * W;
+            const int e = v * VE, p = fdiv(e, m_hw), off = e - p * HW;
+            const int row = fdiv(off, m_w), col = off - row * W;
             float *d = smem + p * plane_floats + xoff + (row + R) * xs + col + R;
-            const bool live = n0 + p < n_end;
+            const bool live = p < live_planes;
 #pragma unroll
             for (int t = 0; t < VE; ++t) d[t] = live ? elem(raw, k, t) : 0.f;
         }
@@ -174,9 +195,9 @@ __device__ __forceinline__ void fused_fwd_body(const FusedArgs &a) {
 #pragma unroll
     for (int k = 0; k < kFusedMaxItems; ++k) {
         cd0[k] = cd1[k] = 0;
-        const int it = tid + k * nthr;
-        if (it >= PB * a.conv_items) continue;
-        const int p = it / a.conv_items;
+        const int it = balanced_item(PB * a.conv_items, k, tid);
+        if (it < 0) continue;
+        const int p = fdiv(it, a.m_conv);
         int loc = it - p * a.conv_items, l = 0;
         while (loc >= a.items_end[l]) ++l;
         loc -= l ? a.items_end[l - 1] : 0;
@@ -193,17 +214,18 @@ __device__ __forceinline__ void fused_fwd_body(const FusedArgs &a) {
     const int fin_per_plane = a.sp[0] * W;
 #pragma unroll
     for (int k = 0; k < kFusedMaxFinal; ++k) {
-        const int it = tid + k * nthr;
+        const int it = balanced_item(PB * fin_per_plane, k, tid);
         fd[k] = 0;
-        if (it >= PB * fin_per_plane) continue;
-        const int p = it / fin_per_plane, r = it - p * fin_per_plane, s = r / W, j = r - s * W;
+        if (it < 0) continue;
+        const int p = fdiv(it, a.m_fin), r = it - p * fin_per_plane, s = fdiv(r, a.m_w), j = r - s * W;
         fd[k] = (uint32_t)j | ((uint32_t)s << 8) | ((uint32_t)p << 16) | ((uint32_t)min(kRH, H - s * kRH) << 24);
     }
 
+    const int CHW = a.C * HW;
     const T *x = static_cast<const T *>(a.x);
     T *y = static_cast<T *>(a.y);
-    uint32_t raw[kFusedRawWords];
-    XP::load(raw, x, n_begin, n_end, c, a.C, HW, PB, tid);
+    uint32_t raw[XP::kRawWords];
+    XP::load(raw, x + ((size_t)n_begin * a.C + c) * HW, min(PB, n_end - n_begin), CHW, HW, a.m_hw, PB, tid);
 
     for (int n0 = n_begin; n0 < n_end; n0 += PB) {
         __syncthreads();  // previous pass done with every region
@@ -216,22 +238,26 @@ __device__ __forceinline__ void fused_fwd_body(const FusedArgs &a) {
         for (int k = 0; k < kFusedMaxFinal; ++k) asm volatile("" : "+v"(fd[k]));
         int t = tid;
         asm volatile("" : "+v"(t));
-        XP::commit(raw, smem, n0, n_end, HW, W, PB, PF, a.xoff, a.xs, R, t);
+        const int live = min(PB, n_end - n0);
+        XP::commit(raw, smem, live, HW, a.m_hw, W, a.m_w, PB, PF, a.xoff, a.xs, R, t);
         __syncthreads();
-        if (n0 + PB < n_end) XP::load(raw, x, n0 + PB, n_end, c, a.C, HW, PB, t);
+        if (n0 + PB < n_end)
+            XP::load(raw, x + ((size_t)(n0 + PB) * a.C + c) * HW, min(PB, n_end - n0 - PB), CHW, HW, a.m_hw, PB,
+                     t);
 
         // 2. Haar analysis, unscaled: S_l = butterfly of S_{l-1}'s low-pass band
         for (int l = 0; l < L; ++l) {
             const int Hl = a.hl[l + 1], Wl = a.wl_[l + 1], per = Hl * Wl;
+            const uint32_t m_per = a.m_per[l], m_wl = a.m_wl[l];
             const int s_off = l == 0 ? a.xoff : a.yb[l - 1];
             const int s_str = l == 0 ? a.xs : a.sy[l - 1];
+            const int d_off = a.yb[l], d_str = a.sy[l], bsl = a.bs[l];
             for (int q = t; q < PB * per; q += nthr) {
-                const int p = q / per, rem = q - p * per, i = rem / Wl, j = rem - i * Wl;
+                const int p = fdiv(q, m_per), rem = q - p * per, i = fdiv(rem, m_wl), j = rem - i * Wl;
                 const float *sp = smem + p * PF + s_off + (2 * i + R) * s_str + 2 * j + R;
                 const float x00 = sp[0], x01 = sp[1], x10 = sp[s_str], x11 = sp[s_str + 1];
                 const float s0 = x00 + x01, s1 = x10 + x11, d0 = x00 - x01, d1 = x10 - x11;
-                float *dp = smem + p * PF + a.yb[l] + (i + R) * a.sy[l] + j + R;
-                const int bsl = a.bs[l];
+                float *dp = smem + p * PF + d_off + (i + R) * d_str + j + R;
                 dp[0] = s0 + s1;
                 dp[bsl] = s0 - s1;
                 dp[2 * bsl] = d0 + d1;
@@ -251,7 +277,7 @@ __device__ __forceinline__ void fused_fwd_body(const FusedArgs &a) {
             float w[KK];
             const float *wp = smem + cd1[k];
 #pragma unroll
-            for (int t = 0; t < KK; ++t) w[t] = wp[t];
+            for (int tp = 0; tp < KK; ++tp) w[tp] = wp[tp];
             conv_strip_dyn<K>(smem + (cd0[k] & 0xffffu), (cd0[k] >> 16) & 0xffu, w, z[k]);
             __builtin_amdgcn_sched_barrier(0);
         }
@@ -269,9 +295,11 @@ __device__ __forceinline__ void fused_fwd_body(const FusedArgs &a) {
         // 5. sign patterns of every block, in place: slot 2 ry + rx
         for (int l = 0; l < L; ++l) {
             const int Hl = a.hl[l + 1], Wl = a.wl_[l + 1], per = Hl * Wl, bsl = a.bs[l];
+            const uint32_t m_per = a.m_per[l], m_wl = a.m_wl[l];
+            const int d_off = a.yb[l], d_str = a.sy[l];
             for (int q = t; q < PB * per; q += nthr) {
-                const int p = q / per, rem = q - p * per, i = rem / Wl, j = rem - i * Wl;
-                float *zp = smem + p * PF + a.yb[l] + (i + R) * a.sy[l] + j + R;
+                const int p = fdiv(q, m_per), rem = q - p * per, i = fdiv(rem, m_wl), j = rem - i * Wl;
+                float *zp = smem + p * PF + d_off + (i + R) * d_str + j + R;
                 const float LL = zp[0], LH = zp[bsl], HL = zp[2 * bsl], HH = zp[3 * bsl];
                 zp[0] = (LL + LH) + (HL + HH);
                 zp[bsl] = (LL + LH) - (HL + HH);
@@ -289,37 +317,54 @@ __device__ __forceinline__ void fused_fwd_body(const FusedArgs &a) {
             w0[i] = uniform(sc0 * a.w0[(size_t)c * KK + (a.rotate ? (K - 1 - u) * K + (K - 1 - v) : i)]);
         }
         const float bias = a.b0 ? uniform(sc0 * a.b0[c]) : 0.f;
+        T *ybase = y + ((size_t)n0 * a.C + c) * HW;
 #pragma unroll
         for (int k = 0; k < kFusedMaxFinal; ++k) {
             const int rows = fd[k] >> 24, p = (fd[k] >> 16) & 0xffu;
-            if (rows == 0 || n0 + p >= n_end) continue;
+            if (rows == 0 || p >= live) continue;
             const int s = (fd[k] >> 8) & 0xffu, j = fd[k] & 0xffu;
             float acc[kRH];
 #pragma unroll
             for (int i = 0; i < kRH; ++i) acc[i] = bias;
             conv_strip<K>(smem + p * PF + a.xoff + (s * kRH) * a.xs + j, a.xs, w0, acc);
-            for (int l = 0; l < L; ++l) {
-                // pixel (8s + i, j): slot 2 ry + rx with ry = bit l of (8s + i), rx = bit l of j,
-                // block (row (8s + i) >> (l+1), column j >> (l+1))
-                const float *zb = smem + p * PF + a.yb[l] + ((j >> l) & 1) * a.bs[l] + ((j >> (l + 1)) + R);
-                const int sy = a.sy[l], bs2 = 2 * a.bs[l];
+            // Level l+1 adds slot 2 ry + rx of the block at (y >> (l+1), x >> (l+1)),
+            // ry = bit l of y = 8s + i, rx = bit l of x = j.  For l <= 2, ry and the
+            // block row offset from 8s depend on i only; for l >= 3 they depend on s.
 #pragma unroll
-                for (int i = 0; i < kRH; ++i) {
-                    const int yy = s * kRH + i;
-                    acc[i] += zb[((yy >> l) & 1) * bs2 + ((yy >> (l + 1)) + R) * sy];
+            for (int l = 0; l < kMaxLevels; ++l) {
+                if (l >= L) break;
+                const int sy = a.sy[l], bs2 = 2 * a.bs[l];
+                const float *zb = smem + p * PF + a.yb[l] + ((j >> l) & 1) * a.bs[l] + (j >> (l + 1)) + R;
+                if (l <= 2) {
+                    const float *zr = zb + ((s << (2 - l)) + R) * sy;
+#pragma unroll
+                    for (int i = 0; i < kRH; ++i) acc[i] += zr[((i >> l) & 1) * bs2 + (i >> (l + 1)) * sy];
+                } else {
+                    const float v = zb[((s >> (l - 3)) & 1) * bs2 + ((s >> (l - 2)) + R) * sy];
+#pragma unroll
+                    for (int i = 0; i < kRH; ++i) acc[i] += v;
                 }
             }
-            T *yp = y + ((size_t)(n0 + p) * a.C + c) * HW + (size_t)(s * kRH) * W + j;
+            const int yoff = p * CHW + (s * kRH) * W + j;
+            if constexpr (sizeof(T) == 2) {
 #pragma unroll
-            for (int i = 0; i < kRH; ++i)
-                if (i < rows) act_store(yp, (size_t)i * W, acc[i]);
+                for (int i = 0; i < kRH; i += 2) {
+                    const uint32_t pk = f32x2_to_bf16x2(acc[i], acc[i + 1]);
+                    if (i < rows) reinterpret_cast<uint16_t *>(ybase)[yoff + i * W] = (uint16_t)pk;
+                    if (i + 1 < rows) reinterpret_cast<uint16_t *>(ybase)[yoff + (i + 1) * W] = (uint16_t)(pk >> 16);
+                }
+            } else {
+#pragma unroll
+                for (int i = 0; i < kRH; ++i)
+                    if (i < rows) ybase[yoff + i * W] = acc[i];
+            }
             __builtin_amdgcn_sched_barrier(0);
         }
     }
 }
 
 template <int K, typename T, int VE>
-__global__ __launch_bounds__(256) void fused_fwd_kernel(FusedArgs a) {
+__global__ __launch_bounds__(256, (K <= 5 ? 4 : 2)) void fused_fwd_kernel(FusedArgs a) {
     fused_fwd_body<K, T, VE>(a);
 }
 

@@ -54,13 +54,21 @@ __device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as
 __device__ __forceinline__ float act_load(const float *p, size_t i) { return p[i]; }
 __device__ __forceinline__ float act_load(const uint16_t *p, size_t i) { return bf16_bits_to_f32(p[i]); }
 
-// float32 -> bfloat16, round to nearest, ties to even; NaN stays a quiet NaN.
+// float32 -> bfloat16, round to nearest, ties to even (gfx950 v_cvt_pk_bf16_f32).
 __device__ __forceinline__ uint32_t f32_to_bf16(float v) {
-    uint32_t u = __float_as_uint(v);
-    if ((u & 0x7fffffffu) > 0x7f800000u) return (u >> 16) | 0x40u;
-    u += 0x7fffu + ((u >> 16) & 1u);
-    return u >> 16;
+    return __builtin_bit_cast(uint16_t, (__bf16)v);
 }
+typedef float wtc_float2 __attribute__((ext_vector_type(2)));
+typedef __bf16 wtc_bf16x2 __attribute__((ext_vector_type(2)));
+// Two values packed low, high in one conversion.
+__device__ __forceinline__ uint32_t f32x2_to_bf16x2(float a, float b) {
+    const wtc_float2 v = {a, b};
+    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, wtc_bf16x2));
+}
+
+// Exact quotient n / d for n, d < 2^16, with m = ceil(2^32 / d) computed on the host
+// (m = 0 encodes d = 1): the error term n (m d - 2^32) / (d 2^32) stays below 1/d.
+__device__ __forceinline__ int fdiv(int n, uint32_t m) { return m ? (int)__umulhi((uint32_t)n, m) : n; }
 
 __device__ __forceinline__ void act_store(float *p, size_t i, float v) { p[i] = v; }
 __device__ __forceinline__ void act_store(uint16_t *p, size_t i, float v) { p[i] = (uint16_t)f32_to_bf16(v); }
@@ -70,7 +78,7 @@ __device__ __forceinline__ void act_store2(float *p, size_t i, float a, float b)
     *reinterpret_cast<float2 *>(p + i) = make_float2(a, b);
 }
 __device__ __forceinline__ void act_store2(uint16_t *p, size_t i, float a, float b) {
-    *reinterpret_cast<uint32_t *>(p + i) = f32_to_bf16(a) | (f32_to_bf16(b) << 16);
+    *reinterpret_cast<uint32_t *>(p + i) = f32x2_to_bf16x2(a, b);
 }
 __device__ __forceinline__ void act_load2(const float *p, size_t i, float &a, float &b) {
     const float2 v = *reinterpret_cast<const float2 *>(p + i);
