@@ -208,8 +208,18 @@ def main():
     print(f"# bench: {args.workload}: {describe(cases)}", file=sys.stderr, flush=True)
     layers = [Layer(c, args.rotate, torch, wt) for c in cases]
     es = lambda c: 2 if c.dtype == "bf16" else 4
-    step_bytes = sum(traffic.step_totals(c.n, c.c, c.h, c.w, c.k, c.levels, es(c))[0] for c in cases)
-    step_flops = sum(traffic.step_totals(c.n, c.c, c.h, c.w, c.k, c.levels, es(c))[1] for c in cases)
+
+    def case_launches(c):
+        # the kernels the library enqueues for this shape, priced by the byte model
+        desc = wt.make_desc(c.n, c.c, c.h, c.w, c.k, c.levels, wt.BF16 if c.dtype == "bf16" else wt.F32)
+        plan = {p: [e["name"] for e in wt.wtconv_plan_launches(desc, op)]
+                for p, op in (("forward", wt.OP_FORWARD), ("backward_input", wt.OP_BACKWARD_INPUT),
+                              ("backward_weight", wt.OP_BACKWARD_WEIGHT))}
+        return traffic.launches_from_plan(c.n, c.c, c.h, c.w, c.k, c.levels, es(c), plan)
+
+    case_ls = {c.name: case_launches(c) for c in cases}
+    step_bytes = sum(b for c in cases for _, _, b, _ in case_ls[c.name])
+    step_flops = sum(f for c in cases for _, _, _, f in case_ls[c.name])
 
     for i in range(args.warmup):
         run_step(layers, i, wt)
@@ -240,9 +250,7 @@ def main():
     # algorithmic bytes / flops per kernel family (summed over layers and passes)
     fam = {}
     for c in cases:
-        for name, _pass, b, f in traffic.launches(c.n, c.c, c.h, c.w, c.k, c.levels, es(c)):
-            fam_name, _, lvl = name.partition("#")
-            key = f"{fam_name}<{c.k},{c.dtype}>" + (f"#{lvl}" if lvl else "")
+        for key, _pass, b, f in case_ls[c.name]:
             d = fam.setdefault(key, {"bytes": 0, "flops": 0, "launches": 0})
             d["bytes"] += b
             d["flops"] += f
@@ -299,7 +307,8 @@ def main():
     }
     if not args.no_cpu_baseline:
         def sample_bytes(c):
-            return traffic.step_totals(c.n, c.c, c.h, c.w, c.k, c.levels, es(c))[0]
+            # the sample runs the full workload's shapes, so its bytes are the step's
+            return sum(b for _, _, b, _ in case_ls[c.name])
         print("# cpu baseline (oracle) ...", file=sys.stderr, flush=True)
         result["cpu_baseline"] = cpu_baseline(cases, args.cpu_budget, sample_bytes)
     print(json.dumps(result), flush=True)

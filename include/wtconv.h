@@ -122,6 +122,21 @@ int wtconv_backward_weight(const wtconv_desc *desc, const void *x, const void *d
                            float *dw0, float *db0, float *ds0, float *dwl, float *dsl,
                            void *workspace, size_t workspace_bytes, void *stream);
 
+/* Launch plan of an operation for this shape, assuming activation pointers aligned
+ * to 16 bytes (as device allocations are): one entry per kernel launch the call
+ * would enqueue, in order, named as the profiling records name them (see below).
+ * Writes up to max_entries entries and the total count to *n_entries.  Host only:
+ * nothing is enqueued.  Returns a status code. */
+typedef struct wtconv_launch {
+    char name[64];       /* kernel family, k, dtype and level, e.g. "fused_fwd<5,bf16>" */
+    int64_t workgroups;  /* grid size in workgroups */
+    int32_t threads;     /* workgroup size */
+    int32_t lds_bytes;   /* dynamic LDS per workgroup */
+} wtconv_launch;
+
+int wtconv_plan_launches(const wtconv_desc *desc, int op, wtconv_launch *out, int max_entries,
+                         int *n_entries);
+
 /* Human-readable text of a status code (static storage). */
 const char *wtconv_status_string(int status);
 

@@ -5,5 +5,5 @@ build step (build.py) and the Python binding (wtconv.py)."""
 from .wtconv import (  # noqa: F401
     BF16, F32, MAX_LEVELS, OP_BACKWARD_INPUT, OP_BACKWARD_WEIGHT, OP_FORWARD, Desc, WTConvError,
     library, make_desc, profile_begin, profile_end, wtconv_backward_input, wtconv_backward_weight,
-    wtconv_forward, wtconv_workspace_size,
+    wtconv_forward, wtconv_plan_launches, wtconv_workspace_size,
 )

@@ -816,6 +816,65 @@ int wtconv_backward_weight(const wtconv_desc *desc, const void *x, const void *d
                  static_cast<char *>(workspace), st);
 }
 
+int wtconv_plan_launches(const wtconv_desc *desc, int op, wtconv_launch *out, int max_entries, int *n_entries) {
+    if (!n_entries) return WTCONV_ERR_NULL;
+    *n_entries = 0;
+    int rc = check_desc(desc);
+    if (rc) return rc;
+    if (op != WTCONV_OP_FORWARD && op != WTCONV_OP_BACKWARD_INPUT && op != WTCONV_OP_BACKWARD_WEIGHT)
+        return WTCONV_ERR_OP;
+    const wtconv_desc &d = *desc;
+    const char *dt = d.dtype == WTCONV_BF16 ? "bf16" : "f32";
+    const size_t es = elem_size(d.dtype);
+    std::vector<wtconv_launch> v;
+    auto add = [&](const char *fam, int level, long long wg, int thr, size_t lds) {
+        wtconv_launch e{};
+        if (level > 0)
+            snprintf(e.name, sizeof(e.name), "%s<%d,%s>#%d", fam, d.k, dt, level);
+        else
+            snprintf(e.name, sizeof(e.name), "%s<%d,%s>", fam, d.k, dt);
+        e.workgroups = wg;
+        e.threads = thr;
+        e.lds_bytes = (int32_t)lds;
+        if (wg > 0) v.push_back(e);
+    };
+    const void *aligned_ptr = reinterpret_cast<const void *>(uintptr_t(256));
+    if (op != WTCONV_OP_BACKWARD_WEIGHT) {
+        if (!empty(d)) {
+            FusedArgs fa{};
+            if (plan_fused(d, vec_width(d.w, d.dtype, aligned_ptr), fa)) {
+                add("fused_fwd", 0, (long long)d.c * fa.nblk, kThreads, (size_t)fa.lds_floats * sizeof(float));
+            } else {
+                const FwdPlan p = plan_forward(d);
+                for (int l = 1; l <= d.levels; ++l)
+                    add("level_fwd", l, grid_of(p.lvl[l - 1], d.c), kThreads, lds_bytes(Kind::LevelFwd, d.k, p.lvl[l - 1]));
+                Tiling t = p.syn;
+                t.VW = vec_width(d.w, d.dtype, aligned_ptr);
+                add("synth", 0, grid_of(t, d.c), kThreads, lds_bytes(Kind::Synth, d.k, t));
+            }
+        }
+    } else if (d.c > 0) {
+        const DwPlan p = plan_backward_weight(d);
+        if (!empty(d)) {
+            if (p.fused && d.levels > 0) {
+                add("fused_dw", 0, (long long)d.c * p.fa.nblk, kThreads, (size_t)p.fa.lds_floats * sizeof(float));
+            } else {
+                for (int l = 1; l <= d.levels; ++l)
+                    add("dw_level", l, grid_of(p.lvl[l - 1], d.c), kThreads, lds_bytes(Kind::DwLevel, d.k, p.lvl[l - 1]));
+            }
+            Tiling t = p.base;
+            t.VW = vec_width(d.w, d.dtype, aligned_ptr);
+            add("dw_base", 0, grid_of(t, d.c), kThreads, lds_bytes(Kind::DwBase, d.k, t));
+        }
+        add("dw_finalize", 0, (long long)d.c * (d.levels + 1), 128, 0);
+    }
+    (void)es;
+    const int n = (int)v.size();
+    for (int i = 0; i < n && i < max_entries && out; ++i) out[i] = v[i];
+    *n_entries = n;
+    return WTCONV_OK;
+}
+
 int wtconv_profile_begin(void) {
     std::lock_guard<std::mutex> lock(g_prof_mu);
     for (auto &r : g_prof) {

@@ -18,7 +18,7 @@ MAX_LEVELS = 8
 
 EXPORTED = ["wtconv_workspace_size", "wtconv_forward", "wtconv_backward_input",
             "wtconv_backward_weight", "wtconv_status_string", "wtconv_version",
-            "wtconv_profile_begin", "wtconv_profile_end"]
+            "wtconv_profile_begin", "wtconv_profile_end", "wtconv_plan_launches"]
 
 
 class Desc(ctypes.Structure):
@@ -31,6 +31,11 @@ class KernelTime(ctypes.Structure):
     _fields_ = [("name", ctypes.c_char * 64), ("count", ctypes.c_int32),
                 ("total_ms", ctypes.c_double), ("min_ms", ctypes.c_double),
                 ("max_ms", ctypes.c_double)]
+
+
+class Launch(ctypes.Structure):
+    _fields_ = [("name", ctypes.c_char * 64), ("workgroups", ctypes.c_int64),
+                ("threads", ctypes.c_int32), ("lds_bytes", ctypes.c_int32)]
 
 
 class WTConvError(RuntimeError):
@@ -59,6 +64,7 @@ def library():
         lib.wtconv_version.argtypes = []
         lib.wtconv_profile_begin.argtypes = []
         lib.wtconv_profile_end.argtypes = [ctypes.POINTER(KernelTime), i32, ctypes.POINTER(i32)]
+        lib.wtconv_plan_launches.argtypes = [dp, i32, ctypes.POINTER(Launch), i32, ctypes.POINTER(i32)]
         for name in EXPORTED:
             if name not in ("wtconv_status_string",):
                 getattr(lib, name).restype = i32
@@ -74,6 +80,17 @@ def _check(rc: int, what: str):
 
 def make_desc(n, c, h, w, k, levels, dtype) -> Desc:
     return Desc(int(n), int(c), int(h), int(w), int(k), int(levels), int(dtype), 0)
+
+
+def wtconv_plan_launches(desc: Desc, op: int):
+    """Kernel launches an operation enqueues for this shape: list of dicts with
+    name, workgroups, threads, lds_bytes (host only)."""
+    arr = (Launch * 32)()
+    n = ctypes.c_int(0)
+    _check(library().wtconv_plan_launches(ctypes.byref(desc), int(op), arr, 32, ctypes.byref(n)),
+           "wtconv_plan_launches")
+    return [{"name": arr[i].name.decode(), "workgroups": arr[i].workgroups, "threads": arr[i].threads,
+             "lds_bytes": arr[i].lds_bytes} for i in range(min(n.value, 32))]
 
 
 def wtconv_workspace_size(desc: Desc, op: int) -> int:

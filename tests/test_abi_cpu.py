@@ -160,3 +160,25 @@ def test_backward_weight_argument_errors():
         assert f(d, **{key: P_ODD}) == E_ALIGN, key
     assert f(d) == E_WS
     assert f(d, ws=P, wsb=16) == E_WS
+
+
+def test_launch_plan_query():
+    # host-only query: the kernels each operation enqueues for a shape
+    plan = lambda d, op: [e["name"] for e in wt.wtconv_plan_launches(d, op)]
+    d = wt.make_desc(64, 96, 56, 56, 5, 3, wt.BF16)       # plane-resident path
+    assert plan(d, wt.OP_FORWARD) == ["fused_fwd<5,bf16>"]
+    assert plan(d, wt.OP_BACKWARD_INPUT) == ["fused_fwd<5,bf16>"]
+    assert plan(d, wt.OP_BACKWARD_WEIGHT) == ["fused_dw<5,bf16>", "dw_base<5,bf16>", "dw_finalize<5,bf16>"]
+    d = wt.make_desc(2, 4, 256, 256, 3, 2, wt.F32)         # per-level path (plane past 64x64)
+    assert plan(d, wt.OP_FORWARD) == ["level_fwd<3,f32>#1", "level_fwd<3,f32>#2", "synth<3,f32>"]
+    assert plan(d, wt.OP_BACKWARD_WEIGHT) == ["dw_level<3,f32>#1", "dw_level<3,f32>#2", "dw_base<3,f32>",
+                                              "dw_finalize<3,f32>"]
+    for e in wt.wtconv_plan_launches(d, wt.OP_FORWARD):
+        assert e["workgroups"] > 0 and e["threads"] == 256 and 0 < e["lds_bytes"] <= 64 * 1024
+    # empty input: nothing to launch forward; the weight gradient still writes zeros
+    d = wt.make_desc(0, 4, 16, 16, 5, 2, wt.F32)
+    assert plan(d, wt.OP_FORWARD) == []
+    assert plan(d, wt.OP_BACKWARD_WEIGHT) == ["dw_finalize<5,f32>"]
+    n = ctypes.c_int(-1)
+    assert wt.library().wtconv_plan_launches(ctypes.byref(d), 7, None, 0, ctypes.byref(n)) == E_OP
+    assert wt.library().wtconv_plan_launches(ctypes.byref(d), 0, None, 0, None) == E_NULL

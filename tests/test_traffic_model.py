@@ -25,6 +25,27 @@ def test_table1_and_eq3(golden_dir):
         g["ref_intensity_fp32"], abs=0.015)
 
 
+def test_launch_model_fused():
+    n, c, h, w, k, L, E = 2, 3, 7, 9, 5, 2, 2
+    ls = traffic.launches(n, c, h, w, k, L, E, fused_fwd=True, fused_dw=True)
+    assert [x[0] for x in ls] == ["fused_fwd", "fused_fwd", "fused_dw", "dw_base", "dw_finalize"]
+    N = n * c * h * w
+    P = n * c
+    # x in, y out; the FLOPs equal the per-level kernels' sum (same arithmetic, no HBM round trips)
+    assert ls[0][2] == E * 2 * N
+    per_level = traffic.launches(n, c, h, w, k, L, E)
+    assert ls[0][3] == sum(f for name, p, _, f in per_level if p == "forward")
+    assert ls[2][2] == E * 2 * N
+    assert ls[2][3] == P * (20 + 6) * (8 * k * k + 16)
+    # parsing of profiled names back to families
+    assert traffic.split_name("level_fwd<5,bf16>#2") == ("level_fwd", 2)
+    assert traffic.split_name("fused_fwd<7,f32>") == ("fused_fwd", 0)
+    plan = {"forward": ["fused_fwd<5,bf16>"], "backward_input": ["fused_fwd<5,bf16>"],
+            "backward_weight": ["fused_dw<5,bf16>", "dw_base<5,bf16>", "dw_finalize<5,bf16>"]}
+    lp = traffic.launches_from_plan(n, c, h, w, k, L, E, plan)
+    assert [x[2:] for x in lp] == [x[2:] for x in ls]
+
+
 def test_launch_model_counts():
     n, c, h, w, k, L, E = 2, 3, 7, 9, 5, 2, 2
     ls = traffic.launches(n, c, h, w, k, L, E)
