@@ -153,8 +153,9 @@ def cpu_baseline(cases, budget_s, model_bytes_fn):
 
 
 def load_traffic(kernel, workload, digest):
-    """HBM bytes per launch (fetch + write) of `kernel` from the rocprofv3 counter
-    record of this workload, if the counters were taken on this kernel source."""
+    """HBM bytes per launch of `kernel` ({fetch_bytes, write_bytes, bytes}) from the
+    rocprofv3 counter record of this workload, if the counters were taken on this
+    kernel source (None otherwise)."""
     path = os.path.join(ROOT, "profiles", f"traffic_{workload}.txt")
     if not os.path.exists(path):
         return None
@@ -282,7 +283,11 @@ def main():
                 "frac": round(dom["tflops"] / ALU_PEAK_TFLOPS, 4)}
     roof["kernel"] = dom["kernel"]
     roof["avg_launch_ms"] = dom["avg_ms"]
-    roof["traffic"] = load_traffic(dom["kernel"], args.workload, digest)
+    measured = load_traffic(dom["kernel"], args.workload, digest)
+    roof["traffic"] = None if measured is None else measured["bytes"]
+    if measured is not None:
+        roof["traffic_fetch_write"] = [measured["fetch_bytes"], measured["write_bytes"]]
+        roof["traffic_vs_algorithmic"] = round(measured["bytes"] / dom["bytes_per_launch"], 3)
 
     value = step_bytes / (ms_per_step * 1e-3) / 1e9
     result = {

@@ -5,6 +5,9 @@
     python rocprof_summary.py counters <fetch.db> <write.db> <copy_fetch.db> <copy_write.db> <copy_bytes>
         FETCH_SIZE / WRITE_SIZE per dispatch (KiB), scaled by what the same counters
         read for a plain device copy of known size, as bytes per launch
+    python rocprof_summary.py traffic <workload> <fetch.db> <write.db> <copy_fetch.db> <copy_write.db> <copy_bytes>
+        the same, keyed by the library's kernel names for the workload's launch plan
+        (the record bench.py reads from profiles/traffic_<workload>.txt)
 """
 from __future__ import annotations
 
@@ -64,8 +67,70 @@ def counters(fetch_db, write_db, copy_fetch_db, copy_write_db, copy_bytes):
     return {"fetch_scale": round(fetch_scale, 4), "write_scale": round(write_scale, 4), "kernels": kernels}
 
 
+def _family(short: str) -> str:
+    """'wtc::fused_fwd_kernel<5, unsigned short, 8>' -> 'fused_fwd'."""
+    return short.split("<")[0].split("::")[-1].removesuffix("_kernel")
+
+
+def traffic(workload, fetch_db, write_db, copy_fetch_db, copy_write_db, copy_bytes):
+    """Measured HBM bytes per launch for every kernel of the workload's launch plan:
+    a counter row matches a planned launch by kernel family and grid size."""
+    import os
+    root = os.path.dirname(os.path.abspath(__file__))
+    sys.path.insert(0, root)
+    import bench
+    import memory_bound_depthwise_amd as wt
+    from synthetic import baseline_cases
+
+    rec = counters(fetch_db, write_db, copy_fetch_db, copy_write_db, copy_bytes)
+    rows = collections.defaultdict(list)
+    for r in rec["kernels"]:
+        rows[(_family(r["kernel"]), r["grid"])].append(r)
+    out = {}
+    allc = baseline_cases()
+    for name in bench.WORKLOADS[workload]:
+        c = allc[name]
+        desc = wt.make_desc(c.n, c.c, c.h, c.w, c.k, c.levels, wt.BF16 if c.dtype == "bf16" else wt.F32)
+        for op in (wt.OP_FORWARD, wt.OP_BACKWARD_INPUT, wt.OP_BACKWARD_WEIGHT):
+            for e in wt.wtconv_plan_launches(desc, op):
+                fam = e["name"].split("<")[0]
+                match = rows.get((fam, e["workgroups"] * e["threads"]))
+                if not match or match[0]["write_bytes"] is None:
+                    continue
+                r = match[0]
+                out[e["name"]] = {"fetch_bytes": r["fetch_bytes"], "write_bytes": r["write_bytes"],
+                                  "bytes": r["fetch_bytes"] + r["write_bytes"]}
+    return {"workload": workload, "source_digest": bench.source_digest(),
+            "fetch_scale": rec["fetch_scale"], "write_scale": rec["write_scale"], "kernels": out}
+
+
+def trace_md(rows):
+    out = ["| kernel | calls | avg µs | min µs | max µs | total µs | % |", "|---|---|---|---|---|---|---|"]
+    for r in rows:
+        out.append(f"| `{r['kernel']}` | {r['calls']} | {r['avg_us']} | {r['min_us']} | {r['max_us']} | "
+                   f"{r['total_us']} | {r['pct']} |")
+    return "\n".join(out)
+
+
+def counters_md(rec):
+    out = ["| kernel | grid (threads) | FETCH_SIZE KiB | WRITE_SIZE KiB | fetch MB | write MB |",
+           "|---|---|---|---|---|---|"]
+    for r in rec["kernels"]:
+        wb = "" if r["write_bytes"] is None else f"{r['write_bytes'] / 1e6:.1f}"
+        out.append(f"| `{r['kernel']}` | {r['grid']} | {r['fetch_kib']} | {r['write_kib']} | "
+                   f"{r['fetch_bytes'] / 1e6:.1f} | {wb} |")
+    return "\n".join(out)
+
+
 if __name__ == "__main__":
+    md = "--md" in sys.argv
+    if md:
+        sys.argv.remove("--md")
     if sys.argv[1] == "trace":
-        print(json.dumps(trace(sys.argv[2]), indent=1))
+        rows = trace(sys.argv[2])
+        print(trace_md(rows) if md else json.dumps(rows, indent=1))
     elif sys.argv[1] == "counters":
-        print(json.dumps(counters(*sys.argv[2:6], float(sys.argv[6])), indent=1))
+        rec = counters(*sys.argv[2:6], float(sys.argv[6]))
+        print(counters_md(rec) if md else json.dumps(rec, indent=1))
+    elif sys.argv[1] == "traffic":
+        print(json.dumps(traffic(sys.argv[2], *sys.argv[3:7], float(sys.argv[7])), indent=1))
