@@ -22,6 +22,7 @@
 #include "wtconv.h"
 #include "wtconv_fused.hpp"
 #include "wtconv_fused_dw.hpp"
+#include "wtconv_plane.hpp"
 #include "wtconv_kernels.hpp"
 
 namespace wtc {
@@ -37,6 +38,8 @@ inline size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
 // Multiply-high reciprocal for fdiv (divisor and dividends below 2^16); 0 encodes 1.
 inline uint32_t magic_of(int d) { return d <= 1 ? 0u : (uint32_t)((0x100000000ULL + (uint64_t)d - 1) / (uint64_t)d); }
 inline int cdiv(long long a, long long b) { return (int)((a + b - 1) / b); }
+// Reciprocal for udiv16 (exact n / d for n < 2^16, d < 2^15): ceil(2^31 / d).
+inline uint32_t magic31_of(int d) { return (uint32_t)(((1ULL << 31) + (uint64_t)d - 1) / (uint64_t)d); }
 
 // ---------------------------------------------------------------------------
 // Profiling: hipEvent pairs around each launch, on the launch stream.
@@ -327,6 +330,155 @@ bool plan_fused(const wtconv_desc &d, int VE, FusedArgs &a) {
 
 
 // ---------------------------------------------------------------------------
+// Plane-resident forward on the polyphase grid: layout, stacking, bank-aware strides
+// ---------------------------------------------------------------------------
+
+constexpr int kPlaneLdsBudget = 53248;   // three workgroups per compute unit
+constexpr int kPlaneTargetBlocks = 768;  // three per compute unit
+
+struct PlaneCfg {
+    int CW = 1, RH = 8;
+};
+
+// Bank cost of the final pass's 16-byte cell reads with row stride sy (cells): a
+// group of 8 lanes covers the 32 banks once when its cells are distinct mod 8; the
+// cost is the largest number of lanes of a group that share a cell slot mod 8,
+// summed over the groups (1 per group = conflict-free).
+long long plane_bank_cost(const PlaneArgs &a, int RH, int sy) {
+    long long cost = 0;
+    const int per_strip = a.PB * a.W1;
+    for (int g = 0; g * 8 < a.final_items; ++g) {
+        int cnt[8] = {0};
+        int worst = 0;
+        for (int t = g * 8; t < std::min(a.final_items, g * 8 + 8); ++t) {
+            const int s = t / per_strip, r = t % per_strip, p = r / a.W1, j = r % a.W1;
+            const int cell = s * RH * sy + p * a.Pw1 + j;
+            worst = std::max(worst, ++cnt[cell & 7]);
+        }
+        cost += worst;
+    }
+    return cost;
+}
+
+// Layout for pb planes per pass; false when it does not fit.  Grid arrays hold one
+// float4 per cell (polyphase components of x, or the four bands of a level).
+bool plane_layout(const wtconv_desc &d, const PlaneCfg &cfg, int pb, PlaneArgs &a) {
+    const int K = d.k, KK = K * K, R = (K - 1) / 2, L = d.levels, RH = cfg.RH, CW = cfg.CW;
+    a = PlaneArgs{};
+    a.n = d.n;
+    a.C = d.c;
+    a.H = d.h;
+    a.W = d.w;
+    a.L = L;
+    a.PB = pb;
+    a.H1 = (d.h + 1) / 2;
+    a.W1 = (d.w + 1) / 2;
+    a.S1 = cdiv(a.H1, RH);
+    a.Gw = cdiv(a.W1, CW);
+    int hs[kMaxLevels + 1], ws[kMaxLevels + 1];
+    hs[0] = d.h;
+    ws[0] = d.w;
+    for (int l = 1; l <= L; ++l) {
+        hs[l] = (hs[l - 1] + 1) / 2;
+        ws[l] = (ws[l - 1] + 1) / 2;
+    }
+    // column pitch between side-by-side planes: at every level the gap is >= R
+    if (pb == 1) {
+        a.Pw1 = a.W1;
+    } else {
+        int pwL = 1;
+        for (int l = 1; l <= L; ++l) pwL = std::max(pwL, cdiv(ws[l] + R, 1LL << (L - l)));
+        while (((long long)pwL << (L - 1)) % CW) ++pwL;
+        a.Pw1 = pwL << (L - 1);
+    }
+    const int W1s = pb == 1 ? a.W1 : pb * a.Pw1;
+    a.commit_items = pb * a.H1 * a.Gw;
+    a.final_items = a.S1 * pb * a.W1;
+    if (a.final_items >= 32768 || a.commit_items >= 32768) return false;
+    if ((long long)pb * d.c * d.h * d.w >= (1LL << 31)) return false;  // 32-bit offsets from a plane base
+    // level-1 arrays: the stride (cells) with the fewest bank conflicts in the final pass
+    const int sy_min = kPlaneCO + W1s + R;
+    long long best = -1;
+    for (int sy = sy_min; sy < sy_min + 8; ++sy) {
+        const long long cost = plane_bank_cost(a, RH, sy);
+        if (best < 0 || cost < best) {
+            best = cost;
+            a.sy1 = sy;
+        }
+    }
+    a.a1 = (a.S1 * RH + 2 * R) * a.sy1;
+    long long cells = 2LL * a.a1;
+    int units = 0;
+    a.units[0] = 0;
+    for (int l = 2; l <= L; ++l) {
+        const int li = l - 2;
+        a.hl[li] = hs[l];
+        a.wls[li] = pb == 1 ? ws[l] : (pb * a.Pw1) >> (l - 1);
+        a.sd[li] = cdiv(hs[l], kPlaneRHd);
+        a.syd[li] = kPlaneCO + a.wls[li] + R;
+        a.offd[li] = (int)cells;
+        cells += (long long)(a.sd[li] * kPlaneRHd + 2 * R) * a.syd[li];
+        units += cdiv((long long)a.sd[li] * a.wls[li], 64);
+        a.units[li + 1] = units;
+        if ((long long)a.hl[li] * a.wls[li] >= 32768) return false;
+    }
+    long long fl = 4 * cells;  // floats
+    for (int l = 2; l <= L; ++l) {
+        const int li = l - 2;
+        a.sq[li] = 2 * a.wls[li];
+        a.offq[li] = (int)fl;
+        fl += ((2LL * hs[l] * a.sq[li]) + 3) & ~3LL;
+    }
+    a.wt = (int)fl;
+    fl += ((4LL * L + 1) * KK + 3) & ~3LL;
+    a.lds_floats = (int)fl;
+    if (fl * 4 > kPlaneLdsBudget) return false;
+    a.m_gw = magic31_of(a.Gw);
+    a.m_h1 = magic31_of(a.H1);
+    a.m_strip = magic31_of(pb * a.W1);
+    a.m_w1 = magic31_of(a.W1);
+    for (int l = 2; l <= L; ++l) a.m_wls[l - 2] = magic31_of(a.wls[l - 2]);
+    return true;
+}
+
+// Choose the variant (CW, RH), PB and the planes per workgroup; false when the
+// shape is outside the kernel's range.
+bool plan_plane(const wtconv_desc &d, PlaneArgs &a, PlaneCfg &cfg) {
+    if (d.levels < 1 || d.n <= 0 || d.c <= 0 || d.h <= 0 || d.w <= 0) return false;
+    if (d.h > kFusedMaxSide || d.w > kFusedMaxSide) return false;
+    const int H1 = (d.h + 1) / 2;
+    cfg.RH = H1 % 7 == 0 ? 7 : (H1 <= 4 ? 4 : 8);
+    cfg.CW = d.w % 8 == 0 ? 4 : (d.w % 4 == 0 ? 2 : 1);
+    const int K = d.k;
+    double best = 1e30;
+    int best_pb = 0;
+    for (int pb = 1; pb <= std::min(d.n, 64); ++pb) {
+        PlaneArgs t{};
+        if (!plane_layout(d, cfg, pb, t)) {
+            if (pb == 1) return false;
+            break;
+        }
+        // wave-instructions per pass: a final item is ~2 (4 + 1) RH K^2 FMAs, a deep
+        // item 4 kPlaneRHd K^2; commit and Haar ~30 per item; ~400 fixed
+        const double fin = cdiv(t.final_items, kPlaneThreads) * 2.0 * (8.0 * cfg.RH * K * K / 2 + 40.0 * cfg.RH);
+        const double deep = cdiv(t.units[d.levels - 1], kPlaneThreads / 64) * (4.0 * kPlaneRHd * K * K + 60.0);
+        const double misc = cdiv(t.commit_items, kPlaneThreads) * 40.0 + 400.0;
+        const double cost = (fin + deep + misc) / pb;
+        if (cost < best - 1e-9) {
+            best = cost;
+            best_pb = pb;
+        }
+    }
+    if (!plane_layout(d, cfg, best_pb, a)) return false;
+    const long long passes = cdiv(d.n, a.PB);
+    const long long want_per_chan = std::max<long long>(1, cdiv(kPlaneTargetBlocks, d.c));
+    const long long passes_per_wg = std::max<long long>(1, cdiv(passes, want_per_chan));
+    a.NB = (int)(passes_per_wg * a.PB);
+    a.nblk = cdiv(d.n, a.NB);
+    return true;
+}
+
+// ---------------------------------------------------------------------------
 // Plane-resident weight gradient of the levels (small planes)
 // ---------------------------------------------------------------------------
 
@@ -560,9 +712,48 @@ int run_fused_forward(const wtconv_desc &d, FusedArgs a, const void *x, const fl
     }
 }
 
+template <int K, typename T, int CW>
+int launch_plane_rh(const PlaneCfg &cfg, const dim3 &grid, size_t shm, hipStream_t st, const PlaneArgs &a) {
+    const int bf = std::is_same<T, uint16_t>::value;
+    switch (cfg.RH) {
+        case 7: return launch("plane_fwd", K, bf, 0, plane_fwd_kernel<K, T, CW, 7>, grid, dim3(kPlaneThreads), shm, st, a);
+        case 4: return launch("plane_fwd", K, bf, 0, plane_fwd_kernel<K, T, CW, 4>, grid, dim3(kPlaneThreads), shm, st, a);
+        default: return launch("plane_fwd", K, bf, 0, plane_fwd_kernel<K, T, CW, 8>, grid, dim3(kPlaneThreads), shm, st, a);
+    }
+}
+
+template <int K, typename T>
+int run_plane_forward(const wtconv_desc &d, PlaneArgs a, const PlaneCfg &cfg, const void *x, const float *w0,
+                      const float *b0, const float *s0, const float *wl, const float *sl, void *y, hipStream_t st,
+                      int rotate) {
+    a.x = x;
+    a.y = y;
+    a.w0 = w0;
+    a.b0 = b0;
+    a.s0 = s0;
+    a.wl = wl;
+    a.sl = sl;
+    a.rotate = rotate;
+    a.vec = d.w % (2 * cfg.CW) == 0 && aligned(x, 2 * cfg.CW * sizeof(T)) ? 1 : 0;
+    a.pair_store = d.w % 2 == 0 && aligned(y, 2 * sizeof(T)) ? 1 : 0;
+    const dim3 grid((unsigned)((long long)d.c * a.nblk));
+    const size_t shm = (size_t)a.lds_floats * sizeof(float);
+    switch (cfg.CW) {
+        case 4: return launch_plane_rh<K, T, 4>(cfg, grid, shm, st, a);
+        case 2: return launch_plane_rh<K, T, 2>(cfg, grid, shm, st, a);
+        default: return launch_plane_rh<K, T, 1>(cfg, grid, shm, st, a);
+    }
+}
+
 template <int K, typename T>
 int run_forward(const wtconv_desc &d, const void *x, const float *w0, const float *b0, const float *s0,
                 const float *wl, const float *sl, void *y, char *ws, hipStream_t st, int rotate) {
+    {
+        PlaneArgs pa{};
+        PlaneCfg cfg{};
+        if (plan_plane(d, pa, cfg))
+            return run_plane_forward<K, T>(d, pa, cfg, x, w0, b0, s0, wl, sl, y, st, rotate);
+    }
     {
         FusedArgs fa{};
         if (plan_fused(d, vec_width(d.w, d.dtype, x), fa))
@@ -842,7 +1033,11 @@ int wtconv_plan_launches(const wtconv_desc *desc, int op, wtconv_launch *out, in
     if (op != WTCONV_OP_BACKWARD_WEIGHT) {
         if (!empty(d)) {
             FusedArgs fa{};
-            if (plan_fused(d, vec_width(d.w, d.dtype, aligned_ptr), fa)) {
+            PlaneArgs pa{};
+            PlaneCfg cfg{};
+            if (plan_plane(d, pa, cfg)) {
+                add("plane_fwd", 0, (long long)d.c * pa.nblk, kPlaneThreads, (size_t)pa.lds_floats * sizeof(float));
+            } else if (plan_fused(d, vec_width(d.w, d.dtype, aligned_ptr), fa)) {
                 add("fused_fwd", 0, (long long)d.c * fa.nblk, kThreads, (size_t)fa.lds_floats * sizeof(float));
             } else {
                 const FwdPlan p = plan_forward(d);

@@ -1,0 +1,446 @@
+// Plane-resident forward kernel of the WTConv layer on the polyphase grid.
+//
+// Paper: "Fast and Memory-Efficient Wavelet Convolutions via I/O-Aware
+// Reformulation", §4.  The layer output is the base conv plus, for every level,
+// the level's filtered coefficients mapped back to pixels by the closed-form
+// synthesis (§4.2, Prop. 2 / Eq. 7): pixel (y, x) takes from level l the sign
+// pattern of the block at (y >> l, x >> l) selected by bit l-1 of y and of x.
+// The kernel keeps a whole plane and its pyramid in LDS and moves only x in and y
+// out (2N elements per pass).
+//
+// Layout.  Everything lives on the level-1 grid (one cell per 2 x 2 pixel block):
+//   X_{py,px}[i][j] = x[2i+py][2j+px]   the four polyphase components of x;
+//   S1_b[i][j]                           the unscaled Haar bands of level 1 (Eq. 5
+//                                        without its factor 1/2, so S_l = 2^l Y_l);
+// deeper levels l >= 2 keep their unscaled bands S_l and, after filtering, their
+// sign patterns Q_l (four per block, at level l-1 resolution: Q_l[2a+ry][2b+rx]).
+// Each array has a zero halo of R = (K-1)/2 cells and a row stride chosen so that
+// the lanes of a wavefront, which take consecutive items, hit consecutive banks.
+// Small planes are placed side by side, PB per pass, with zero columns between
+// them at least R wide at every level, so that each pass fills the workgroup.
+//
+// One workgroup (128 threads) owns one channel and walks a range of its planes:
+//   1. commit: the prefetched 2 x 2CW pixel patches become X and S1 (the level-1
+//      butterflies are done in registers); the loads of the next pass are issued;
+//   2. Haar analysis of levels 2..L from the low-pass band of the level above;
+//   3. deep levels: one item is one column x 4 rows of all four bands of one level
+//      (each wavefront stays on one level, so the weights are wave-uniform and are
+//      read with scalar loads); the filtered bands are scaled by s(l) 4^-l (the
+//      scale of Eq. 8, the 2^-l of S_l and the 2^-l synthesis weight of Eq. 7), and
+//      their four sign patterns (Eq. 12/13) are written to Q_l;
+//   4. final: one item is one level-1 column x RH level-1 rows, i.e. a 2-pixel x
+//      2RH-pixel tile.  The lane filters the four level-1 bands, adds the deeper
+//      levels' patterns and the bias to the low-pass band (it enters all four sign
+//      patterns with a plus sign), forms the patterns (the level-1 synthesis), then
+//      runs the base conv over the polyphase components and stores
+//      y = s0 (W0 * x) + patterns, two adjacent pixels per store.
+// With rotate = 1 (and no bias) the same kernel computes the input gradient
+// (each kernel turned by 180 degrees, Prop. 1 / Eq. 1).
+
+#pragma once
+
+#include "wtconv_kernels.hpp"
+
+namespace wtc {
+
+constexpr int kPlaneThreads = 128;
+constexpr int kPlaneCO = 4;         // first data cell of every grid row (left halo)
+constexpr int kPlaneRHd = 4;        // level rows of a deep-level item
+constexpr int kPlaneMaxWords = 16;  // prefetch registers per thread
+
+// Exact n / d for 0 <= n < 2^16 and 1 <= d < 2^15 with m = ceil(2^31 / d): one
+// multiply-high and no special case for d = 1 (checked exhaustively on the host).
+__device__ __forceinline__ int udiv16(int n, uint32_t m) { return (int)__umulhi((uint32_t)n << 1, m); }
+
+struct PlaneArgs {
+    const void *x;
+    void *y;
+    const float *w0, *b0, *s0, *wl, *sl;
+    int n, C, H, W, L;
+    int rotate;
+    int vec;               // x rows are read with vector loads (W % 2CW == 0, aligned)
+    int pair_store;        // y is written two pixels per store (W even, aligned)
+    int NB, nblk;          // images per workgroup, workgroups per channel
+    int PB, Pw1;           // planes per pass (side by side), level-1 column pitch between them
+    int H1, W1;            // level-1 grid of one plane
+    int S1;                // level-1 strips of RH rows
+    int sy1, a1;           // level-1 grid: row stride and size in cells; X at cell 0, S1 at cell a1
+    int Gw;                // commit column groups of CW cells per level-1 row
+    int commit_items;      // PB * H1 * Gw
+    int final_items;       // S1 * PB * W1
+    // deep levels l = 2..L at index l - 2
+    int hl[kMaxLevels], wls[kMaxLevels];   // grid rows, width of the side-by-side row
+    int sd[kMaxLevels];                    // strips of kPlaneRHd rows
+    int syd[kMaxLevels], offd[kMaxLevels];  // bands: row stride (cells), offset (cells)
+    int sq[kMaxLevels], offq[kMaxLevels];  // sign patterns: row stride (floats), offset (floats)
+    int units[kMaxLevels + 1];             // cumulative 64-item units of the deep levels
+    int wt;                                // weight table (floats)
+    int lds_floats;
+    uint32_t m_gw, m_h1, m_strip, m_w1;    // udiv16 reciprocals of Gw, H1, PB*W1, W1
+    uint32_t m_wls[kMaxLevels];            // ... of the deep widths
+};
+
+// Raw words of one commit item: two pixel rows of 2CW elements.
+template <typename T, int CW>
+struct PatchIO {
+    static constexpr int kWords = sizeof(T) == 2 ? CW : 2 * CW;  // per row
+
+    __device__ __forceinline__ static void load_row(uint32_t *r, const T *src, bool vec, int col0, int W) {
+        if (vec) {
+            if constexpr (sizeof(T) * 2 * CW == 32) {
+                const uint4 q0 = reinterpret_cast<const uint4 *>(src)[0];
+                const uint4 q1 = reinterpret_cast<const uint4 *>(src)[1];
+                r[0] = q0.x; r[1] = q0.y; r[2] = q0.z; r[3] = q0.w;
+                r[4] = q1.x; r[5] = q1.y; r[6] = q1.z; r[7] = q1.w;
+            } else if constexpr (sizeof(T) * 2 * CW == 16) {
+                const uint4 q = *reinterpret_cast<const uint4 *>(src);
+                r[0] = q.x; r[1] = q.y; r[2] = q.z; r[3] = q.w;
+            } else if constexpr (sizeof(T) * 2 * CW == 8) {
+                const uint2 q = *reinterpret_cast<const uint2 *>(src);
+                r[0] = q.x; r[1] = q.y;
+            } else {
+                r[0] = *reinterpret_cast<const uint32_t *>(src);
+            }
+        } else {
+#pragma unroll
+            for (int e = 0; e < 2 * CW; ++e) {
+                uint32_t v = 0;
+                if (col0 + e < W) {
+                    if constexpr (sizeof(T) == 2) v = reinterpret_cast<const uint16_t *>(src)[e];
+                    else v = reinterpret_cast<const uint32_t *>(src)[e];
+                }
+                if constexpr (sizeof(T) == 2) {
+                    if (e & 1) r[e >> 1] |= v << 16;
+                    else r[e >> 1] = v;
+                } else {
+                    r[e] = v;
+                }
+            }
+        }
+    }
+
+    __device__ __forceinline__ static float elem(const uint32_t *r, int e) {
+        if constexpr (sizeof(T) == 2) {
+            const uint32_t wv = r[e >> 1];
+            return __uint_as_float((e & 1) ? (wv & 0xffff0000u) : (wv << 16));
+        } else {
+            return __uint_as_float(r[e]);
+        }
+    }
+};
+
+// One commit item: patch rows 2i, 2i+1 of plane p, level-1 cells [CW m, CW m + CW):
+// the polyphase components and the level-1 butterflies of each cell.
+template <int K, typename T, int CW>
+__device__ __forceinline__ void commit_patch(float4 *s4, int sy1, int a1, int pw1,
+                                             const uint32_t (&raw)[2][PatchIO<T, CW>::kWords], int p, int i, int m) {
+    constexpr int R = (K - 1) / 2;
+    using IO = PatchIO<T, CW>;
+    float4 *d = s4 + (i + R) * sy1 + kPlaneCO + p * pw1 + m * CW;
+#pragma unroll
+    for (int q = 0; q < CW; ++q) {
+        const float x00 = IO::elem(raw[0], 2 * q), x01 = IO::elem(raw[0], 2 * q + 1);
+        const float x10 = IO::elem(raw[1], 2 * q), x11 = IO::elem(raw[1], 2 * q + 1);
+        const float s0 = x00 + x01, s1 = x10 + x11, d0 = x00 - x01, d1 = x10 - x11;
+        d[q] = make_float4(x00, x01, x10, x11);
+        d[a1 + q] = make_float4(s0 + s1, s0 - s1, d0 + d1, d0 - d1);
+    }
+}
+
+// Wave-uniform value made opaque to the optimizer: what is computed from it is
+// computed after this point, inside the current phase, instead of being held in
+// scalar registers from the top of the kernel.
+__device__ __forceinline__ int opaque(int v) {
+    v = __builtin_amdgcn_readfirstlane(v);
+    asm volatile("" : "+s"(v));
+    return v;
+}
+
+// z[b][i] += sum_{u,v} wt[v][u].b * win[(i + u) * stride + v].b for the four bands b.
+// The tap-column loop stays rolled: unrolled, the compiler issues the reads of every
+// column up front and runs out of registers.
+template <int K, int RH>
+__device__ __forceinline__ void conv_bands(const float4 *win, int stride, const float4 *wt, float (&z)[4][RH]) {
+#pragma unroll 1
+    for (int v = 0; v < K; ++v) {
+        float4 wb[K];
+#pragma unroll
+        for (int u = 0; u < K; ++u) wb[u] = wt[v * K + u];
+        float4 cl[RH + K - 1];
+#pragma unroll
+        for (int t = 0; t < RH + K - 1; ++t) cl[t] = win[t * stride + v];
+#pragma unroll
+        for (int u = 0; u < K; ++u)
+#pragma unroll
+            for (int i = 0; i < RH; ++i) {
+                z[0][i] = fmaf(wb[u].x, cl[i + u].x, z[0][i]);
+                z[1][i] = fmaf(wb[u].y, cl[i + u].y, z[1][i]);
+                z[2][i] = fmaf(wb[u].z, cl[i + u].z, z[2][i]);
+                z[3][i] = fmaf(wb[u].w, cl[i + u].w, z[3][i]);
+            }
+    }
+}
+
+template <int K, typename T, int CW, int RH>
+__device__ __forceinline__ void plane_fwd_body(const PlaneArgs &args) {
+    constexpr int R = (K - 1) / 2, KK = K * K;
+    constexpr int RC = (R + 1) / 2;  // cells a pixel tap reaches beyond its own cell
+    constexpr int NT = kPlaneThreads;
+    using IO = PatchIO<T, CW>;
+    constexpr int SLOTS = kPlaneMaxWords / (2 * IO::kWords) > 0 ? kPlaneMaxWords / (2 * IO::kWords) : 1;
+    extern __shared__ float smem[];
+    float4 *s4 = reinterpret_cast<float4 *>(smem);
+    const PlaneArgs &a0 = args;
+    const int c = blockIdx.x % a0.C, nb = blockIdx.x / a0.C;
+    const int n_begin = nb * a0.NB, n_end = min(a0.n, n_begin + a0.NB);
+    const int tid = threadIdx.x;
+    const int HW = a0.H * a0.W, CHW = a0.C * HW, PB = a0.PB;
+    // plane (0, c); offsets below it are 32-bit (PB C H W < 2^31)
+    const T *xc = static_cast<const T *>(a0.x) + (size_t)c * HW;
+    T *yc = static_cast<T *>(a0.y) + (size_t)c * HW;
+
+    for (int i = tid * 4; i < a0.lds_floats; i += NT * 4)
+        *reinterpret_cast<float4 *>(smem + i) = make_float4(0.f, 0.f, 0.f, 0.f);
+    __syncthreads();
+    // Folded weights of this channel (kernels turned by 180 degrees for the input
+    // gradient): level l, band b: s(l,b) 4^-l W(l,b) (Eq. 8 scale, the 2^-l of the
+    // unscaled pyramid and the 2^-l synthesis weight), as [l][v][u] float4 over b;
+    // base: s0 W0 as [v][u].
+    {
+        const int L = a0.L;
+        for (int e = tid; e < (4 * L + 1) * KK; e += NT) {
+            const int lb = e / KK, tap = e - lb * KK;  // tap = v K + u (column-major)
+            const int v = tap / K, u = tap - v * K;
+            const int src = a0.rotate ? (K - 1 - u) * K + (K - 1 - v) : u * K + v;
+            if (lb < 4 * L) {
+                const int l = lb >> 2, b = lb & 3;
+                const size_t pc = ((size_t)l * a0.C + c) * 4 + b;
+                smem[a0.wt + (l * KK + tap) * 4 + b] = a0.sl[pc] * a0.wl[pc * KK + src] * ldexpf(1.0f, -2 * (l + 1));
+            } else {
+                smem[a0.wt + 4 * L * KK + tap] = a0.s0[c] * a0.w0[(size_t)c * KK + src];
+            }
+        }
+    }
+
+    // Patch (p, i, m) of commit item g: plane p, level-1 row i, cell group m.
+    auto patch_of = [&](const auto &A, int g, int &p, int &i, int &m) {
+        const int q = udiv16(g, A.m_gw);
+        m = g - q * A.Gw;
+        p = udiv16(q, A.m_h1);
+        i = q - p * A.H1;
+    };
+    auto load_patch = [&](const auto &A, uint32_t (&r)[2][IO::kWords], const T *xb, int live, int g) {
+#pragma unroll
+        for (int w = 0; w < IO::kWords; ++w) r[0][w] = r[1][w] = 0;
+        int p, i, m;
+        patch_of(A, g, p, i, m);
+        if (p >= live) return;
+        const int col0 = 2 * CW * m;
+        const T *src = xb + (p * A.C * A.H * A.W + (2 * i) * A.W + col0);
+        IO::load_row(r[0], src, A.vec, col0, A.W);
+        if (2 * i + 1 < A.H) IO::load_row(r[1], src + A.W, A.vec, col0, A.W);
+    };
+
+    uint32_t raw[SLOTS][2][IO::kWords];
+    auto prefetch = [&](const auto &A, int n0) {
+        const int live = min(A.PB, n_end - n0);
+        const T *xb = xc + (size_t)n0 * CHW;
+#pragma unroll
+        for (int k = 0; k < SLOTS; ++k) {
+            const int g = tid + k * NT;
+            if (g < A.commit_items) load_patch(A, raw[k], xb, live, g);
+        }
+    };
+    prefetch(args, n_begin);
+
+    for (int n0 = n_begin; n0 < n_end; n0 += PB) {
+        // Every argument below is read through a pointer made opaque per pass, so
+        // that nothing derived from the arguments is held in registers across passes.
+        // (The argument block is the kernel's only argument: offset 0 of its segment.)
+        const __attribute__((address_space(4))) PlaneArgs *ap =
+            (const __attribute__((address_space(4))) PlaneArgs *)__builtin_amdgcn_kernarg_segment_ptr();
+        asm volatile("" : "+s"(ap));
+        const auto &a = *ap;
+        const int live = min(PB, n_end - n0);
+        const int H = a.H, W = a.W, L = a.L;
+        __syncthreads();  // the previous pass is done with every array (and the weight table is written)
+        // 1. commit
+        {
+            const int sy1 = opaque(a.sy1), a1 = opaque(a.a1), pw1 = opaque(a.Pw1);
+#pragma unroll
+            for (int k = 0; k < SLOTS; ++k) {
+                const int g = tid + k * NT;
+                if (g >= a.commit_items) continue;
+                int p, i, m;
+                patch_of(a, g, p, i, m);
+                commit_patch<K, T, CW>(s4, sy1, a1, pw1, raw[k], p, i, m);
+            }
+            const T *xb = xc + (size_t)n0 * CHW;
+            for (int g = tid + SLOTS * NT; g < a.commit_items; g += NT) {  // beyond the prefetch registers
+                uint32_t r[2][IO::kWords];
+                load_patch(a, r, xb, live, g);
+                int p, i, m;
+                patch_of(a, g, p, i, m);
+                commit_patch<K, T, CW>(s4, sy1, a1, pw1, r, p, i, m);
+            }
+        }
+        __syncthreads();
+        if (n0 + PB < n_end) prefetch(a, n0 + PB);
+
+        // 2. Haar analysis of levels 2..L (unscaled butterflies of the low-pass band)
+        for (int l = 2; l <= L; ++l) {
+            const int li = l - 2, Wls = a.wls[li];
+            const float4 *src = s4 + (l == 2 ? a.a1 : a.offd[li - 1]);
+            const int ss = l == 2 ? a.sy1 : a.syd[li - 1];
+            float4 *dst = s4 + a.offd[li];
+            const int ds = a.syd[li];
+            for (int q = tid; q < a.hl[li] * Wls; q += NT) {
+                const int i = udiv16(q, a.m_wls[li]), j = q - i * Wls;
+                const float4 *sp = src + (2 * i + R) * ss + 2 * j + kPlaneCO;
+                const float x00 = sp[0].x, x01 = sp[1].x, x10 = sp[ss].x, x11 = sp[ss + 1].x;
+                const float s0 = x00 + x01, s1 = x10 + x11, d0 = x00 - x01, d1 = x10 - x11;
+                dst[(i + R) * ds + j + kPlaneCO] = make_float4(s0 + s1, s0 - s1, d0 + d1, d0 - d1);
+            }
+            __syncthreads();
+        }
+
+        // 3. deep levels: filtered bands -> sign patterns Q_l
+        if (L >= 2) {
+            const int wave = tid >> 6, lane = tid & 63;
+            for (int u = wave; u < a.units[L - 1]; u += NT / 64) {
+                int li = 0;
+                while (u >= a.units[li + 1]) ++li;
+                li = __builtin_amdgcn_readfirstlane(li);
+                const int item = (u - a.units[li]) * 64 + lane, Wls = a.wls[li];
+                const int s = udiv16(item, a.m_wls[li]), j = item - s * Wls;
+                if (s < a.sd[li]) {
+                    const int syd = opaque(a.syd[li]);
+                    float z[4][kPlaneRHd];
+#pragma unroll
+                    for (int b = 0; b < 4; ++b)
+#pragma unroll
+                        for (int i = 0; i < kPlaneRHd; ++i) z[b][i] = 0.f;
+                    conv_bands<K, kPlaneRHd>(s4 + a.offd[li] + (s * kPlaneRHd) * syd + j + kPlaneCO - R, syd,
+                                             s4 + (opaque(a.wt) >> 2) + (li + 1) * KK, z);
+                    const int sq = a.sq[li];
+                    float *q = smem + a.offq[li] + 2 * j;
+#pragma unroll
+                    for (int i = 0; i < kPlaneRHd; ++i) {
+                        const int row = s * kPlaneRHd + i;
+                        if (row >= a.hl[li]) break;
+                        const float a0v = z[0][i] + z[1][i], a1v = z[0][i] - z[1][i];
+                        const float b0 = z[2][i] + z[3][i], b1 = z[2][i] - z[3][i];
+                        *reinterpret_cast<float2 *>(q + (2 * row) * sq) = make_float2(a0v + b0, a0v - b0);
+                        *reinterpret_cast<float2 *>(q + (2 * row + 1) * sq) = make_float2(a1v + b1, a1v - b1);
+                    }
+                }
+            }
+            __syncthreads();
+        }
+
+        // 4. level 1 + deeper patterns + base conv, one store per pixel pair
+        {
+            const float bias = a.b0 ? a.s0[c] * a.b0[c] : 0.f;
+            T *yb = yc + (size_t)n0 * CHW;
+            for (int t = tid; t < a.final_items; t += NT) {
+                // opaque per item: the weight-table reads stay next to their use
+                const int sy1 = opaque(a.sy1), a1 = opaque(a.a1), wt = opaque(a.wt);
+                const int s = udiv16(t, a.m_strip), r = t - s * (PB * a.W1);
+                const int p = udiv16(r, a.m_w1), j = r - p * a.W1;
+                const int col = p * a.Pw1 + j, row0 = s * RH;
+                float z[4][RH];
+#pragma unroll
+                for (int b = 0; b < 4; ++b)
+#pragma unroll
+                    for (int i = 0; i < RH; ++i) z[b][i] = 0.f;
+                conv_bands<K, RH>(s4 + a1 + row0 * sy1 + col + kPlaneCO - R, sy1, s4 + (wt >> 2), z);
+                // deeper levels' patterns and the bias enter through the low-pass band
+#pragma unroll
+                for (int i = 0; i < RH; ++i) {
+                    float tv = bias;
+                    const int r1 = min(row0 + i, a.H1 - 1);
+                    for (int l = 2; l <= L; ++l)
+                        tv += smem[a.offq[l - 2] + (r1 >> (l - 2)) * a.sq[l - 2] + (col >> (l - 2))];
+                    z[0][i] += tv;
+                }
+                // level-1 synthesis: slot (ry, rx) = LL +- LH +- HL +- HH
+                float P[2][2][RH];
+#pragma unroll
+                for (int i = 0; i < RH; ++i) {
+                    const float a0v = z[0][i] + z[1][i], a1v = z[0][i] - z[1][i];
+                    const float b0 = z[2][i] + z[3][i], b1 = z[2][i] - z[3][i];
+                    P[0][0][i] = a0v + b0;
+                    P[0][1][i] = a0v - b0;
+                    P[1][0][i] = a1v + b1;
+                    P[1][1][i] = a1v - b1;
+                }
+                // base conv over the polyphase components, accumulated onto the patterns:
+                // output (2i+ry, 2j+rx), tap (u, v) reads pixel (2i+ry+u-R, 2j+rx+v-R),
+                // i.e. component (py, px) of cell (i + di, j + dj)
+                const float4 *xw = s4 + (row0 + R - RC) * sy1 + col + kPlaneCO;
+                const float *w0 = smem + wt + 4 * L * KK;
+#pragma unroll 1
+                for (int dj = -RC; dj <= RC; ++dj) {  // rolled, for the same reason as conv_bands
+                    float4 cl[RH + 2 * RC];
+#pragma unroll
+                    for (int tt = 0; tt < RH + 2 * RC; ++tt) cl[tt] = xw[tt * sy1 + dj];
+#pragma unroll
+                    for (int px = 0; px < 2; ++px)
+#pragma unroll
+                        for (int rx = 0; rx < 2; ++rx) {
+                            const int v = 2 * dj + px - rx + R;
+                            if (v < 0 || v >= K) continue;
+                            float wv[K];
+#pragma unroll
+                            for (int u = 0; u < K; ++u) wv[u] = w0[v * K + u];
+#pragma unroll
+                            for (int py = 0; py < 2; ++py)
+#pragma unroll
+                                for (int ry = 0; ry < 2; ++ry)
+#pragma unroll
+                                    for (int u = 0; u < K; ++u) {
+                                        const int e = ry + u - R;
+                                        if ((e & 1) != py) continue;
+                                        const int di = (e - py) / 2;
+#pragma unroll
+                                        for (int i = 0; i < RH; ++i) {
+                                            const float4 q = cl[i + di + RC];
+                                            const float xv = py == 0 ? (px == 0 ? q.x : q.y) : (px == 0 ? q.z : q.w);
+                                            P[ry][rx][i] = fmaf(wv[u], xv, P[ry][rx][i]);
+                                        }
+                                    }
+                        }
+                }
+                if (p < live) {
+                    T *yp = yb + (p * CHW + 2 * j);
+#pragma unroll
+                    for (int i = 0; i < RH; ++i) {
+                        if (row0 + i >= a.H1) break;
+#pragma unroll
+                        for (int ry = 0; ry < 2; ++ry) {
+                            const int pr = 2 * (row0 + i) + ry;
+                            if (pr >= H) break;
+                            T *dst = yp + pr * W;
+                            if (a.pair_store) {
+                                if constexpr (sizeof(T) == 2)
+                                    *reinterpret_cast<uint32_t *>(dst) = f32x2_to_bf16x2(P[ry][0][i], P[ry][1][i]);
+                                else
+                                    *reinterpret_cast<float2 *>(dst) = make_float2(P[ry][0][i], P[ry][1][i]);
+                            } else {
+                                act_store(dst, 0, P[ry][0][i]);
+                                if (2 * j + 1 < W) act_store(dst, 1, P[ry][1][i]);
+                            }
+                        }
+                    }
+                }
+            }
+        }
+    }
+}
+
+template <int K, typename T, int CW, int RH>
+__global__ __launch_bounds__(kPlaneThreads, 3) void plane_fwd_kernel(PlaneArgs a) {
+    plane_fwd_body<K, T, CW, RH>(a);
+}
+
+}  // namespace wtc

@@ -10,7 +10,8 @@ re-reads are not counted (they are O(C k^2) or cache hits).
 Per launch, with E = element size, P = n*C planes, H_l x W_l the level-l grid,
 B_l = P*H_l*W_l coefficient blocks of level l:
   Plane-resident kernels (the whole pyramid of a plane stays in LDS):
-  fused_fwd    : reads x (N), writes y (N).  FLOPs: the per-level kernels' total,
+  fused_fwd,
+  plane_fwd    : read x (N), write y (N).  FLOPs: the per-level kernels' total,
                  sum_l B_l*(8k^2 + 20) + N*(2k^2 + L).
   fused_dw     : reads x and dy (2N).  FLOPs: sum_l B_l*(8k^2 + 16).
   Per-level kernels:
@@ -47,7 +48,7 @@ def kernel_cost(family, level, n, c, h, w, k, levels, elem_bytes):
     E = elem_bytes
     hs, ws = level_sizes(h, w, levels)
     blocks = [P * hs[l] * ws[l] for l in range(levels + 1)]
-    if family == "fused_fwd":
+    if family in ("fused_fwd", "plane_fwd"):
         fl = sum(blocks[l] * (8 * k * k + 20) for l in range(1, levels + 1)) + N * (2 * k * k + levels)
         return E * 2 * N, fl
     if family == "fused_dw":
