@@ -333,8 +333,7 @@ bool plan_fused(const wtconv_desc &d, int VE, FusedArgs &a) {
 // Plane-resident forward on the polyphase grid: layout, stacking, bank-aware strides
 // ---------------------------------------------------------------------------
 
-constexpr int kPlaneLdsBudget = 53248;   // three workgroups per compute unit
-constexpr int kPlaneTargetBlocks = 768;  // three per compute unit
+constexpr int kPlaneLdsBudget = 40960;  // four workgroups per compute unit
 
 struct PlaneCfg {
     int CW = 1, RH = 8;
@@ -407,9 +406,8 @@ bool plane_layout(const wtconv_desc &d, const PlaneCfg &cfg, int pb, PlaneArgs &
         }
     }
     a.a1 = (a.S1 * RH + 2 * R) * a.sy1;
-    long long cells = 2LL * a.a1;
-    int units = 0;
-    a.units[0] = 0;
+    long long cells = a.a1;
+    int deep = 0;
     for (int l = 2; l <= L; ++l) {
         const int li = l - 2;
         a.hl[li] = hs[l];
@@ -418,9 +416,9 @@ bool plane_layout(const wtconv_desc &d, const PlaneCfg &cfg, int pb, PlaneArgs &
         a.syd[li] = kPlaneCO + a.wls[li] + R;
         a.offd[li] = (int)cells;
         cells += (long long)(a.sd[li] * kPlaneRHd + 2 * R) * a.syd[li];
-        units += cdiv((long long)a.sd[li] * a.wls[li], 64);
-        a.units[li + 1] = units;
-        if ((long long)a.hl[li] * a.wls[li] >= 32768) return false;
+        deep += a.sd[li] * a.wls[li];
+        a.dend[li] = deep;
+        if ((long long)a.hl[li] * a.wls[li] >= 32768 || deep >= 32768) return false;
     }
     long long fl = 4 * cells;  // floats
     for (int l = 2; l <= L; ++l) {
@@ -458,10 +456,12 @@ bool plan_plane(const wtconv_desc &d, PlaneArgs &a, PlaneCfg &cfg) {
             if (pb == 1) return false;
             break;
         }
-        // wave-instructions per pass: a final item is ~2 (4 + 1) RH K^2 FMAs, a deep
-        // item 4 kPlaneRHd K^2; commit and Haar ~30 per item; ~400 fixed
-        const double fin = cdiv(t.final_items, kPlaneThreads) * 2.0 * (8.0 * cfg.RH * K * K / 2 + 40.0 * cfg.RH);
-        const double deep = cdiv(t.units[d.levels - 1], kPlaneThreads / 64) * (4.0 * kPlaneRHd * K * K + 60.0);
+        // wave-instructions per pass: a final item is ~(4 + 4) RH K^2 FMAs plus
+        // ~60 RH others, a deep item 4 kPlaneRHd K^2; commit and Haar ~30 per item;
+        // ~400 fixed
+        const double fin = cdiv(t.final_items, kPlaneThreads) * 2.0 * (8.0 * cfg.RH * K * K + 60.0 * cfg.RH);
+        const int deep_items = d.levels >= 2 ? t.dend[d.levels - 2] : 0;
+        const double deep = cdiv(deep_items, kPlaneThreads) * 2.0 * (4.0 * kPlaneRHd * K * K + 60.0);
         const double misc = cdiv(t.commit_items, kPlaneThreads) * 40.0 + 400.0;
         const double cost = (fin + deep + misc) / pb;
         if (cost < best - 1e-9) {
@@ -470,11 +470,10 @@ bool plan_plane(const wtconv_desc &d, PlaneArgs &a, PlaneCfg &cfg) {
         }
     }
     if (!plane_layout(d, cfg, best_pb, a)) return false;
-    const long long passes = cdiv(d.n, a.PB);
-    const long long want_per_chan = std::max<long long>(1, cdiv(kPlaneTargetBlocks, d.c));
-    const long long passes_per_wg = std::max<long long>(1, cdiv(passes, want_per_chan));
-    a.NB = (int)(passes_per_wg * a.PB);
-    a.nblk = cdiv(d.n, a.NB);
+    a.NG = cdiv(d.n, a.PB);
+    const long long units = (long long)d.c * a.NG;
+    if (units >= (1LL << 31)) return false;
+    a.U = (int)units;
     return true;
 }
 
@@ -713,13 +712,45 @@ int run_fused_forward(const wtconv_desc &d, FusedArgs a, const void *x, const fl
 }
 
 template <int K, typename T, int CW>
-int launch_plane_rh(const PlaneCfg &cfg, const dim3 &grid, size_t shm, hipStream_t st, const PlaneArgs &a) {
-    const int bf = std::is_same<T, uint16_t>::value;
-    switch (cfg.RH) {
-        case 7: return launch("plane_fwd", K, bf, 0, plane_fwd_kernel<K, T, CW, 7>, grid, dim3(kPlaneThreads), shm, st, a);
-        case 4: return launch("plane_fwd", K, bf, 0, plane_fwd_kernel<K, T, CW, 4>, grid, dim3(kPlaneThreads), shm, st, a);
-        default: return launch("plane_fwd", K, bf, 0, plane_fwd_kernel<K, T, CW, 8>, grid, dim3(kPlaneThreads), shm, st, a);
+const void *plane_kernel_rh(int RH) {
+    switch (RH) {
+        case 7: return reinterpret_cast<const void *>(plane_fwd_kernel<K, T, CW, 7>);
+        case 4: return reinterpret_cast<const void *>(plane_fwd_kernel<K, T, CW, 4>);
+        default: return reinterpret_cast<const void *>(plane_fwd_kernel<K, T, CW, 8>);
     }
+}
+
+template <int K, typename T>
+const void *plane_kernel(const PlaneCfg &cfg) {
+    switch (cfg.CW) {
+        case 4: return plane_kernel_rh<K, T, 4>(cfg.RH);
+        case 2: return plane_kernel_rh<K, T, 2>(cfg.RH);
+        default: return plane_kernel_rh<K, T, 1>(cfg.RH);
+    }
+}
+
+const void *plane_kernel_for(const wtconv_desc &d, const PlaneCfg &cfg) {
+    const bool bf = d.dtype == WTCONV_BF16;
+    switch (d.k) {
+        case 3: return bf ? plane_kernel<3, uint16_t>(cfg) : plane_kernel<3, float>(cfg);
+        case 5: return bf ? plane_kernel<5, uint16_t>(cfg) : plane_kernel<5, float>(cfg);
+        default: return bf ? plane_kernel<7, uint16_t>(cfg) : plane_kernel<7, float>(cfg);
+    }
+}
+
+// Persistent grid: as many workgroups as can be resident at once on the current
+// device (they stride over the units), never more than the units.
+int plane_grid(const wtconv_desc &d, const PlaneArgs &a, const PlaneCfg &cfg) {
+    int dev = 0, cus = 0, per_cu = 0;
+    const size_t shm = (size_t)a.lds_floats * sizeof(float);
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, plane_kernel_for(d, cfg), kPlaneThreads, shm) != hipSuccess ||
+        cus <= 0 || per_cu <= 0) {
+        (void)hipGetLastError();
+        cus = 256;
+        per_cu = std::max(1, std::min(4, (int)((160 * 1024) / std::max<size_t>(shm, 1))));
+    }
+    return (int)std::min<long long>(a.U, (long long)cus * per_cu);
 }
 
 template <int K, typename T>
@@ -736,13 +767,23 @@ int run_plane_forward(const wtconv_desc &d, PlaneArgs a, const PlaneCfg &cfg, co
     a.rotate = rotate;
     a.vec = d.w % (2 * cfg.CW) == 0 && aligned(x, 2 * cfg.CW * sizeof(T)) ? 1 : 0;
     a.pair_store = d.w % 2 == 0 && aligned(y, 2 * sizeof(T)) ? 1 : 0;
-    const dim3 grid((unsigned)((long long)d.c * a.nblk));
+    const dim3 grid((unsigned)plane_grid(d, a, cfg));
     const size_t shm = (size_t)a.lds_floats * sizeof(float);
-    switch (cfg.CW) {
-        case 4: return launch_plane_rh<K, T, 4>(cfg, grid, shm, st, a);
-        case 2: return launch_plane_rh<K, T, 2>(cfg, grid, shm, st, a);
-        default: return launch_plane_rh<K, T, 1>(cfg, grid, shm, st, a);
+    const int bf = std::is_same<T, uint16_t>::value;
+#define WTC_PLANE_LAUNCH(CW_, RH_) \
+    launch("plane_fwd", K, bf, 0, plane_fwd_kernel<K, T, CW_, RH_>, grid, dim3(kPlaneThreads), shm, st, a)
+    switch (cfg.CW * 16 + cfg.RH) {
+        case 4 * 16 + 7: return WTC_PLANE_LAUNCH(4, 7);
+        case 4 * 16 + 4: return WTC_PLANE_LAUNCH(4, 4);
+        case 4 * 16 + 8: return WTC_PLANE_LAUNCH(4, 8);
+        case 2 * 16 + 7: return WTC_PLANE_LAUNCH(2, 7);
+        case 2 * 16 + 4: return WTC_PLANE_LAUNCH(2, 4);
+        case 2 * 16 + 8: return WTC_PLANE_LAUNCH(2, 8);
+        case 1 * 16 + 7: return WTC_PLANE_LAUNCH(1, 7);
+        case 1 * 16 + 4: return WTC_PLANE_LAUNCH(1, 4);
+        default: return WTC_PLANE_LAUNCH(1, 8);
     }
+#undef WTC_PLANE_LAUNCH
 }
 
 template <int K, typename T>
@@ -1036,7 +1077,7 @@ int wtconv_plan_launches(const wtconv_desc *desc, int op, wtconv_launch *out, in
             PlaneArgs pa{};
             PlaneCfg cfg{};
             if (plan_plane(d, pa, cfg)) {
-                add("plane_fwd", 0, (long long)d.c * pa.nblk, kPlaneThreads, (size_t)pa.lds_floats * sizeof(float));
+                add("plane_fwd", 0, plane_grid(d, pa, cfg), kPlaneThreads, (size_t)pa.lds_floats * sizeof(float));
             } else if (plan_fused(d, vec_width(d.w, d.dtype, aligned_ptr), fa)) {
                 add("fused_fwd", 0, (long long)d.c * fa.nblk, kThreads, (size_t)fa.lds_floats * sizeof(float));
             } else {

@@ -8,32 +8,35 @@
 // The kernel keeps a whole plane and its pyramid in LDS and moves only x in and y
 // out (2N elements per pass).
 //
-// Layout.  Everything lives on the level-1 grid (one cell per 2 x 2 pixel block):
-//   X_{py,px}[i][j] = x[2i+py][2j+px]   the four polyphase components of x;
-//   S1_b[i][j]                           the unscaled Haar bands of level 1 (Eq. 5
-//                                        without its factor 1/2, so S_l = 2^l Y_l);
-// deeper levels l >= 2 keep their unscaled bands S_l and, after filtering, their
-// sign patterns Q_l (four per block, at level l-1 resolution: Q_l[2a+ry][2b+rx]).
-// Each array has a zero halo of R = (K-1)/2 cells and a row stride chosen so that
-// the lanes of a wavefront, which take consecutive items, hit consecutive banks.
-// Small planes are placed side by side, PB per pass, with zero columns between
-// them at least R wide at every level, so that each pass fills the workgroup.
+// Layout.  Everything lives on the level-1 grid (one cell per 2 x 2 pixel block).
+// LDS holds, per cell, the four unscaled level-1 Haar bands S1 = (LL, LH, HL, HH)
+// as one float4 (Eq. 5 without its factor 1/2, so S_l = 2^l Y_l); x itself is not
+// kept: the base conv rebuilds the four pixels of a cell from its bands with the
+// inverse butterfly (Prop. 1: H^2 = I, so the synthesis is the same butterfly; its
+// factor 1/4 is folded into the base weights).  Deeper levels l >= 2 keep their
+// bands S_l (float4 per cell) and, after filtering, their sign patterns Q_l (four
+// per block, at level l-1 resolution: Q_l[2a+ry][2b+rx]).  Each array has a zero
+// halo of R = (K-1)/2 cells and a row stride chosen so that the lanes of a
+// wavefront, which take consecutive items, hit distinct banks.  Small planes are
+// placed side by side, PB per pass, with zero columns between them at least R wide
+// at every level, so that each pass fills the workgroup.
 //
 // One workgroup (128 threads) owns one channel and walks a range of its planes:
-//   1. commit: the prefetched 2 x 2CW pixel patches become X and S1 (the level-1
+//   1. commit: the prefetched 2 x 2CW pixel patches become S1 (the level-1
 //      butterflies are done in registers); the loads of the next pass are issued;
 //   2. Haar analysis of levels 2..L from the low-pass band of the level above;
-//   3. deep levels: one item is one column x 4 rows of all four bands of one level
-//      (each wavefront stays on one level, so the weights are wave-uniform and are
-//      read with scalar loads); the filtered bands are scaled by s(l) 4^-l (the
-//      scale of Eq. 8, the 2^-l of S_l and the 2^-l synthesis weight of Eq. 7), and
-//      their four sign patterns (Eq. 12/13) are written to Q_l;
+//   3. deep levels: one item is one column x 2 rows of all four bands of one level;
+//      the filtered bands (weights folded with s(l) 4^-l: the scale of Eq. 8, the
+//      2^-l of S_l and the 2^-l synthesis weight of Eq. 7) give the four sign
+//      patterns of each block (Eq. 12/13), written to Q_l;
 //   4. final: one item is one level-1 column x RH level-1 rows, i.e. a 2-pixel x
-//      2RH-pixel tile.  The lane filters the four level-1 bands, adds the deeper
-//      levels' patterns and the bias to the low-pass band (it enters all four sign
-//      patterns with a plus sign), forms the patterns (the level-1 synthesis), then
-//      runs the base conv over the polyphase components and stores
-//      y = s0 (W0 * x) + patterns, two adjacent pixels per store.
+//      2RH-pixel tile.  Walking the K columns of the level-1 window, the lane
+//      filters the four level-1 bands and, on the columns the base conv needs,
+//      rebuilds x and runs the base conv over its polyphase components; then it adds
+//      the deeper levels' patterns and the bias to the low-pass band (it enters all
+//      four sign patterns with a plus sign), forms the level-1 patterns (the
+//      level-1 synthesis) and stores y = s0 (W0 * x) + patterns, two adjacent
+//      pixels per store.
 // With rotate = 1 (and no bias) the same kernel computes the input gradient
 // (each kernel turned by 180 degrees, Prop. 1 / Eq. 1).
 
@@ -45,7 +48,7 @@ namespace wtc {
 
 constexpr int kPlaneThreads = 128;
 constexpr int kPlaneCO = 4;         // first data cell of every grid row (left halo)
-constexpr int kPlaneRHd = 4;        // level rows of a deep-level item
+constexpr int kPlaneRHd = 2;        // level rows of a deep-level item
 constexpr int kPlaneMaxWords = 16;  // prefetch registers per thread
 
 // Exact n / d for 0 <= n < 2^16 and 1 <= d < 2^15 with m = ceil(2^31 / d): one
@@ -60,11 +63,11 @@ struct PlaneArgs {
     int rotate;
     int vec;               // x rows are read with vector loads (W % 2CW == 0, aligned)
     int pair_store;        // y is written two pixels per store (W even, aligned)
-    int NB, nblk;          // images per workgroup, workgroups per channel
     int PB, Pw1;           // planes per pass (side by side), level-1 column pitch between them
+    int NG, U;             // image groups of PB per channel, units (C NG; a unit is one pass)
     int H1, W1;            // level-1 grid of one plane
     int S1;                // level-1 strips of RH rows
-    int sy1, a1;           // level-1 grid: row stride and size in cells; X at cell 0, S1 at cell a1
+    int sy1, a1;           // level-1 bands: row stride and size in cells (from cell 0)
     int Gw;                // commit column groups of CW cells per level-1 row
     int commit_items;      // PB * H1 * Gw
     int final_items;       // S1 * PB * W1
@@ -73,7 +76,7 @@ struct PlaneArgs {
     int sd[kMaxLevels];                    // strips of kPlaneRHd rows
     int syd[kMaxLevels], offd[kMaxLevels];  // bands: row stride (cells), offset (cells)
     int sq[kMaxLevels], offq[kMaxLevels];  // sign patterns: row stride (floats), offset (floats)
-    int units[kMaxLevels + 1];             // cumulative 64-item units of the deep levels
+    int dend[kMaxLevels];                  // cumulative deep items (strips x width) by level
     int wt;                                // weight table (floats)
     int lds_floats;
     uint32_t m_gw, m_h1, m_strip, m_w1;    // udiv16 reciprocals of Gw, H1, PB*W1, W1
@@ -130,9 +133,9 @@ struct PatchIO {
 };
 
 // One commit item: patch rows 2i, 2i+1 of plane p, level-1 cells [CW m, CW m + CW):
-// the polyphase components and the level-1 butterflies of each cell.
+// the level-1 butterflies of each cell.
 template <int K, typename T, int CW>
-__device__ __forceinline__ void commit_patch(float4 *s4, int sy1, int a1, int pw1,
+__device__ __forceinline__ void commit_patch(float4 *s4, int sy1, int pw1,
                                              const uint32_t (&raw)[2][PatchIO<T, CW>::kWords], int p, int i, int m) {
     constexpr int R = (K - 1) / 2;
     using IO = PatchIO<T, CW>;
@@ -142,8 +145,7 @@ __device__ __forceinline__ void commit_patch(float4 *s4, int sy1, int a1, int pw
         const float x00 = IO::elem(raw[0], 2 * q), x01 = IO::elem(raw[0], 2 * q + 1);
         const float x10 = IO::elem(raw[1], 2 * q), x11 = IO::elem(raw[1], 2 * q + 1);
         const float s0 = x00 + x01, s1 = x10 + x11, d0 = x00 - x01, d1 = x10 - x11;
-        d[q] = make_float4(x00, x01, x10, x11);
-        d[a1 + q] = make_float4(s0 + s1, s0 - s1, d0 + d1, d0 - d1);
+        d[q] = make_float4(s0 + s1, s0 - s1, d0 + d1, d0 - d1);
     }
 }
 
@@ -153,6 +155,11 @@ __device__ __forceinline__ void commit_patch(float4 *s4, int sy1, int a1, int pw
 __device__ __forceinline__ int opaque(int v) {
     v = __builtin_amdgcn_readfirstlane(v);
     asm volatile("" : "+s"(v));
+    return v;
+}
+// The same for a value that may differ between lanes.
+__device__ __forceinline__ int opaque_lane(int v) {
+    asm volatile("" : "+v"(v));
     return v;
 }
 
@@ -191,37 +198,19 @@ __device__ __forceinline__ void plane_fwd_body(const PlaneArgs &args) {
     extern __shared__ float smem[];
     float4 *s4 = reinterpret_cast<float4 *>(smem);
     const PlaneArgs &a0 = args;
-    const int c = blockIdx.x % a0.C, nb = blockIdx.x / a0.C;
-    const int n_begin = nb * a0.NB, n_end = min(a0.n, n_begin + a0.NB);
     const int tid = threadIdx.x;
     const int HW = a0.H * a0.W, CHW = a0.C * HW, PB = a0.PB;
-    // plane (0, c); offsets below it are 32-bit (PB C H W < 2^31)
-    const T *xc = static_cast<const T *>(a0.x) + (size_t)c * HW;
-    T *yc = static_cast<T *>(a0.y) + (size_t)c * HW;
+    constexpr int WSLOTS = 4;  // weight-table entries per thread carried in registers
 
     for (int i = tid * 4; i < a0.lds_floats; i += NT * 4)
         *reinterpret_cast<float4 *>(smem + i) = make_float4(0.f, 0.f, 0.f, 0.f);
-    __syncthreads();
-    // Folded weights of this channel (kernels turned by 180 degrees for the input
-    // gradient): level l, band b: s(l,b) 4^-l W(l,b) (Eq. 8 scale, the 2^-l of the
-    // unscaled pyramid and the 2^-l synthesis weight), as [l][v][u] float4 over b;
-    // base: s0 W0 as [v][u].
-    {
-        const int L = a0.L;
-        for (int e = tid; e < (4 * L + 1) * KK; e += NT) {
-            const int lb = e / KK, tap = e - lb * KK;  // tap = v K + u (column-major)
-            const int v = tap / K, u = tap - v * K;
-            const int src = a0.rotate ? (K - 1 - u) * K + (K - 1 - v) : u * K + v;
-            if (lb < 4 * L) {
-                const int l = lb >> 2, b = lb & 3;
-                const size_t pc = ((size_t)l * a0.C + c) * 4 + b;
-                smem[a0.wt + (l * KK + tap) * 4 + b] = a0.sl[pc] * a0.wl[pc * KK + src] * ldexpf(1.0f, -2 * (l + 1));
-            } else {
-                smem[a0.wt + 4 * L * KK + tap] = a0.s0[c] * a0.w0[(size_t)c * KK + src];
-            }
-        }
-    }
 
+    // A unit is PB images of one channel: unit u = (channel u / NG, images
+    // [(u % NG) PB, ...)).  Workgroup w takes units w, w + G, w + 2G, ...
+    auto unit_of = [&](const auto &A, int u, int &c, int &n0) {
+        c = u / A.NG;
+        n0 = (u - c * A.NG) * A.PB;
+    };
     // Patch (p, i, m) of commit item g: plane p, level-1 row i, cell group m.
     auto patch_of = [&](const auto &A, int g, int &p, int &i, int &m) {
         const int q = udiv16(g, A.m_gw);
@@ -236,24 +225,55 @@ __device__ __forceinline__ void plane_fwd_body(const PlaneArgs &args) {
         patch_of(A, g, p, i, m);
         if (p >= live) return;
         const int col0 = 2 * CW * m;
-        const T *src = xb + (p * A.C * A.H * A.W + (2 * i) * A.W + col0);
+        const T *src = xb + (p * CHW + (2 * i) * A.W + col0);
         IO::load_row(r[0], src, A.vec, col0, A.W);
         if (2 * i + 1 < A.H) IO::load_row(r[1], src + A.W, A.vec, col0, A.W);
     };
+    // Weight-table entry e of channel c: the two factors of its folded value.
+    // Level l, band b: s(l,b) 4^-l W(l,b) (Eq. 8 scale, the 2^-l of the unscaled
+    // pyramid and the 2^-l synthesis weight), as [l][v][u] float4 over b; base:
+    // s0 W0 / 4 as [v][u] (the base conv runs on 4x, rebuilt from S1).  Kernels are
+    // turned by 180 degrees for the input gradient.
+    auto weight_factors = [&](const auto &A, int c, int e, float &f0, float &f1) {
+        const int lb = e / KK, tap = e - lb * KK;  // tap = v K + u (column-major)
+        const int v = tap / K, u = tap - v * K;
+        const int src = A.rotate ? (K - 1 - u) * K + (K - 1 - v) : u * K + v;
+        if (lb < 4 * A.L) {
+            const int l = lb >> 2, b = lb & 3;
+            const size_t pc = ((size_t)l * A.C + c) * 4 + b;
+            f0 = ldexpf(A.sl[pc], -2 * (l + 1));
+            f1 = A.wl[pc * KK + src];
+        } else {
+            f0 = 0.25f * A.s0[c];
+            f1 = A.w0[(size_t)c * KK + src];
+        }
+    };
+    auto weight_slot = [&](const auto &A, int e) {  // LDS float index of entry e
+        const int lb = e / KK, tap = e - lb * KK;
+        return lb < 4 * A.L ? A.wt + ((lb >> 2) * KK + tap) * 4 + (lb & 3) : A.wt + 4 * A.L * KK + tap;
+    };
 
     uint32_t raw[SLOTS][2][IO::kWords];
-    auto prefetch = [&](const auto &A, int n0) {
-        const int live = min(A.PB, n_end - n0);
-        const T *xb = xc + (size_t)n0 * CHW;
+    float wf0[WSLOTS], wf1[WSLOTS];
+    auto prefetch = [&](const auto &A, int u) {
+        int c, n0;
+        unit_of(A, u, c, n0);
+        const int live = min(A.PB, A.n - n0);
+        const T *xb = static_cast<const T *>(A.x) + ((size_t)n0 * A.C + c) * HW;
 #pragma unroll
         for (int k = 0; k < SLOTS; ++k) {
             const int g = tid + k * NT;
             if (g < A.commit_items) load_patch(A, raw[k], xb, live, g);
         }
+#pragma unroll
+        for (int k = 0; k < WSLOTS; ++k) {
+            const int e = tid + k * NT;
+            if (e < (4 * A.L + 1) * KK) weight_factors(A, c, e, wf0[k], wf1[k]);
+        }
     };
-    prefetch(args, n_begin);
+    if ((int)blockIdx.x < a0.U) prefetch(args, blockIdx.x);
 
-    for (int n0 = n_begin; n0 < n_end; n0 += PB) {
+    for (int u = blockIdx.x; u < a0.U; u += gridDim.x) {
         // Every argument below is read through a pointer made opaque per pass, so
         // that nothing derived from the arguments is held in registers across passes.
         // (The argument block is the kernel's only argument: offset 0 of its segment.)
@@ -261,36 +281,50 @@ __device__ __forceinline__ void plane_fwd_body(const PlaneArgs &args) {
             (const __attribute__((address_space(4))) PlaneArgs *)__builtin_amdgcn_kernarg_segment_ptr();
         asm volatile("" : "+s"(ap));
         const auto &a = *ap;
-        const int live = min(PB, n_end - n0);
+        int c, n0;
+        unit_of(a, u, c, n0);
+        const int live = min(PB, a.n - n0);
         const int H = a.H, W = a.W, L = a.L;
-        __syncthreads();  // the previous pass is done with every array (and the weight table is written)
-        // 1. commit
+        __syncthreads();  // the previous pass is done with every array
+        // 1. commit: this unit's weight table and level-1 bands
         {
-            const int sy1 = opaque(a.sy1), a1 = opaque(a.a1), pw1 = opaque(a.Pw1);
+            const int nw = (4 * L + 1) * KK;
+#pragma unroll
+            for (int k = 0; k < WSLOTS; ++k) {
+                const int e = tid + k * NT;
+                if (e < nw) smem[weight_slot(a, e)] = wf0[k] * wf1[k];
+            }
+            for (int e = tid + WSLOTS * NT; e < nw; e += NT) {  // beyond the registers
+                float f0, f1;
+                weight_factors(a, c, e, f0, f1);
+                smem[weight_slot(a, e)] = f0 * f1;
+            }
+            const int sy1 = opaque(a.sy1), pw1 = opaque(a.Pw1);
 #pragma unroll
             for (int k = 0; k < SLOTS; ++k) {
                 const int g = tid + k * NT;
                 if (g >= a.commit_items) continue;
                 int p, i, m;
                 patch_of(a, g, p, i, m);
-                commit_patch<K, T, CW>(s4, sy1, a1, pw1, raw[k], p, i, m);
+                commit_patch<K, T, CW>(s4, sy1, pw1, raw[k], p, i, m);
             }
-            const T *xb = xc + (size_t)n0 * CHW;
-            for (int g = tid + SLOTS * NT; g < a.commit_items; g += NT) {  // beyond the prefetch registers
+            const T *xb = static_cast<const T *>(a.x) + ((size_t)n0 * a.C + c) * HW;
+            for (int g = tid + SLOTS * NT; g < a.commit_items; g += NT) {  // beyond the registers
                 uint32_t r[2][IO::kWords];
                 load_patch(a, r, xb, live, g);
                 int p, i, m;
                 patch_of(a, g, p, i, m);
-                commit_patch<K, T, CW>(s4, sy1, a1, pw1, r, p, i, m);
+                commit_patch<K, T, CW>(s4, sy1, pw1, r, p, i, m);
             }
         }
         __syncthreads();
-        if (n0 + PB < n_end) prefetch(a, n0 + PB);
+        if (u + (int)gridDim.x < a.U) prefetch(a, u + gridDim.x);
+        T *yb = static_cast<T *>(a.y) + ((size_t)n0 * a.C + c) * HW;
 
         // 2. Haar analysis of levels 2..L (unscaled butterflies of the low-pass band)
         for (int l = 2; l <= L; ++l) {
             const int li = l - 2, Wls = a.wls[li];
-            const float4 *src = s4 + (l == 2 ? a.a1 : a.offd[li - 1]);
+            const float4 *src = s4 + (l == 2 ? 0 : a.offd[li - 1]);
             const int ss = l == 2 ? a.sy1 : a.syd[li - 1];
             float4 *dst = s4 + a.offd[li];
             const int ds = a.syd[li];
@@ -304,95 +338,98 @@ __device__ __forceinline__ void plane_fwd_body(const PlaneArgs &args) {
             __syncthreads();
         }
 
-        // 3. deep levels: filtered bands -> sign patterns Q_l
+        // 3. deep levels: filtered bands -> sign patterns Q_l; items of all levels
+        //    are spread over all lanes
         if (L >= 2) {
-            const int wave = tid >> 6, lane = tid & 63;
-            for (int u = wave; u < a.units[L - 1]; u += NT / 64) {
+            for (int it = tid; it < a.dend[L - 2]; it += NT) {
                 int li = 0;
-                while (u >= a.units[li + 1]) ++li;
-                li = __builtin_amdgcn_readfirstlane(li);
-                const int item = (u - a.units[li]) * 64 + lane, Wls = a.wls[li];
-                const int s = udiv16(item, a.m_wls[li]), j = item - s * Wls;
-                if (s < a.sd[li]) {
-                    const int syd = opaque(a.syd[li]);
-                    float z[4][kPlaneRHd];
+                while (it >= a.dend[li]) ++li;
+                const int loc = it - (li ? a.dend[li - 1] : 0), Wls = a.wls[li];
+                const int s = udiv16(loc, a.m_wls[li]), j = loc - s * Wls;
+                const int syd = opaque_lane(a.syd[li]);  // items of several levels share a wavefront
+                float z[4][kPlaneRHd];
 #pragma unroll
-                    for (int b = 0; b < 4; ++b)
+                for (int b = 0; b < 4; ++b)
 #pragma unroll
-                        for (int i = 0; i < kPlaneRHd; ++i) z[b][i] = 0.f;
-                    conv_bands<K, kPlaneRHd>(s4 + a.offd[li] + (s * kPlaneRHd) * syd + j + kPlaneCO - R, syd,
-                                             s4 + (opaque(a.wt) >> 2) + (li + 1) * KK, z);
-                    const int sq = a.sq[li];
-                    float *q = smem + a.offq[li] + 2 * j;
+                    for (int i = 0; i < kPlaneRHd; ++i) z[b][i] = 0.f;
+                conv_bands<K, kPlaneRHd>(s4 + a.offd[li] + (s * kPlaneRHd) * syd + j + kPlaneCO - R, syd,
+                                         s4 + (opaque(a.wt) >> 2) + (li + 1) * KK, z);
+                const int sq = a.sq[li];
+                float *q = smem + a.offq[li] + 2 * j;
 #pragma unroll
-                    for (int i = 0; i < kPlaneRHd; ++i) {
-                        const int row = s * kPlaneRHd + i;
-                        if (row >= a.hl[li]) break;
-                        const float a0v = z[0][i] + z[1][i], a1v = z[0][i] - z[1][i];
-                        const float b0 = z[2][i] + z[3][i], b1 = z[2][i] - z[3][i];
-                        *reinterpret_cast<float2 *>(q + (2 * row) * sq) = make_float2(a0v + b0, a0v - b0);
-                        *reinterpret_cast<float2 *>(q + (2 * row + 1) * sq) = make_float2(a1v + b1, a1v - b1);
-                    }
+                for (int i = 0; i < kPlaneRHd; ++i) {
+                    const int row = s * kPlaneRHd + i;
+                    if (row >= a.hl[li]) break;
+                    const float a0v = z[0][i] + z[1][i], a1v = z[0][i] - z[1][i];
+                    const float b0 = z[2][i] + z[3][i], b1 = z[2][i] - z[3][i];
+                    *reinterpret_cast<float2 *>(q + (2 * row) * sq) = make_float2(a0v + b0, a0v - b0);
+                    *reinterpret_cast<float2 *>(q + (2 * row + 1) * sq) = make_float2(a1v + b1, a1v - b1);
                 }
             }
             __syncthreads();
         }
 
-        // 4. level 1 + deeper patterns + base conv, one store per pixel pair
+        // 4. level 1 + base conv + deeper patterns, one store per pixel pair
         {
             const float bias = a.b0 ? a.s0[c] * a.b0[c] : 0.f;
-            T *yb = yc + (size_t)n0 * CHW;
             for (int t = tid; t < a.final_items; t += NT) {
                 // opaque per item: the weight-table reads stay next to their use
-                const int sy1 = opaque(a.sy1), a1 = opaque(a.a1), wt = opaque(a.wt);
+                const int sy1 = opaque(a.sy1), wt = opaque(a.wt);
                 const int s = udiv16(t, a.m_strip), r = t - s * (PB * a.W1);
                 const int p = udiv16(r, a.m_w1), j = r - p * a.W1;
                 const int col = p * a.Pw1 + j, row0 = s * RH;
-                float z[4][RH];
-#pragma unroll
-                for (int b = 0; b < 4; ++b)
-#pragma unroll
-                    for (int i = 0; i < RH; ++i) z[b][i] = 0.f;
-                conv_bands<K, RH>(s4 + a1 + row0 * sy1 + col + kPlaneCO - R, sy1, s4 + (wt >> 2), z);
-                // deeper levels' patterns and the bias enter through the low-pass band
+                float z[4][RH], P[2][2][RH];
 #pragma unroll
                 for (int i = 0; i < RH; ++i) {
-                    float tv = bias;
-                    const int r1 = min(row0 + i, a.H1 - 1);
-                    for (int l = 2; l <= L; ++l)
-                        tv += smem[a.offq[l - 2] + (r1 >> (l - 2)) * a.sq[l - 2] + (col >> (l - 2))];
-                    z[0][i] += tv;
-                }
-                // level-1 synthesis: slot (ry, rx) = LL +- LH +- HL +- HH
-                float P[2][2][RH];
 #pragma unroll
-                for (int i = 0; i < RH; ++i) {
-                    const float a0v = z[0][i] + z[1][i], a1v = z[0][i] - z[1][i];
-                    const float b0 = z[2][i] + z[3][i], b1 = z[2][i] - z[3][i];
-                    P[0][0][i] = a0v + b0;
-                    P[0][1][i] = a0v - b0;
-                    P[1][0][i] = a1v + b1;
-                    P[1][1][i] = a1v - b1;
+                    for (int b = 0; b < 4; ++b) z[b][i] = 0.f;
+#pragma unroll
+                    for (int b = 0; b < 4; ++b) P[b >> 1][b & 1][i] = 0.f;
                 }
-                // base conv over the polyphase components, accumulated onto the patterns:
-                // output (2i+ry, 2j+rx), tap (u, v) reads pixel (2i+ry+u-R, 2j+rx+v-R),
-                // i.e. component (py, px) of cell (i + di, j + dj)
-                const float4 *xw = s4 + (row0 + R - RC) * sy1 + col + kPlaneCO;
+                // window cell (t, v) is level-1 cell (row0 - R + t, col - R + v)
+                const float4 *win = s4 + row0 * sy1 + col + kPlaneCO - R;
+                const float4 *wt1 = s4 + (wt >> 2);
                 const float *w0 = smem + wt + 4 * L * KK;
 #pragma unroll 1
-                for (int dj = -RC; dj <= RC; ++dj) {  // rolled, for the same reason as conv_bands
-                    float4 cl[RH + 2 * RC];
+                for (int v = 0; v < K; ++v) {  // rolled: see conv_bands
+                    float4 cl[RH + K - 1];
+                    {
+                        float4 wb[K];
 #pragma unroll
-                    for (int tt = 0; tt < RH + 2 * RC; ++tt) cl[tt] = xw[tt * sy1 + dj];
+                        for (int u = 0; u < K; ++u) wb[u] = wt1[v * K + u];
+#pragma unroll
+                        for (int tt = 0; tt < RH + K - 1; ++tt) cl[tt] = win[tt * sy1 + v];
+#pragma unroll
+                        for (int u = 0; u < K; ++u)
+#pragma unroll
+                            for (int i = 0; i < RH; ++i) {
+                                z[0][i] = fmaf(wb[u].x, cl[i + u].x, z[0][i]);
+                                z[1][i] = fmaf(wb[u].y, cl[i + u].y, z[1][i]);
+                                z[2][i] = fmaf(wb[u].z, cl[i + u].z, z[2][i]);
+                                z[3][i] = fmaf(wb[u].w, cl[i + u].w, z[3][i]);
+                            }
+                    }
+                    // base conv on the columns it reaches: output (2i+ry, 2j+rx), tap
+                    // (u, w) reads pixel (2i+ry+u-R, 2j+rx+w-R), i.e. component
+                    // (py, px) of cell (i + di, j + dj)
+                    const int dj = v - R;
+                    if (dj < -RC || dj > RC) continue;
+                    float4 xq[RH + 2 * RC];  // 4 x (x00, x01, x10, x11) by the inverse butterfly
+#pragma unroll
+                    for (int tt = 0; tt < RH + 2 * RC; ++tt) {
+                        const float4 c4 = cl[tt + R - RC];
+                        const float A = c4.x + c4.y, B = c4.x - c4.y, C = c4.z + c4.w, D = c4.z - c4.w;
+                        xq[tt] = make_float4(A + C, A - C, B + D, B - D);
+                    }
 #pragma unroll
                     for (int px = 0; px < 2; ++px)
 #pragma unroll
                         for (int rx = 0; rx < 2; ++rx) {
-                            const int v = 2 * dj + px - rx + R;
-                            if (v < 0 || v >= K) continue;
+                            const int w = 2 * dj + px - rx + R;
+                            if (w < 0 || w >= K) continue;
                             float wv[K];
 #pragma unroll
-                            for (int u = 0; u < K; ++u) wv[u] = w0[v * K + u];
+                            for (int u = 0; u < K; ++u) wv[u] = w0[w * K + u];
 #pragma unroll
                             for (int py = 0; py < 2; ++py)
 #pragma unroll
@@ -404,12 +441,31 @@ __device__ __forceinline__ void plane_fwd_body(const PlaneArgs &args) {
                                         const int di = (e - py) / 2;
 #pragma unroll
                                         for (int i = 0; i < RH; ++i) {
-                                            const float4 q = cl[i + di + RC];
+                                            const float4 q = xq[i + di + RC];
                                             const float xv = py == 0 ? (px == 0 ? q.x : q.y) : (px == 0 ? q.z : q.w);
                                             P[ry][rx][i] = fmaf(wv[u], xv, P[ry][rx][i]);
                                         }
                                     }
                         }
+                }
+                // deeper levels' patterns and the bias enter through the low-pass band
+#pragma unroll
+                for (int i = 0; i < RH; ++i) {
+                    float tv = bias;
+                    const int r1 = min(row0 + i, a.H1 - 1);
+                    for (int l = 2; l <= L; ++l)
+                        tv += smem[a.offq[l - 2] + (r1 >> (l - 2)) * a.sq[l - 2] + (col >> (l - 2))];
+                    z[0][i] += tv;
+                }
+                // level-1 synthesis: slot (ry, rx) = LL +- LH +- HL +- HH, onto the base conv
+#pragma unroll
+                for (int i = 0; i < RH; ++i) {
+                    const float a0v = z[0][i] + z[1][i], a1v = z[0][i] - z[1][i];
+                    const float b0 = z[2][i] + z[3][i], b1 = z[2][i] - z[3][i];
+                    P[0][0][i] += a0v + b0;
+                    P[0][1][i] += a0v - b0;
+                    P[1][0][i] += a1v + b1;
+                    P[1][1][i] += a1v - b1;
                 }
                 if (p < live) {
                     T *yp = yb + (p * CHW + 2 * j);
@@ -439,7 +495,7 @@ __device__ __forceinline__ void plane_fwd_body(const PlaneArgs &args) {
 }
 
 template <int K, typename T, int CW, int RH>
-__global__ __launch_bounds__(kPlaneThreads, 3) void plane_fwd_kernel(PlaneArgs a) {
+__global__ __launch_bounds__(kPlaneThreads, 2) void plane_fwd_kernel(PlaneArgs a) {
     plane_fwd_body<K, T, CW, RH>(a);
 }
 
