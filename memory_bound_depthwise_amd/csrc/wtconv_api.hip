@@ -14,6 +14,7 @@
 #include <cmath>
 #include <cstdio>
 #include <cstring>
+#include <memory>
 #include <mutex>
 #include <string>
 #include <type_traits>
@@ -23,6 +24,7 @@
 #include "wtconv_fused.hpp"
 #include "wtconv_fused_dw.hpp"
 #include "wtconv_plane.hpp"
+#include "wtconv_plane_dw.hpp"
 #include "wtconv_kernels.hpp"
 
 namespace wtc {
@@ -339,24 +341,39 @@ struct PlaneCfg {
     int CW = 1, RH = 8;
 };
 
-// Bank cost of the final pass's 16-byte cell reads with row stride sy (cells): a
-// group of 8 lanes covers the 32 banks once when its cells are distinct mod 8; the
-// cost is the largest number of lanes of a group that share a cell slot mod 8,
-// summed over the groups (1 per group = conflict-free).
-long long plane_bank_cost(const PlaneArgs &a, int RH, int sy) {
+// Bank cost of 16-byte cell reads by items (strip s, plane p, column j), item t =
+// (s PB + p) W1 + j on lane t, cell s RH sy + p Pw1 + j: gfx950 serves a 16-byte
+// read 16 lanes at a time from 64 banks, conflict-free when the 16 cells are
+// distinct mod 16.  Cost: per group of 16 lanes the largest number of lanes sharing
+// a cell slot mod 16 (1 = conflict-free), summed.
+long long cell_bank_cost(int items, int pb, int W1, int pitch, int RH, int sy) {
     long long cost = 0;
-    const int per_strip = a.PB * a.W1;
-    for (int g = 0; g * 8 < a.final_items; ++g) {
-        int cnt[8] = {0};
+    const int per_strip = pb * W1;
+    for (int g = 0; g * 16 < items; ++g) {
+        int cnt[16] = {0};
         int worst = 0;
-        for (int t = g * 8; t < std::min(a.final_items, g * 8 + 8); ++t) {
-            const int s = t / per_strip, r = t % per_strip, p = r / a.W1, j = r % a.W1;
-            const int cell = s * RH * sy + p * a.Pw1 + j;
-            worst = std::max(worst, ++cnt[cell & 7]);
+        for (int t = g * 16; t < std::min(items, g * 16 + 16); ++t) {
+            const int s = t / per_strip, r = t % per_strip, p = r / W1, j = r % W1;
+            const int cell = s * RH * sy + p * pitch + j;
+            worst = std::max(worst, ++cnt[cell & 15]);
         }
         cost += worst;
     }
     return cost;
+}
+
+// Smallest row stride in [lo, lo + 16) with the least bank cost.
+int best_stride(int items, int pb, int W1, int pitch, int RH, int lo) {
+    long long best = -1;
+    int sy = lo;
+    for (int cand = lo; cand < lo + 16; ++cand) {
+        const long long cost = cell_bank_cost(items, pb, W1, pitch, RH, cand);
+        if (best < 0 || cost < best) {
+            best = cost;
+            sy = cand;
+        }
+    }
+    return sy;
 }
 
 // Layout for pb planes per pass; false when it does not fit.  Grid arrays hold one
@@ -396,15 +413,7 @@ bool plane_layout(const wtconv_desc &d, const PlaneCfg &cfg, int pb, PlaneArgs &
     if (a.final_items >= 32768 || a.commit_items >= 32768) return false;
     if ((long long)pb * d.c * d.h * d.w >= (1LL << 31)) return false;  // 32-bit offsets from a plane base
     // level-1 arrays: the stride (cells) with the fewest bank conflicts in the final pass
-    const int sy_min = kPlaneCO + W1s + R;
-    long long best = -1;
-    for (int sy = sy_min; sy < sy_min + 8; ++sy) {
-        const long long cost = plane_bank_cost(a, RH, sy);
-        if (best < 0 || cost < best) {
-            best = cost;
-            a.sy1 = sy;
-        }
-    }
+    a.sy1 = best_stride(a.final_items, pb, a.W1, a.Pw1, RH, kPlaneCO + W1s + R);
     a.a1 = (a.S1 * RH + 2 * R) * a.sy1;
     long long cells = a.a1;
     int deep = 0;
@@ -475,6 +484,79 @@ bool plan_plane(const wtconv_desc &d, PlaneArgs &a, PlaneCfg &cfg) {
     if (units >= (1LL << 31)) return false;
     a.U = (int)units;
     return true;
+}
+
+// ---------------------------------------------------------------------------
+// Plane-resident base weight gradient (polyphase cells of x and dy)
+// ---------------------------------------------------------------------------
+
+constexpr int kDwbLdsBudget = 40960;  // four workgroups per compute unit
+constexpr int kPlaneDwTargetBlocks = 1024;  // four per compute unit on 256 compute units
+
+bool dwb_layout(const wtconv_desc &d, const PlaneCfg &cfg, int pb, PlaneDwbArgs &a) {
+    const int K = d.k, KK = K * K, R = (K - 1) / 2, RC = (R + 1) / 2, RH = cfg.RH, CW = cfg.CW;
+    a = PlaneDwbArgs{};
+    a.n = d.n;
+    a.C = d.c;
+    a.H = d.h;
+    a.W = d.w;
+    a.PB = pb;
+    a.H1 = (d.h + 1) / 2;
+    a.W1 = (d.w + 1) / 2;
+    a.S1 = cdiv(a.H1, RH);
+    a.Gw = cdiv(a.W1, CW);
+    a.Pw1 = pb == 1 ? a.W1 : cdiv(a.W1 + RC, CW) * CW;
+    const int W1s = pb == 1 ? a.W1 : pb * a.Pw1;
+    a.commit_items = pb * a.H1 * a.Gw;
+    a.final_items = a.S1 * pb * a.W1;
+    if (a.final_items >= 32768 || a.commit_items >= 32768) return false;
+    if ((long long)pb * d.c * d.h * d.w >= (1LL << 31)) return false;  // 32-bit offsets from a plane base
+    a.sx = best_stride(a.final_items, pb, a.W1, a.Pw1, RH, kPlaneCO + W1s + RC);
+    a.ax = (a.S1 * RH + 2 * RC) * a.sx;
+    a.sd = best_stride(a.final_items, pb, a.W1, a.Pw1, RH, W1s);
+    const long long floats = 4LL * (a.ax + (long long)a.S1 * RH * a.sd);
+    a.lds_floats = (int)std::max<long long>(floats, (long long)kPlaneThreads * (KK + 2));
+    a.lds_floats = (a.lds_floats + 3) & ~3;
+    if ((long long)a.lds_floats * 4 > kDwbLdsBudget) return false;
+    a.m_gw = magic31_of(a.Gw);
+    a.m_h1 = magic31_of(a.H1);
+    a.m_strip = magic31_of(pb * a.W1);
+    a.m_w1 = magic31_of(a.W1);
+    return true;
+}
+
+// Workgroups per channel for the plane-resident weight gradients: about
+// kPlaneDwTargetBlocks in all, at most one per image group.
+int dw_blocks_per_channel(const wtconv_desc &d, int NG) {
+    return std::max(1, std::min(NG, kPlaneDwTargetBlocks / std::max(1, d.c)));
+}
+
+bool plan_dwb(const wtconv_desc &d, PlaneDwbArgs &a, PlaneCfg &cfg) {
+    if (d.n <= 0 || d.c <= 0 || d.h <= 0 || d.w <= 0) return false;
+    if (d.h > kFusedMaxSide || d.w > kFusedMaxSide) return false;
+    const int H1 = (d.h + 1) / 2;
+    cfg.RH = H1 % 7 == 0 ? 7 : (H1 <= 4 ? 4 : 8);
+    cfg.CW = d.w % 8 == 0 ? 4 : (d.w % 4 == 0 ? 2 : 1);
+    double best = 1e30;
+    int best_pb = 0;
+    for (int pb = 1; pb <= std::min(d.n, 64); ++pb) {
+        PlaneDwbArgs t{};
+        if (!dwb_layout(d, cfg, pb, t)) {
+            if (pb == 1) return false;
+            break;
+        }
+        // wave-instructions per pass: an item is ~4 RH K^2 FMAs + 30 RH others
+        const double cost = (cdiv(t.final_items, kPlaneThreads) * 2.0 * (4.0 * cfg.RH * d.k * d.k + 30.0 * cfg.RH) +
+                             cdiv(t.commit_items, kPlaneThreads) * 60.0 + 200.0) / pb;
+        if (cost < best - 1e-9) {
+            best = cost;
+            best_pb = pb;
+        }
+    }
+    if (!dwb_layout(d, cfg, best_pb, a)) return false;
+    a.NG = cdiv(d.n, a.PB);
+    a.k = dw_blocks_per_channel(d, a.NG);
+    return (long long)d.c * a.k < (1LL << 31);
 }
 
 // ---------------------------------------------------------------------------
@@ -583,6 +665,9 @@ struct FwdPlan {
 struct DwPlan {
     bool fused;          // levels by the plane-resident kernel (no carriers)
     FusedDwArgs fa;
+    bool dwb;            // base by the plane-resident kernel
+    PlaneDwbArgs ba;
+    PlaneCfg bcfg;
     LevelDims ld;
     size_t xc_off[kMaxLevels], gc_off[kMaxLevels];
     size_t part_off;                 // byte offset of the partials
@@ -594,7 +679,7 @@ struct DwPlan {
 
 size_t elem_size(int dtype) { return dtype == WTCONV_BF16 ? 2 : 4; }
 
-FwdPlan plan_forward(const wtconv_desc &d) {
+FwdPlan build_forward_plan(const wtconv_desc &d) {
     FwdPlan p{};
     p.ld = level_dims(d);
     const size_t es = elem_size(d.dtype), planes = (size_t)d.n * d.c;
@@ -614,7 +699,7 @@ FwdPlan plan_forward(const wtconv_desc &d) {
     return p;
 }
 
-DwPlan plan_backward_weight(const wtconv_desc &d) {
+DwPlan build_backward_weight_plan(const wtconv_desc &d) {
     DwPlan p{};
     p.ld = level_dims(d);
     p.fused = plan_fused_dw(d, p.fa);
@@ -631,9 +716,13 @@ DwPlan plan_backward_weight(const wtconv_desc &d) {
     p.part_off = off;
     const int KK = d.k * d.k;
     p.base = pick_tiling(Kind::DwBase, d.k, d.n, d.c, d.h, d.w, max_vec_width(d.dtype));
+    p.dwb = plan_dwb(d, p.ba, p.bcfg);
     long long floats = 0;
     p.region[0] = 0;
-    p.G[0] = (d.n > 0 && d.h > 0 && d.w > 0) ? p.base.nblk * p.base.tiles : 0;
+    if (p.dwb)
+        p.G[0] = p.ba.k;
+    else
+        p.G[0] = (d.n > 0 && d.h > 0 && d.w > 0) ? p.base.nblk * p.base.tiles : 0;
     floats += (long long)d.c * p.G[0] * (KK + 1);
     for (int l = 1; l <= d.levels; ++l) {
         p.lvl[l - 1] = pick_tiling(Kind::DwLevel, d.k, d.n, d.c, p.ld.H[l], p.ld.W[l], 1);
@@ -653,6 +742,44 @@ DwPlan plan_backward_weight(const wtconv_desc &d) {
 // ---------------------------------------------------------------------------
 
 bool empty(const wtconv_desc &d) { return d.n == 0 || d.c == 0 || d.h == 0 || d.w == 0; }
+
+// Plans depend on the descriptor only; they are built once per descriptor and
+// kept (a call's host cost is then a lookup, not the layout searches).
+struct PlanSet {
+    wtconv_desc d;
+    FwdPlan fp;
+    DwPlan dp;
+    bool plane;  // forward by the plane-resident kernel
+    PlaneArgs pa;
+    PlaneCfg pcfg;
+};
+
+bool same_desc(const wtconv_desc &a, const wtconv_desc &b) {
+    return a.n == b.n && a.c == b.c && a.h == b.h && a.w == b.w && a.k == b.k && a.levels == b.levels &&
+           a.dtype == b.dtype && a.reserved == b.reserved;
+}
+
+std::shared_ptr<const PlanSet> plans_for(const wtconv_desc &d) {
+    static std::mutex mu;
+    static std::vector<std::shared_ptr<const PlanSet>> cache;  // most recent last
+    {
+        std::lock_guard<std::mutex> lock(mu);
+        for (size_t i = cache.size(); i-- > 0;)
+            if (same_desc(cache[i]->d, d)) return cache[i];
+    }
+    auto ps = std::make_shared<PlanSet>();
+    ps->d = d;
+    ps->fp = build_forward_plan(d);
+    ps->dp = build_backward_weight_plan(d);
+    ps->plane = plan_plane(d, ps->pa, ps->pcfg);
+    std::lock_guard<std::mutex> lock(mu);
+    if (cache.size() >= 64) cache.erase(cache.begin());
+    cache.push_back(ps);
+    return ps;
+}
+
+FwdPlan plan_forward(const wtconv_desc &d) { return plans_for(d)->fp; }
+DwPlan plan_backward_weight(const wtconv_desc &d) { return plans_for(d)->dp; }
 
 int check_desc(const wtconv_desc *d) {
     if (!d) return WTCONV_ERR_NULL;
@@ -743,12 +870,29 @@ const void *plane_kernel_for(const wtconv_desc &d, const PlaneCfg &cfg) {
 int plane_grid(const wtconv_desc &d, const PlaneArgs &a, const PlaneCfg &cfg) {
     int dev = 0, cus = 0, per_cu = 0;
     const size_t shm = (size_t)a.lds_floats * sizeof(float);
+    const void *kern = plane_kernel_for(d, cfg);
+    static std::mutex mu;
+    struct Entry {
+        int dev;
+        const void *kern;
+        size_t shm;
+        int slots;
+    };
+    static std::vector<Entry> seen;
+    if (hipGetDevice(&dev) == hipSuccess) {
+        std::lock_guard<std::mutex> lock(mu);
+        for (const Entry &e : seen)
+            if (e.dev == dev && e.kern == kern && e.shm == shm) return (int)std::min<long long>(a.U, e.slots);
+    }
     if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, plane_kernel_for(d, cfg), kPlaneThreads, shm) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, kPlaneThreads, shm) != hipSuccess ||
         cus <= 0 || per_cu <= 0) {
         (void)hipGetLastError();
         cus = 256;
         per_cu = std::max(1, std::min(4, (int)((160 * 1024) / std::max<size_t>(shm, 1))));
+    } else {
+        std::lock_guard<std::mutex> lock(mu);
+        seen.push_back(Entry{dev, kern, shm, cus * per_cu});
     }
     return (int)std::min<long long>(a.U, (long long)cus * per_cu);
 }
@@ -787,13 +931,37 @@ int run_plane_forward(const wtconv_desc &d, PlaneArgs a, const PlaneCfg &cfg, co
 }
 
 template <int K, typename T>
+int run_plane_dwb(const wtconv_desc &d, PlaneDwbArgs a, const PlaneCfg &cfg, const void *x, const void *dy,
+                  float *partial, hipStream_t st) {
+    a.x = x;
+    a.dy = dy;
+    a.partial = partial;
+    a.vec = d.w % (2 * cfg.CW) == 0 && aligned(x, 2 * cfg.CW * sizeof(T)) && aligned(dy, 2 * cfg.CW * sizeof(T)) ? 1 : 0;
+    const dim3 grid((unsigned)((long long)d.c * a.k));
+    const size_t shm = (size_t)a.lds_floats * sizeof(float);
+    const int bf = std::is_same<T, uint16_t>::value;
+#define WTC_DWB_LAUNCH(CW_, RH_) \
+    launch("plane_dwb", K, bf, 0, plane_dwb_kernel<K, T, CW_, RH_>, grid, dim3(kPlaneThreads), shm, st, a)
+    switch (cfg.CW * 16 + cfg.RH) {
+        case 4 * 16 + 7: return WTC_DWB_LAUNCH(4, 7);
+        case 4 * 16 + 4: return WTC_DWB_LAUNCH(4, 4);
+        case 4 * 16 + 8: return WTC_DWB_LAUNCH(4, 8);
+        case 2 * 16 + 7: return WTC_DWB_LAUNCH(2, 7);
+        case 2 * 16 + 4: return WTC_DWB_LAUNCH(2, 4);
+        case 2 * 16 + 8: return WTC_DWB_LAUNCH(2, 8);
+        case 1 * 16 + 7: return WTC_DWB_LAUNCH(1, 7);
+        case 1 * 16 + 4: return WTC_DWB_LAUNCH(1, 4);
+        default: return WTC_DWB_LAUNCH(1, 8);
+    }
+#undef WTC_DWB_LAUNCH
+}
+
+template <int K, typename T>
 int run_forward(const wtconv_desc &d, const void *x, const float *w0, const float *b0, const float *s0,
                 const float *wl, const float *sl, void *y, char *ws, hipStream_t st, int rotate) {
     {
-        PlaneArgs pa{};
-        PlaneCfg cfg{};
-        if (plan_plane(d, pa, cfg))
-            return run_plane_forward<K, T>(d, pa, cfg, x, w0, b0, s0, wl, sl, y, st, rotate);
+        const auto ps = plans_for(d);
+        if (ps->plane) return run_plane_forward<K, T>(d, ps->pa, ps->pcfg, x, w0, b0, s0, wl, sl, y, st, rotate);
     }
     {
         FusedArgs fa{};
@@ -904,6 +1072,10 @@ int run_backward_weight(const wtconv_desc &d, const void *x, const void *dy, con
                             dim3(kThreads), shm, st, a);
             if (rc) return rc;
         }
+        if (p.dwb) {
+            int rc = run_plane_dwb<K, T>(d, p.ba, p.bcfg, x, dy, partial + p.region[0], st);
+            if (rc) return rc;
+        }
         DwBaseArgs b{};
         b.x = x;
         b.dy = dy;
@@ -915,8 +1087,9 @@ int run_backward_weight(const wtconv_desc &d, const void *x, const void *dy, con
         b.t = p.base;
         b.t.VW = std::min(vec_width(d.w, d.dtype, x), vec_width(d.w, d.dtype, dy));
         const size_t shm = lds_bytes(Kind::DwBase, K, b.t);
-        int rc = launch("dw_base", K, bf, 0, dw_base_kernel<K, T>, dim3((unsigned)grid_of(b.t, d.c)), dim3(kThreads),
-                        shm, st, b);
+        int rc = p.dwb ? 0
+                       : launch("dw_base", K, bf, 0, dw_base_kernel<K, T>, dim3((unsigned)grid_of(b.t, d.c)),
+                                dim3(kThreads), shm, st, b);
         if (rc) return rc;
     }
     FinalizeArgs f{};
@@ -1074,10 +1247,10 @@ int wtconv_plan_launches(const wtconv_desc *desc, int op, wtconv_launch *out, in
     if (op != WTCONV_OP_BACKWARD_WEIGHT) {
         if (!empty(d)) {
             FusedArgs fa{};
-            PlaneArgs pa{};
-            PlaneCfg cfg{};
-            if (plan_plane(d, pa, cfg)) {
-                add("plane_fwd", 0, plane_grid(d, pa, cfg), kPlaneThreads, (size_t)pa.lds_floats * sizeof(float));
+            const auto ps = plans_for(d);
+            if (ps->plane) {
+                add("plane_fwd", 0, plane_grid(d, ps->pa, ps->pcfg), kPlaneThreads,
+                    (size_t)ps->pa.lds_floats * sizeof(float));
             } else if (plan_fused(d, vec_width(d.w, d.dtype, aligned_ptr), fa)) {
                 add("fused_fwd", 0, (long long)d.c * fa.nblk, kThreads, (size_t)fa.lds_floats * sizeof(float));
             } else {
@@ -1098,9 +1271,13 @@ int wtconv_plan_launches(const wtconv_desc *desc, int op, wtconv_launch *out, in
                 for (int l = 1; l <= d.levels; ++l)
                     add("dw_level", l, grid_of(p.lvl[l - 1], d.c), kThreads, lds_bytes(Kind::DwLevel, d.k, p.lvl[l - 1]));
             }
-            Tiling t = p.base;
-            t.VW = vec_width(d.w, d.dtype, aligned_ptr);
-            add("dw_base", 0, grid_of(t, d.c), kThreads, lds_bytes(Kind::DwBase, d.k, t));
+            if (p.dwb) {
+                add("plane_dwb", 0, (long long)d.c * p.ba.k, kPlaneThreads, (size_t)p.ba.lds_floats * sizeof(float));
+            } else {
+                Tiling t = p.base;
+                t.VW = vec_width(d.w, d.dtype, aligned_ptr);
+                add("dw_base", 0, grid_of(t, d.c), kThreads, lds_bytes(Kind::DwBase, d.k, t));
+            }
         }
         add("dw_finalize", 0, (long long)d.c * (d.levels + 1), 128, 0);
     }

@@ -24,7 +24,8 @@ B_l = P*H_l*W_l coefficient blocks of level l:
   dw_level l   : reads the x and dy carriers (2*P*H_{l-1}*W_{l-1}); writes both
                  next carriers for l < L.  FLOPs: 2*4*k^2 + 16 per block.
   Both paths:
-  dw_base      : reads x and dy (2N).  FLOPs: 2*k^2 + 1 per pixel.
+  dw_base,
+  plane_dwb    : read x and dy (2N).  FLOPs: 2*k^2 + 1 per pixel.
   dw_finalize  : parameter-sized, counted as 0.
 backward_input launches the same kernels as forward.  Which path a shape takes
 is the library's decision (wtconv_plan_launches); `launches` takes it as flags.
@@ -64,7 +65,7 @@ def kernel_cost(family, level, n, c, h, w, k, levels, elem_bytes):
         l = level
         elems = 2 * blocks[l - 1] + (2 * blocks[l] if l < levels else 0)
         return E * elems, blocks[l] * (8 * k * k + 16)
-    if family == "dw_base":
+    if family in ("dw_base", "plane_dwb"):
         return E * 2 * N, N * (2 * k * k + 1)
     if family == "dw_finalize":
         return 0, 0
