@@ -491,7 +491,6 @@ bool plan_plane(const wtconv_desc &d, PlaneArgs &a, PlaneCfg &cfg) {
 // ---------------------------------------------------------------------------
 
 constexpr int kDwbLdsBudget = 40960;  // four workgroups per compute unit
-constexpr int kPlaneDwTargetBlocks = 1024;  // four per compute unit on 256 compute units
 
 bool dwb_layout(const wtconv_desc &d, const PlaneCfg &cfg, int pb, PlaneDwbArgs &a) {
     const int K = d.k, KK = K * K, R = (K - 1) / 2, RC = (R + 1) / 2, RH = cfg.RH, CW = cfg.CW;
@@ -525,10 +524,13 @@ bool dwb_layout(const wtconv_desc &d, const PlaneCfg &cfg, int pb, PlaneDwbArgs 
     return true;
 }
 
-// Workgroups per channel for the plane-resident weight gradients: about
-// kPlaneDwTargetBlocks in all, at most one per image group.
-int dw_blocks_per_channel(const wtconv_desc &d, int NG) {
-    return std::max(1, std::min(NG, kPlaneDwTargetBlocks / std::max(1, d.c)));
+// Workgroups per channel for the plane-resident weight gradients: as many as fit
+// on the device at once (resident workgroups per compute unit from the LDS size,
+// at most four of two wavefronts each, x 256 compute units), at most one per image
+// group.
+int dw_blocks_per_channel(const wtconv_desc &d, int NG, int lds_floats) {
+    const int per_cu = std::max(1, std::min(4, (160 * 1024) / std::max(1, lds_floats * 4)));
+    return std::max(1, std::min(NG, 256 * per_cu / std::max(1, d.c)));
 }
 
 bool plan_dwb(const wtconv_desc &d, PlaneDwbArgs &a, PlaneCfg &cfg) {
@@ -555,7 +557,147 @@ bool plan_dwb(const wtconv_desc &d, PlaneDwbArgs &a, PlaneCfg &cfg) {
     }
     if (!dwb_layout(d, cfg, best_pb, a)) return false;
     a.NG = cdiv(d.n, a.PB);
-    a.k = dw_blocks_per_channel(d, a.NG);
+    a.k = dw_blocks_per_channel(d, a.NG, a.lds_floats);
+    return (long long)d.c * a.k < (1LL << 31);
+}
+
+// ---------------------------------------------------------------------------
+// Plane-resident level weight gradients (band-major pyramids of x and dy)
+// ---------------------------------------------------------------------------
+
+constexpr int kDwlLdsBudget = 53248;  // three workgroups per compute unit
+
+// Column stride (floats) >= lo for the column-major band arrays: a multiple of 4 with
+// an odd quotient, so that 16 consecutive columns' 16-byte reads hit distinct
+// groups of 4 banks (gfx950 serves 16 lanes of a 16-byte read per cycle).
+int column_stride(int lo) {
+    int s = (lo + 3) & ~3;
+    if ((s / 4) % 2 == 0) s += 4;
+    return s;
+}
+
+bool dwl_layout(const wtconv_desc &d, const PlaneCfg &cfg, int pb, PlaneDwlArgs &a) {
+    const int K = d.k, KK = K * K, R = (K - 1) / 2, L = d.levels, RHD = cfg.RH, CW = cfg.CW;
+    a = PlaneDwlArgs{};
+    a.n = d.n;
+    a.C = d.c;
+    a.H = d.h;
+    a.W = d.w;
+    a.L = L;
+    a.PB = pb;
+    a.H1 = (d.h + 1) / 2;
+    a.W1 = (d.w + 1) / 2;
+    a.Gw = cdiv(a.W1, CW);
+    int hs[kMaxLevels + 1], ws[kMaxLevels + 1];
+    hs[0] = d.h;
+    ws[0] = d.w;
+    for (int l = 1; l <= L; ++l) {
+        hs[l] = (hs[l - 1] + 1) / 2;
+        ws[l] = (ws[l - 1] + 1) / 2;
+    }
+    if (pb == 1) {
+        a.Pw1 = a.W1;
+    } else {
+        int pwL = 1;
+        for (int l = 1; l <= L; ++l) pwL = std::max(pwL, cdiv(ws[l] + R, 1LL << (L - l)));
+        while (((long long)pwL << (L - 1)) % CW) ++pwL;
+        a.Pw1 = pwL << (L - 1);
+    }
+    a.commit_items = pb * a.H1 * a.Gw;
+    if (a.commit_items >= 32768) return false;
+    if ((long long)pb * d.c * d.h * d.w >= (1LL << 31)) return false;
+    long long fl = 0;
+    const int WQ = (RHD + 2 * R + 3) / 4;
+    for (int l = 1; l <= L; ++l) {
+        const int li = l - 1;
+        a.hl[li] = hs[l];
+        a.wl[li] = pb == 1 ? ws[l] : (pb * a.Pw1) >> (l - 1);
+        a.ns[li] = cdiv(hs[l], RHD);
+        const int items = a.ns[li] * a.wl[li];
+        if (items >= 32768 || 2LL * hs[l] * a.wl[li] >= 32768) return false;
+        a.xs[li] = column_stride(std::max((a.ns[li] - 1) * RHD + 4 * WQ, a.ns[li] * RHD + 2 * R));
+        a.xb[li] = a.xs[li] * (a.wl[li] + 2 * R);
+        a.xo[li] = (int)fl;
+        fl += 4LL * a.xb[li];
+        a.gs[li] = column_stride(std::max(a.ns[li] * RHD, hs[l] + 1));
+        a.gb[li] = a.gs[li] * (a.wl[li] + 1);
+        a.go[li] = (int)fl;
+        fl += 4LL * a.gb[li];
+        a.m_wl[li] = magic31_of(a.wl[li]);
+        a.m_hl[li] = magic31_of(a.hl[li]);
+    }
+    fl = std::max<long long>(fl, (long long)kPlaneThreads * (KK + 1));
+    a.lds_floats = (int)((fl + 3) & ~3LL);
+    if ((long long)a.lds_floats * 4 > kDwlLdsBudget) return false;
+    // lanes per (level, band): greedy, to minimise the largest item count of a lane
+    int M[kMaxLevels];
+    for (int l = 0; l < L; ++l) M[l] = 1;
+    if (4 * L > kPlaneThreads) return false;
+    int used = 4 * L;
+    while (used + 4 <= kPlaneThreads) {
+        int worst = -1, wl_items = 0;
+        for (int l = 0; l < L; ++l) {
+            const int items = a.ns[l] * a.wl[l], per = cdiv(items, M[l]);
+            if (M[l] < std::min(items, 255) && per > wl_items) {
+                wl_items = per;
+                worst = l;
+            }
+        }
+        if (worst < 0) break;
+        ++M[worst];
+        used += 4;
+    }
+    int t = 0;
+    for (int l = 0; l < L; ++l) {
+        a.lane0[l] = t;
+        a.lanes[l] = M[l];
+        for (int b = 0; b < 4; ++b)
+            for (int m = 0; m < M[l]; ++m, ++t)
+                a.lane[t] = (uint32_t)(l + 1) | ((uint32_t)b << 4) | ((uint32_t)m << 8) | ((uint32_t)M[l] << 16);
+    }
+    for (; t < kPlaneThreads; ++t) a.lane[t] = 0;
+    a.groups = 4 * L;
+    a.m_gw = magic31_of(a.Gw);
+    a.m_h1 = magic31_of(a.H1);
+    return true;
+}
+
+// Largest item count of a lane (the pass time) for a layout.
+int dwl_lane_items(const PlaneDwlArgs &a) {
+    int worst = 0;
+    for (int t = 0; t < kPlaneThreads; ++t) {
+        const uint32_t in = a.lane[t];
+        const int M = (in >> 16) & 255, l = (int)(in & 15) - 1;
+        if (M) worst = std::max(worst, cdiv(a.ns[l] * a.wl[l], M));
+    }
+    return worst;
+}
+
+bool plan_dwl(const wtconv_desc &d, PlaneDwlArgs &a, PlaneCfg &cfg) {
+    if (d.levels < 1 || d.n <= 0 || d.c <= 0 || d.h <= 0 || d.w <= 0) return false;
+    if (d.h > kFusedMaxSide || d.w > kFusedMaxSide) return false;
+    cfg.RH = 4;  // item rows: one 16-byte read of dy per item
+    cfg.CW = d.w % 8 == 0 ? 4 : (d.w % 4 == 0 ? 2 : 1);
+    double best = 1e30;
+    int best_pb = 0;
+    for (int pb = 1; pb <= std::min(d.n, 64); ++pb) {
+        PlaneDwlArgs t{};
+        if (!dwl_layout(d, cfg, pb, t)) {
+            if (pb == 1) return false;
+            break;
+        }
+        // wave-instructions per pass: a lane's items of RHD K^2 FMAs + 30 others;
+        // commit and Haar ~60 per item; ~300 fixed
+        const double cost = (2.0 * dwl_lane_items(t) * (cfg.RH * d.k * d.k + 30.0) +
+                             cdiv(t.commit_items, kPlaneThreads) * 120.0 + 300.0) / pb;
+        if (cost < best - 1e-9) {
+            best = cost;
+            best_pb = pb;
+        }
+    }
+    if (!dwl_layout(d, cfg, best_pb, a)) return false;
+    a.NG = cdiv(d.n, a.PB);
+    a.k = dw_blocks_per_channel(d, a.NG, a.lds_floats);
     return (long long)d.c * a.k < (1LL << 31);
 }
 
@@ -668,6 +810,9 @@ struct DwPlan {
     bool dwb;            // base by the plane-resident kernel
     PlaneDwbArgs ba;
     PlaneCfg bcfg;
+    bool dwl;            // levels by the band-major plane-resident kernel
+    PlaneDwlArgs la;
+    PlaneCfg lcfg;
     LevelDims ld;
     size_t xc_off[kMaxLevels], gc_off[kMaxLevels];
     size_t part_off;                 // byte offset of the partials
@@ -702,10 +847,11 @@ FwdPlan build_forward_plan(const wtconv_desc &d) {
 DwPlan build_backward_weight_plan(const wtconv_desc &d) {
     DwPlan p{};
     p.ld = level_dims(d);
-    p.fused = plan_fused_dw(d, p.fa);
+    p.dwl = plan_dwl(d, p.la, p.lcfg);
+    p.fused = !p.dwl && plan_fused_dw(d, p.fa);
     const size_t es = elem_size(d.dtype), planes = (size_t)d.n * d.c;
     size_t off = 0;
-    if (!p.fused) {
+    if (!p.fused && !p.dwl) {
         for (int l = 1; l < d.levels; ++l) {
             p.xc_off[l - 1] = off;
             off = align_up(off + planes * p.ld.H[l] * p.ld.W[l] * es);
@@ -727,7 +873,9 @@ DwPlan build_backward_weight_plan(const wtconv_desc &d) {
     for (int l = 1; l <= d.levels; ++l) {
         p.lvl[l - 1] = pick_tiling(Kind::DwLevel, d.k, d.n, d.c, p.ld.H[l], p.ld.W[l], 1);
         p.region[l] = floats;
-        if (p.fused)
+        if (p.dwl)
+            p.G[l] = p.la.k;
+        else if (p.fused)
             p.G[l] = p.fa.nblk;
         else
             p.G[l] = (d.n > 0 && d.h > 0 && d.w > 0) ? p.lvl[l - 1].nblk * p.lvl[l - 1].tiles : 0;
@@ -957,6 +1105,29 @@ int run_plane_dwb(const wtconv_desc &d, PlaneDwbArgs a, const PlaneCfg &cfg, con
 }
 
 template <int K, typename T>
+int run_plane_dwl(const wtconv_desc &d, const DwPlan &p, const void *x, const void *dy, float *partial,
+                  hipStream_t st) {
+    PlaneDwlArgs a = p.la;
+    const PlaneCfg &cfg = p.lcfg;
+    a.x = x;
+    a.dy = dy;
+    a.partial = partial;
+    for (int l = 0; l < d.levels; ++l) a.off[l] = p.region[l + 1];
+    a.vec = d.w % (2 * cfg.CW) == 0 && aligned(x, 2 * cfg.CW * sizeof(T)) && aligned(dy, 2 * cfg.CW * sizeof(T)) ? 1 : 0;
+    const dim3 grid((unsigned)((long long)d.c * a.k));
+    const size_t shm = (size_t)a.lds_floats * sizeof(float);
+    const int bf = std::is_same<T, uint16_t>::value;
+#define WTC_DWL_LAUNCH(CW_, RH_) \
+    launch("plane_dwl", K, bf, 0, plane_dwl_kernel<K, T, CW_, RH_>, grid, dim3(kPlaneThreads), shm, st, a)
+    switch (cfg.CW) {
+        case 4: return WTC_DWL_LAUNCH(4, 4);
+        case 2: return WTC_DWL_LAUNCH(2, 4);
+        default: return WTC_DWL_LAUNCH(1, 4);
+    }
+#undef WTC_DWL_LAUNCH
+}
+
+template <int K, typename T>
 int run_forward(const wtconv_desc &d, const void *x, const float *w0, const float *b0, const float *s0,
                 const float *wl, const float *sl, void *y, char *ws, hipStream_t st, int rotate) {
     {
@@ -1026,6 +1197,10 @@ int run_backward_weight(const wtconv_desc &d, const void *x, const void *dy, con
     const int bf = std::is_same<T, uint16_t>::value;
     const int L = d.levels;
     float *partial = reinterpret_cast<float *>(ws + p.part_off);
+    if (!empty(d) && p.dwl && L > 0) {
+        int rc = run_plane_dwl<K, T>(d, p, x, dy, partial, st);
+        if (rc) return rc;
+    }
     if (!empty(d) && p.fused && L > 0) {
         FusedDwArgs a = p.fa;
         a.x = x;
@@ -1051,7 +1226,7 @@ int run_backward_weight(const wtconv_desc &d, const void *x, const void *dy, con
         if (rc) return rc;
     }
     if (!empty(d)) {
-        for (int l = 1; l <= L && !p.fused; ++l) {
+        for (int l = 1; l <= L && !p.fused && !p.dwl; ++l) {
             DwLevelArgs a{};
             a.xin = l == 1 ? x : (const void *)(ws + p.xc_off[l - 2]);
             a.gin = l == 1 ? dy : (const void *)(ws + p.gc_off[l - 2]);
@@ -1265,7 +1440,9 @@ int wtconv_plan_launches(const wtconv_desc *desc, int op, wtconv_launch *out, in
     } else if (d.c > 0) {
         const DwPlan p = plan_backward_weight(d);
         if (!empty(d)) {
-            if (p.fused && d.levels > 0) {
+            if (p.dwl && d.levels > 0) {
+                add("plane_dwl", 0, (long long)d.c * p.la.k, kPlaneThreads, (size_t)p.la.lds_floats * sizeof(float));
+            } else if (p.fused && d.levels > 0) {
                 add("fused_dw", 0, (long long)d.c * p.fa.nblk, kThreads, (size_t)p.fa.lds_floats * sizeof(float));
             } else {
                 for (int l = 1; l <= d.levels; ++l)

@@ -203,4 +203,241 @@ __global__ __launch_bounds__(kPlaneThreads, 2) void plane_dwb_kernel(PlaneDwbArg
     }
 }
 
+// ---------------------------------------------------------------------------
+// Plane-resident weight gradient of the levels.
+//
+// Level l, band b: the branch is z = s(l,b) (W(l,b) * Y_l,b) on the orthonormal
+// Haar coefficients Y_l of x (§3.1), and the synthesis back to pixels is the
+// adjoint of the analysis (Prop. 1), so dL/dz = G_l,b, the analysis of dy, and
+// dL/dW(l,b)[u][v] = s(l,b) sum_ij G_l,b[i][j] Y_l,b[i+u-R][j+v-R].  With the
+// unscaled pyramids of both (S_l = 2^l Y_l, the same for dy) the raw sum is 4^-l
+// sum G S; the finalize kernel applies s(l,b) and the Eq. 9 scale gradient.
+//
+// LDS holds the unscaled bands of x (zero halo of R cells) and of dy, every level,
+// band by band and column-major, so that a column of an item's window is
+// contiguous and is read 16 bytes at a time.  Each lane is tied to one (level,
+// band) for the whole kernel and owns its k^2 tap accumulators; an item is one
+// column x RHD rows of that level's grid, and the items of a (level, band) are
+// dealt round-robin to its lanes (the lane table comes from the host).  Per pass:
+//   1. commit x and dy patches as level-1 bands (butterflies in registers);
+//   2. Haar analysis of levels 2..L for x and dy;
+//   3. every lane runs its items.
+// At the end the lanes of each (level, band) are summed in a fixed order into the
+// workgroup's partial row of that level.
+// ---------------------------------------------------------------------------
+
+struct PlaneDwlArgs {
+    const void *x, *dy;
+    float *partial;                 // level l region at off[l-1]: [C][k][4 K^2]
+    long long off[kMaxLevels];
+    int n, C, H, W, L;
+    int vec;                        // x and dy rows are read with vector loads
+    int PB, Pw1, NG, k;             // as for the base kernel
+    int H1, W1, Gw, commit_items;
+    // level l = 1..L at index l-1 (its grid, side-by-side planes included).  Band b
+    // of x: element (row r, column j) at xo + b xb + (j + R) xs + (r + R); of dy:
+    // go + b gb + j gs + r.  Strides and offsets are multiples of 4 floats.
+    int hl[kMaxLevels], wl[kMaxLevels];    // rows, width
+    int ns[kMaxLevels];                    // strips of RHD rows
+    int xs[kMaxLevels], xb[kMaxLevels], xo[kMaxLevels];  // x: column stride, band size, offset (floats)
+    int gs[kMaxLevels], gb[kMaxLevels], go[kMaxLevels];  // dy: the same
+    uint32_t m_wl[kMaxLevels], m_hl[kMaxLevels];          // udiv16 reciprocals of wl, hl
+    uint32_t lane[kPlaneThreads];          // level (bits 0-3) | band (4-5) | index in group (8-15) | lanes in group (16-23)
+    int groups;                            // (level, band) groups in use: 4 L
+    int lane0[kMaxLevels], lanes[kMaxLevels];  // level l: first lane of band 0, lanes per band
+    int lds_floats;
+    uint32_t m_gw, m_h1;                   // udiv16 reciprocals of Gw, H1
+};
+
+template <int K, typename T, int CW, int RHD>
+__global__ __launch_bounds__(kPlaneThreads, 2) void plane_dwl_kernel(PlaneDwlArgs a) {
+    constexpr int R = (K - 1) / 2, KK = K * K;
+    constexpr int NT = kPlaneThreads;
+    constexpr int WQ = (RHD + 2 * R + 3) / 4;  // 16-byte reads per window column
+    static_assert(RHD % 4 == 0, "item rows are read 16 bytes at a time");
+    using IO = PatchIO<T, CW>;
+    constexpr int SLOTS = kPlaneMaxWords / (2 * IO::kWords) > 0 ? kPlaneMaxWords / (2 * IO::kWords) : 1;
+    extern __shared__ float smem[];
+    const int c = blockIdx.x / a.k, r = blockIdx.x - c * a.k;
+    const int g_begin = (int)((long long)r * a.NG / a.k), g_end = (int)((long long)(r + 1) * a.NG / a.k);
+    const int tid = threadIdx.x, PB = a.PB, L = a.L;
+    const int HW = a.H * a.W, CHW = a.C * HW;
+    const T *xc = static_cast<const T *>(a.x) + (size_t)c * HW;
+    const T *dc = static_cast<const T *>(a.dy) + (size_t)c * HW;
+
+    for (int i = tid * 4; i < a.lds_floats; i += NT * 4)
+        *reinterpret_cast<float4 *>(smem + i) = make_float4(0.f, 0.f, 0.f, 0.f);
+
+    // commit item g = (p Gw + m) H1 + i: consecutive lanes take consecutive rows of
+    // a column group, so that their column-major stores hit distinct banks
+    auto patch_of = [&](int g, int &p, int &i, int &m) {
+        const int q = udiv16(g, a.m_h1);
+        i = g - q * a.H1;
+        p = udiv16(q, a.m_gw);
+        m = q - p * a.Gw;
+    };
+    auto load_patch = [&](uint32_t (&rw)[2][IO::kWords], const T *base, int live, int g) {
+#pragma unroll
+        for (int w = 0; w < IO::kWords; ++w) rw[0][w] = rw[1][w] = 0;
+        int p, i, m;
+        patch_of(g, p, i, m);
+        if (p >= live) return;
+        const int col0 = 2 * CW * m;
+        const T *src = base + (p * CHW + (2 * i) * a.W + col0);
+        IO::load_row(rw[0], src, a.vec, col0, a.W);
+        if (2 * i + 1 < a.H) IO::load_row(rw[1], src + a.W, a.vec, col0, a.W);
+    };
+    // level-1 bands of a patch's CW cells: element (row, col + q) of each band
+    // (column stride cs, band size bs)
+    auto store_bands = [&](float *base, int cs, int bs, const uint32_t (&rw)[2][IO::kWords], int row, int col) {
+#pragma unroll
+        for (int q = 0; q < CW; ++q) {
+            const float x00 = IO::elem(rw[0], 2 * q), x01 = IO::elem(rw[0], 2 * q + 1);
+            const float x10 = IO::elem(rw[1], 2 * q), x11 = IO::elem(rw[1], 2 * q + 1);
+            const float s0 = x00 + x01, s1 = x10 + x11, d0 = x00 - x01, d1 = x10 - x11;
+            float *d = base + (col + q) * cs + row;
+            d[0] = s0 + s1;
+            d[bs] = s0 - s1;
+            d[2 * bs] = d0 + d1;
+            d[3 * bs] = d0 - d1;
+        }
+    };
+
+    uint32_t xr[SLOTS][2][IO::kWords], dr[SLOTS][2][IO::kWords];
+    auto prefetch = [&](int g) {
+        const int n0 = g * PB, live = min(PB, a.n - n0);
+#pragma unroll
+        for (int k = 0; k < SLOTS; ++k) {
+            const int e = tid + k * NT;
+            if (e >= a.commit_items) continue;
+            load_patch(xr[k], xc + (size_t)n0 * CHW, live, e);
+            load_patch(dr[k], dc + (size_t)n0 * CHW, live, e);
+        }
+    };
+
+    const uint32_t info = a.lane[tid];
+    const int lv = info & 15, band = (info >> 4) & 3, gm = (info >> 8) & 255, gM = (info >> 16) & 255;
+    // the lane's item geometry, fixed for the kernel (the level differs between
+    // lanes of a wavefront, so it is looked up once, not per item)
+    const int li0 = gM > 0 ? lv - 1 : 0;
+    const int it_w = a.wl[li0], it_end = gM > 0 ? a.ns[li0] * it_w : 0;
+    const uint32_t it_mw = a.m_wl[li0];
+    const int it_xs = a.xs[li0], it_gs = a.gs[li0];
+    const int it_x = a.xo[li0] + band * a.xb[li0], it_g = a.go[li0] + band * a.gb[li0];
+    float acc[KK];
+#pragma unroll
+    for (int t = 0; t < KK; ++t) acc[t] = 0.f;
+    if (g_begin < g_end) prefetch(g_begin);
+
+    for (int g = g_begin; g < g_end; ++g) {
+        const int n0 = g * PB, live = min(PB, a.n - n0);
+        __syncthreads();  // the previous pass is done with the bands
+        {
+            const int xs = opaque(a.xs[0]), xb = opaque(a.xb[0]), gs = opaque(a.gs[0]), gb = opaque(a.gb[0]);
+            const int pw1 = opaque(a.Pw1);
+            float *xbase = smem + a.xo[0] + R * xs + R;
+            float *gbase = smem + a.go[0];
+#pragma unroll
+            for (int k = 0; k < SLOTS; ++k) {
+                const int e = tid + k * NT;
+                if (e >= a.commit_items) continue;
+                int p, i, m;
+                patch_of(e, p, i, m);
+                store_bands(xbase, xs, xb, xr[k], i, p * pw1 + m * CW);
+                store_bands(gbase, gs, gb, dr[k], i, p * pw1 + m * CW);
+            }
+            for (int e = tid + SLOTS * NT; e < a.commit_items; e += NT) {  // beyond the registers
+                uint32_t rw[2][IO::kWords];
+                int p, i, m;
+                patch_of(e, p, i, m);
+                load_patch(rw, xc + (size_t)n0 * CHW, live, e);
+                store_bands(xbase, xs, xb, rw, i, p * pw1 + m * CW);
+                load_patch(rw, dc + (size_t)n0 * CHW, live, e);
+                store_bands(gbase, gs, gb, rw, i, p * pw1 + m * CW);
+            }
+        }
+        __syncthreads();
+        if (g + 1 < g_end) prefetch(g + 1);
+
+        // Haar analysis of levels 2..L (unscaled butterflies of the low-pass bands);
+        // consecutive lanes take consecutive rows of a column
+        for (int l = 1; l < L; ++l) {
+            const int Hn = a.hl[l], Wn = a.wl[l];
+            const int xs0 = a.xs[l - 1], gs0 = a.gs[l - 1], xs1 = a.xs[l], gs1 = a.gs[l];
+            const int xb1 = a.xb[l], gb1 = a.gb[l];
+            const float *xsrc = smem + a.xo[l - 1] + R * xs0 + R;  // LL band of the level above
+            const float *gsrc = smem + a.go[l - 1];
+            float *xdst = smem + a.xo[l] + R * xs1 + R;
+            float *gdst = smem + a.go[l];
+            for (int q = tid; q < 2 * Hn * Wn; q += NT) {
+                const bool isg = q >= Hn * Wn;
+                const int qq = isg ? q - Hn * Wn : q;
+                const int j = udiv16(qq, a.m_hl[l]), i = qq - j * Hn;
+                const int ss = isg ? gs0 : xs0, ds = isg ? gs1 : xs1, db = isg ? gb1 : xb1;
+                const float *sp = (isg ? gsrc : xsrc) + (2 * j) * ss + 2 * i;
+                const float x00 = sp[0], x10 = sp[1], x01 = sp[ss], x11 = sp[ss + 1];
+                const float s0 = x00 + x01, s1 = x10 + x11, d0 = x00 - x01, d1 = x10 - x11;
+                float *dp = (isg ? gdst : xdst) + j * ds + i;
+                dp[0] = s0 + s1;
+                dp[db] = s0 - s1;
+                dp[2 * db] = d0 + d1;
+                dp[3 * db] = d0 - d1;
+            }
+            __syncthreads();
+        }
+
+        // this lane's items: column j x RHD rows of (level lv, band)
+        if (gM > 0) {
+            for (int it = gm; it < it_end; it += gM) {
+                const int s = udiv16(it, it_mw), j = it - s * it_w;
+                // dy rows s RHD .. + RHD of column j; x window rows s RHD - R ..,
+                // columns j - R .. j + R (storage column j + v, row s RHD + t)
+                const float4 *gcol = reinterpret_cast<const float4 *>(smem + it_g + j * it_gs + s * RHD);
+                const float *xwin = smem + it_x + j * it_xs + s * RHD;
+                const int xs = it_xs;
+                float gv[RHD];
+#pragma unroll
+                for (int q = 0; q < RHD / 4; ++q) {
+                    const float4 g4 = gcol[q];
+                    gv[4 * q] = g4.x;
+                    gv[4 * q + 1] = g4.y;
+                    gv[4 * q + 2] = g4.z;
+                    gv[4 * q + 3] = g4.w;
+                }
+#pragma unroll
+                for (int v = 0; v < K; ++v) {
+                    const float4 *cp = reinterpret_cast<const float4 *>(xwin + v * xs);
+                    float col[4 * WQ];
+#pragma unroll
+                    for (int q = 0; q < WQ; ++q) {
+                        const float4 c4 = cp[q];
+                        col[4 * q] = c4.x;
+                        col[4 * q + 1] = c4.y;
+                        col[4 * q + 2] = c4.z;
+                        col[4 * q + 3] = c4.w;
+                    }
+#pragma unroll
+                    for (int u = 0; u < K; ++u)
+#pragma unroll
+                        for (int i = 0; i < RHD; ++i) acc[u * K + v] = fmaf(gv[i], col[i + u], acc[u * K + v]);
+                }
+            }
+        }
+    }
+
+    // fixed-order reduction: lanes of a group are consecutive in the lane table
+    __syncthreads();
+#pragma unroll
+    for (int t = 0; t < KK; ++t) smem[tid * (KK + 1) + t] = acc[t];
+    __syncthreads();
+    for (int q = tid; q < a.groups * KK; q += NT) {
+        const int grp = q / KK, tap = q - grp * KK;
+        const int l = grp >> 2, b = grp & 3;  // 0-based level
+        const int t0 = a.lane0[l] + b * a.lanes[l];
+        float sum = 0.f;
+        for (int t = t0; t < t0 + a.lanes[l]; ++t) sum += smem[t * (KK + 1) + tap];
+        a.partial[a.off[l] + ((size_t)c * a.k + r) * 4 * KK + b * KK + tap] = ldexpf(sum, -2 * (l + 1));
+    }
+}
+
 }  // namespace wtc

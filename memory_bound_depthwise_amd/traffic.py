@@ -13,7 +13,8 @@ B_l = P*H_l*W_l coefficient blocks of level l:
   fused_fwd,
   plane_fwd    : read x (N), write y (N).  FLOPs: the per-level kernels' total,
                  sum_l B_l*(8k^2 + 20) + N*(2k^2 + L).
-  fused_dw     : reads x and dy (2N).  FLOPs: sum_l B_l*(8k^2 + 16).
+  fused_dw,
+  plane_dwl    : read x and dy (2N).  FLOPs: sum_l B_l*(8k^2 + 16).
   Per-level kernels:
   level_fwd l  : reads the carrier P*H_{l-1}*W_{l-1}; writes Q(l) 4*B_l and,
                  for l < L, the carrier B_l.
@@ -52,7 +53,7 @@ def kernel_cost(family, level, n, c, h, w, k, levels, elem_bytes):
     if family in ("fused_fwd", "plane_fwd"):
         fl = sum(blocks[l] * (8 * k * k + 20) for l in range(1, levels + 1)) + N * (2 * k * k + levels)
         return E * 2 * N, fl
-    if family == "fused_dw":
+    if family in ("fused_dw", "plane_dwl"):
         return E * 2 * N, sum(blocks[l] * (8 * k * k + 16) for l in range(1, levels + 1))
     if family == "level_fwd":
         l = level
