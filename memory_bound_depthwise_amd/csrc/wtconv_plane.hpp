@@ -271,7 +271,11 @@ __device__ __forceinline__ void plane_fwd_body(const PlaneArgs &args) {
             if (e < (4 * A.L + 1) * KK) weight_factors(A, c, e, wf0[k], wf1[k]);
         }
     };
-    if ((int)blockIdx.x < a0.U) prefetch(args, blockIdx.x);
+    if ((int)blockIdx.x < a0.U) {
+        prefetch(args, blockIdx.x);
+#pragma unroll
+        for (int k = 0; k < WSLOTS; ++k) wf0[k] *= wf1[k];
+    }
 
     for (int u = blockIdx.x; u < a0.U; u += gridDim.x) {
         // Every argument below is read through a pointer made opaque per pass, so
@@ -292,7 +296,7 @@ __device__ __forceinline__ void plane_fwd_body(const PlaneArgs &args) {
 #pragma unroll
             for (int k = 0; k < WSLOTS; ++k) {
                 const int e = tid + k * NT;
-                if (e < nw) smem[weight_slot(a, e)] = wf0[k] * wf1[k];
+                if (e < nw) smem[weight_slot(a, e)] = wf0[k];  // the product, formed after the prefetch
             }
             for (int e = tid + WSLOTS * NT; e < nw; e += NT) {  // beyond the registers
                 float f0, f1;
@@ -338,6 +342,13 @@ __device__ __forceinline__ void plane_fwd_body(const PlaneArgs &args) {
             __syncthreads();
         }
 
+        // the next unit's weight factors have arrived by now: keep their products
+        // only, which frees registers for the final phase
+        if (u + (int)gridDim.x < a.U) {
+#pragma unroll
+            for (int k = 0; k < WSLOTS; ++k) wf0[k] *= wf1[k];
+        }
+
         // 3. deep levels: filtered bands -> sign patterns Q_l; items of all levels
         //    are spread over all lanes
         if (L >= 2) {
@@ -380,44 +391,60 @@ __device__ __forceinline__ void plane_fwd_body(const PlaneArgs &args) {
                 const int col = p * a.Pw1 + j, row0 = s * RH;
                 float z[4][RH], P[2][2][RH];
 #pragma unroll
-                for (int i = 0; i < RH; ++i) {
+                for (int i = 0; i < RH; ++i)
 #pragma unroll
                     for (int b = 0; b < 4; ++b) z[b][i] = 0.f;
-#pragma unroll
-                    for (int b = 0; b < 4; ++b) P[b >> 1][b & 1][i] = 0.f;
-                }
                 // window cell (t, v) is level-1 cell (row0 - R + t, col - R + v)
                 const float4 *win = s4 + row0 * sy1 + col + kPlaneCO - R;
                 const float4 *wt1 = s4 + (wt >> 2);
-                const float *w0 = smem + wt + 4 * L * KK;
 #pragma unroll 1
                 for (int v = 0; v < K; ++v) {  // rolled: see conv_bands
+                    float4 wb[K];
+#pragma unroll
+                    for (int u = 0; u < K; ++u) wb[u] = wt1[v * K + u];
                     float4 cl[RH + K - 1];
-                    {
-                        float4 wb[K];
 #pragma unroll
-                        for (int u = 0; u < K; ++u) wb[u] = wt1[v * K + u];
+                    for (int tt = 0; tt < RH + K - 1; ++tt) cl[tt] = win[tt * sy1 + v];
 #pragma unroll
-                        for (int tt = 0; tt < RH + K - 1; ++tt) cl[tt] = win[tt * sy1 + v];
+                    for (int u = 0; u < K; ++u)
 #pragma unroll
-                        for (int u = 0; u < K; ++u)
+                        for (int i = 0; i < RH; ++i) {
+                            z[0][i] = fmaf(wb[u].x, cl[i + u].x, z[0][i]);
+                            z[1][i] = fmaf(wb[u].y, cl[i + u].y, z[1][i]);
+                            z[2][i] = fmaf(wb[u].z, cl[i + u].z, z[2][i]);
+                            z[3][i] = fmaf(wb[u].w, cl[i + u].w, z[3][i]);
+                        }
+                }
+                // deeper levels' patterns and the bias enter through the low-pass band
 #pragma unroll
-                            for (int i = 0; i < RH; ++i) {
-                                z[0][i] = fmaf(wb[u].x, cl[i + u].x, z[0][i]);
-                                z[1][i] = fmaf(wb[u].y, cl[i + u].y, z[1][i]);
-                                z[2][i] = fmaf(wb[u].z, cl[i + u].z, z[2][i]);
-                                z[3][i] = fmaf(wb[u].w, cl[i + u].w, z[3][i]);
-                            }
-                    }
-                    // base conv on the columns it reaches: output (2i+ry, 2j+rx), tap
-                    // (u, w) reads pixel (2i+ry+u-R, 2j+rx+w-R), i.e. component
-                    // (py, px) of cell (i + di, j + dj)
-                    const int dj = v - R;
-                    if (dj < -RC || dj > RC) continue;
+                for (int i = 0; i < RH; ++i) {
+                    float tv = bias;
+                    const int r1 = min(row0 + i, a.H1 - 1);
+                    for (int l = 2; l <= L; ++l)
+                        tv += smem[a.offq[l - 2] + (r1 >> (l - 2)) * a.sq[l - 2] + (col >> (l - 2))];
+                    z[0][i] += tv;
+                }
+                // level-1 synthesis: slot (ry, rx) = LL +- LH +- HL +- HH
+#pragma unroll
+                for (int i = 0; i < RH; ++i) {
+                    const float a0v = z[0][i] + z[1][i], a1v = z[0][i] - z[1][i];
+                    const float b0 = z[2][i] + z[3][i], b1 = z[2][i] - z[3][i];
+                    P[0][0][i] = a0v + b0;
+                    P[0][1][i] = a0v - b0;
+                    P[1][0][i] = a1v + b1;
+                    P[1][1][i] = a1v - b1;
+                }
+                // base conv onto the patterns: output (2i+ry, 2j+rx), tap (u, w) reads
+                // pixel (2i+ry+u-R, 2j+rx+w-R), i.e. component (py, px) of cell
+                // (i + di, j + dj); x is rebuilt from the cell's bands
+                const float4 *xwin = s4 + (row0 + R - RC) * sy1 + col + kPlaneCO;
+                const float *w0 = smem + wt + 4 * L * KK;
+#pragma unroll 1
+                for (int dj = -RC; dj <= RC; ++dj) {  // rolled: see conv_bands
                     float4 xq[RH + 2 * RC];  // 4 x (x00, x01, x10, x11) by the inverse butterfly
 #pragma unroll
                     for (int tt = 0; tt < RH + 2 * RC; ++tt) {
-                        const float4 c4 = cl[tt + R - RC];
+                        const float4 c4 = xwin[tt * sy1 + dj];
                         const float A = c4.x + c4.y, B = c4.x - c4.y, C = c4.z + c4.w, D = c4.z - c4.w;
                         xq[tt] = make_float4(A + C, A - C, B + D, B - D);
                     }
@@ -448,25 +475,6 @@ __device__ __forceinline__ void plane_fwd_body(const PlaneArgs &args) {
                                     }
                         }
                 }
-                // deeper levels' patterns and the bias enter through the low-pass band
-#pragma unroll
-                for (int i = 0; i < RH; ++i) {
-                    float tv = bias;
-                    const int r1 = min(row0 + i, a.H1 - 1);
-                    for (int l = 2; l <= L; ++l)
-                        tv += smem[a.offq[l - 2] + (r1 >> (l - 2)) * a.sq[l - 2] + (col >> (l - 2))];
-                    z[0][i] += tv;
-                }
-                // level-1 synthesis: slot (ry, rx) = LL +- LH +- HL +- HH, onto the base conv
-#pragma unroll
-                for (int i = 0; i < RH; ++i) {
-                    const float a0v = z[0][i] + z[1][i], a1v = z[0][i] - z[1][i];
-                    const float b0 = z[2][i] + z[3][i], b1 = z[2][i] - z[3][i];
-                    P[0][0][i] += a0v + b0;
-                    P[0][1][i] += a0v - b0;
-                    P[1][0][i] += a1v + b1;
-                    P[1][1][i] += a1v - b1;
-                }
                 if (p < live) {
                     T *yp = yb + (p * CHW + 2 * j);
 #pragma unroll
@@ -495,7 +503,7 @@ __device__ __forceinline__ void plane_fwd_body(const PlaneArgs &args) {
 }
 
 template <int K, typename T, int CW, int RH>
-__global__ __launch_bounds__(kPlaneThreads, 2) void plane_fwd_kernel(PlaneArgs a) {
+__global__ __launch_bounds__(kPlaneThreads, 3) void plane_fwd_kernel(PlaneArgs a) {
     plane_fwd_body<K, T, CW, RH>(a);
 }
 
