@@ -619,22 +619,26 @@ bool dwl_layout(const wtconv_desc &d, const PlaneCfg &cfg, int pb, PlaneDwlArgs 
         a.xb[li] = a.xs[li] * (a.wl[li] + 2 * R);
         a.xo[li] = (int)fl;
         fl += 4LL * a.xb[li];
-        a.gs[li] = column_stride(std::max(a.ns[li] * RHD, hs[l] + 1));
-        a.gb[li] = a.gs[li] * (a.wl[li] + 1);
+        // dy columns: ns RHD >= hl rows (a multiple of 4, so the pad row an odd hl
+        // needs for the next level's butterflies is inside), one pad column if wl
+        // is odd
+        a.gs[li] = column_stride(a.ns[li] * RHD);
+        a.gb[li] = a.gs[li] * (a.wl[li] + (a.wl[li] & 1));
         a.go[li] = (int)fl;
         fl += 4LL * a.gb[li];
         a.m_wl[li] = magic31_of(a.wl[li]);
         a.m_hl[li] = magic31_of(a.hl[li]);
     }
-    fl = std::max<long long>(fl, (long long)kPlaneThreads * (KK + 1));
+    const int TC = KK <= 24 ? KK : (KK + 1) / 2;  // reduction chunk of the kernel
+    fl = std::max<long long>(fl, (long long)kDwlThreads * (TC + 1));
     a.lds_floats = (int)((fl + 3) & ~3LL);
     if ((long long)a.lds_floats * 4 > kDwlLdsBudget) return false;
     // lanes per (level, band): greedy, to minimise the largest item count of a lane
     int M[kMaxLevels];
     for (int l = 0; l < L; ++l) M[l] = 1;
-    if (4 * L > kPlaneThreads) return false;
+    if (4 * L > kDwlThreads) return false;
     int used = 4 * L;
-    while (used + 4 <= kPlaneThreads) {
+    while (used + 4 <= kDwlThreads) {
         int worst = -1, wl_items = 0;
         for (int l = 0; l < L; ++l) {
             const int items = a.ns[l] * a.wl[l], per = cdiv(items, M[l]);
@@ -655,7 +659,7 @@ bool dwl_layout(const wtconv_desc &d, const PlaneCfg &cfg, int pb, PlaneDwlArgs 
             for (int m = 0; m < M[l]; ++m, ++t)
                 a.lane[t] = (uint32_t)(l + 1) | ((uint32_t)b << 4) | ((uint32_t)m << 8) | ((uint32_t)M[l] << 16);
     }
-    for (; t < kPlaneThreads; ++t) a.lane[t] = 0;
+    for (; t < kDwlThreads; ++t) a.lane[t] = 0;
     a.groups = 4 * L;
     a.m_gw = magic31_of(a.Gw);
     a.m_h1 = magic31_of(a.H1);
@@ -665,7 +669,7 @@ bool dwl_layout(const wtconv_desc &d, const PlaneCfg &cfg, int pb, PlaneDwlArgs 
 // Largest item count of a lane (the pass time) for a layout.
 int dwl_lane_items(const PlaneDwlArgs &a) {
     int worst = 0;
-    for (int t = 0; t < kPlaneThreads; ++t) {
+    for (int t = 0; t < kDwlThreads; ++t) {
         const uint32_t in = a.lane[t];
         const int M = (in >> 16) & 255, l = (int)(in & 15) - 1;
         if (M) worst = std::max(worst, cdiv(a.ns[l] * a.wl[l], M));
@@ -689,7 +693,7 @@ bool plan_dwl(const wtconv_desc &d, PlaneDwlArgs &a, PlaneCfg &cfg) {
         // wave-instructions per pass: a lane's items of RHD K^2 FMAs + 30 others;
         // commit and Haar ~60 per item; ~300 fixed
         const double cost = (2.0 * dwl_lane_items(t) * (cfg.RH * d.k * d.k + 30.0) +
-                             cdiv(t.commit_items, kPlaneThreads) * 120.0 + 300.0) / pb;
+                             cdiv(t.commit_items, kDwlThreads) * 120.0 + 300.0) / pb;
         if (cost < best - 1e-9) {
             best = cost;
             best_pb = pb;
@@ -1118,7 +1122,7 @@ int run_plane_dwl(const wtconv_desc &d, const DwPlan &p, const void *x, const vo
     const size_t shm = (size_t)a.lds_floats * sizeof(float);
     const int bf = std::is_same<T, uint16_t>::value;
 #define WTC_DWL_LAUNCH(CW_, RH_) \
-    launch("plane_dwl", K, bf, 0, plane_dwl_kernel<K, T, CW_, RH_>, grid, dim3(kPlaneThreads), shm, st, a)
+    launch("plane_dwl", K, bf, 0, plane_dwl_kernel<K, T, CW_, RH_>, grid, dim3(kDwlThreads), shm, st, a)
     switch (cfg.CW) {
         case 4: return WTC_DWL_LAUNCH(4, 4);
         case 2: return WTC_DWL_LAUNCH(2, 4);
@@ -1441,7 +1445,7 @@ int wtconv_plan_launches(const wtconv_desc *desc, int op, wtconv_launch *out, in
         const DwPlan p = plan_backward_weight(d);
         if (!empty(d)) {
             if (p.dwl && d.levels > 0) {
-                add("plane_dwl", 0, (long long)d.c * p.la.k, kPlaneThreads, (size_t)p.la.lds_floats * sizeof(float));
+                add("plane_dwl", 0, (long long)d.c * p.la.k, kDwlThreads, (size_t)p.la.lds_floats * sizeof(float));
             } else if (p.fused && d.levels > 0) {
                 add("fused_dw", 0, (long long)d.c * p.fa.nblk, kThreads, (size_t)p.fa.lds_floats * sizeof(float));
             } else {

@@ -226,6 +226,10 @@ __global__ __launch_bounds__(kPlaneThreads, 2) void plane_dwb_kernel(PlaneDwbArg
 // workgroup's partial row of that level.
 // ---------------------------------------------------------------------------
 
+// Workgroup size of the level kernel: its LDS allows three workgroups per compute
+// unit, so four wavefronts each keep twelve wavefronts per compute unit.
+constexpr int kDwlThreads = 256;
+
 struct PlaneDwlArgs {
     const void *x, *dy;
     float *partial;                 // level l region at off[l-1]: [C][k][4 K^2]
@@ -242,7 +246,7 @@ struct PlaneDwlArgs {
     int xs[kMaxLevels], xb[kMaxLevels], xo[kMaxLevels];  // x: column stride, band size, offset (floats)
     int gs[kMaxLevels], gb[kMaxLevels], go[kMaxLevels];  // dy: the same
     uint32_t m_wl[kMaxLevels], m_hl[kMaxLevels];          // udiv16 reciprocals of wl, hl
-    uint32_t lane[kPlaneThreads];          // level (bits 0-3) | band (4-5) | index in group (8-15) | lanes in group (16-23)
+    uint32_t lane[kDwlThreads];            // level (bits 0-3) | band (4-5) | index in group (8-15) | lanes in group (16-23)
     int groups;                            // (level, band) groups in use: 4 L
     int lane0[kMaxLevels], lanes[kMaxLevels];  // level l: first lane of band 0, lanes per band
     int lds_floats;
@@ -250,9 +254,9 @@ struct PlaneDwlArgs {
 };
 
 template <int K, typename T, int CW, int RHD>
-__global__ __launch_bounds__(kPlaneThreads, 2) void plane_dwl_kernel(PlaneDwlArgs a) {
+__global__ __launch_bounds__(kDwlThreads, 3) void plane_dwl_kernel(PlaneDwlArgs a) {
     constexpr int R = (K - 1) / 2, KK = K * K;
-    constexpr int NT = kPlaneThreads;
+    constexpr int NT = kDwlThreads;
     constexpr int WQ = (RHD + 2 * R + 3) / 4;  // 16-byte reads per window column
     static_assert(RHD % 4 == 0, "item rows are read 16 bytes at a time");
     using IO = PatchIO<T, CW>;
@@ -425,18 +429,25 @@ __global__ __launch_bounds__(kPlaneThreads, 2) void plane_dwl_kernel(PlaneDwlArg
         }
     }
 
-    // fixed-order reduction: lanes of a group are consecutive in the lane table
-    __syncthreads();
+    // fixed-order reduction: lanes of a group are consecutive in the lane table; the
+    // taps go through LDS TC at a time (TC + 1 floats per lane fit the allocation)
+    constexpr int TC = KK <= 24 ? KK : (KK + 1) / 2;
 #pragma unroll
-    for (int t = 0; t < KK; ++t) smem[tid * (KK + 1) + t] = acc[t];
-    __syncthreads();
-    for (int q = tid; q < a.groups * KK; q += NT) {
-        const int grp = q / KK, tap = q - grp * KK;
-        const int l = grp >> 2, b = grp & 3;  // 0-based level
-        const int t0 = a.lane0[l] + b * a.lanes[l];
-        float sum = 0.f;
-        for (int t = t0; t < t0 + a.lanes[l]; ++t) sum += smem[t * (KK + 1) + tap];
-        a.partial[a.off[l] + ((size_t)c * a.k + r) * 4 * KK + b * KK + tap] = ldexpf(sum, -2 * (l + 1));
+    for (int t0 = 0; t0 < KK; t0 += TC) {
+        __syncthreads();
+#pragma unroll
+        for (int t = 0; t < TC; ++t)
+            if (t0 + t < KK) smem[tid * (TC + 1) + t] = acc[t0 + t];
+        __syncthreads();
+        const int nt = min(TC, KK - t0);
+        for (int q = tid; q < a.groups * nt; q += NT) {
+            const int grp = q / nt, tap = q - grp * nt;
+            const int l = grp >> 2, b = grp & 3;  // 0-based level
+            const int l0 = a.lane0[l] + b * a.lanes[l];
+            float sum = 0.f;
+            for (int t = l0; t < l0 + a.lanes[l]; ++t) sum += smem[t * (TC + 1) + tap];
+            a.partial[a.off[l] + ((size_t)c * a.k + r) * 4 * KK + b * KK + t0 + tap] = ldexpf(sum, -2 * (l + 1));
+        }
     }
 }
 
