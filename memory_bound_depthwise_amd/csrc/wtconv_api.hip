@@ -437,7 +437,10 @@ bool plane_layout(const wtconv_desc &d, const PlaneCfg &cfg, int pb, PlaneArgs &
         fl += ((2LL * hs[l] * a.sq[li]) + 3) & ~3LL;
     }
     a.wt = (int)fl;
-    fl += ((4LL * L + 1) * KK + 3) & ~3LL;
+    fl += ((4LL * L + 1) * KK + 1 + 3) & ~3LL;  // weights, then the folded bias
+    a.zero_floats = (int)fl;
+    a.tab = (int)fl;  // deep-level geometry table, filled once per workgroup
+    fl += (kPlaneTabFields * std::max(L - 1, 0) + 3) & ~3;
     a.lds_floats = (int)fl;
     if (fl * 4 > kPlaneLdsBudget) return false;
     a.m_gw = magic31_of(a.Gw);
@@ -468,10 +471,10 @@ bool plan_plane(const wtconv_desc &d, PlaneArgs &a, PlaneCfg &cfg) {
         // wave-instructions per pass: a final item is ~(4 + 4) RH K^2 FMAs plus
         // ~60 RH others, a deep item 4 kPlaneRHd K^2; commit and Haar ~30 per item;
         // ~400 fixed
-        const double fin = cdiv(t.final_items, kPlaneThreads) * 2.0 * (8.0 * cfg.RH * K * K + 60.0 * cfg.RH);
+        const double fin = cdiv(t.final_items, kFwdThreads) * 2.0 * (8.0 * cfg.RH * K * K + 60.0 * cfg.RH);
         const int deep_items = d.levels >= 2 ? t.dend[d.levels - 2] : 0;
-        const double deep = cdiv(deep_items, kPlaneThreads) * 2.0 * (4.0 * kPlaneRHd * K * K + 60.0);
-        const double misc = cdiv(t.commit_items, kPlaneThreads) * 40.0 + 400.0;
+        const double deep = cdiv(deep_items, kFwdThreads) * 2.0 * (4.0 * kPlaneRHd * K * K + 60.0);
+        const double misc = cdiv(t.commit_items, kFwdThreads) * 40.0 + 400.0;
         const double cost = (fin + deep + misc) / pb;
         if (cost < best - 1e-9) {
             best = cost;
@@ -514,7 +517,7 @@ bool dwb_layout(const wtconv_desc &d, const PlaneCfg &cfg, int pb, PlaneDwbArgs 
     a.ax = (a.S1 * RH + 2 * RC) * a.sx;
     a.sd = best_stride(a.final_items, pb, a.W1, a.Pw1, RH, W1s);
     const long long floats = 4LL * (a.ax + (long long)a.S1 * RH * a.sd);
-    a.lds_floats = (int)std::max<long long>(floats, (long long)kPlaneThreads * (KK + 2));
+    a.lds_floats = (int)std::max<long long>(floats, (long long)kDwbThreads * (KK + 2));
     a.lds_floats = (a.lds_floats + 3) & ~3;
     if ((long long)a.lds_floats * 4 > kDwbLdsBudget) return false;
     a.m_gw = magic31_of(a.Gw);
@@ -548,8 +551,8 @@ bool plan_dwb(const wtconv_desc &d, PlaneDwbArgs &a, PlaneCfg &cfg) {
             break;
         }
         // wave-instructions per pass: an item is ~4 RH K^2 FMAs + 30 RH others
-        const double cost = (cdiv(t.final_items, kPlaneThreads) * 2.0 * (4.0 * cfg.RH * d.k * d.k + 30.0 * cfg.RH) +
-                             cdiv(t.commit_items, kPlaneThreads) * 60.0 + 200.0) / pb;
+        const double cost = (cdiv(t.final_items, kDwbThreads) * 2.0 * (4.0 * cfg.RH * d.k * d.k + 30.0 * cfg.RH) +
+                             cdiv(t.commit_items, kDwbThreads) * 60.0 + 200.0) / pb;
         if (cost < best - 1e-9) {
             best = cost;
             best_pb = pb;
@@ -1037,7 +1040,7 @@ int plane_grid(const wtconv_desc &d, const PlaneArgs &a, const PlaneCfg &cfg) {
             if (e.dev == dev && e.kern == kern && e.shm == shm) return (int)std::min<long long>(a.U, e.slots);
     }
     if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, kPlaneThreads, shm) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, kFwdThreads, shm) != hipSuccess ||
         cus <= 0 || per_cu <= 0) {
         (void)hipGetLastError();
         cus = 256;
@@ -1067,7 +1070,7 @@ int run_plane_forward(const wtconv_desc &d, PlaneArgs a, const PlaneCfg &cfg, co
     const size_t shm = (size_t)a.lds_floats * sizeof(float);
     const int bf = std::is_same<T, uint16_t>::value;
 #define WTC_PLANE_LAUNCH(CW_, RH_) \
-    launch("plane_fwd", K, bf, 0, plane_fwd_kernel<K, T, CW_, RH_>, grid, dim3(kPlaneThreads), shm, st, a)
+    launch("plane_fwd", K, bf, 0, plane_fwd_kernel<K, T, CW_, RH_>, grid, dim3(kFwdThreads), shm, st, a)
     switch (cfg.CW * 16 + cfg.RH) {
         case 4 * 16 + 7: return WTC_PLANE_LAUNCH(4, 7);
         case 4 * 16 + 4: return WTC_PLANE_LAUNCH(4, 4);
@@ -1093,7 +1096,7 @@ int run_plane_dwb(const wtconv_desc &d, PlaneDwbArgs a, const PlaneCfg &cfg, con
     const size_t shm = (size_t)a.lds_floats * sizeof(float);
     const int bf = std::is_same<T, uint16_t>::value;
 #define WTC_DWB_LAUNCH(CW_, RH_) \
-    launch("plane_dwb", K, bf, 0, plane_dwb_kernel<K, T, CW_, RH_>, grid, dim3(kPlaneThreads), shm, st, a)
+    launch("plane_dwb", K, bf, 0, plane_dwb_kernel<K, T, CW_, RH_>, grid, dim3(kDwbThreads), shm, st, a)
     switch (cfg.CW * 16 + cfg.RH) {
         case 4 * 16 + 7: return WTC_DWB_LAUNCH(4, 7);
         case 4 * 16 + 4: return WTC_DWB_LAUNCH(4, 4);
@@ -1428,7 +1431,7 @@ int wtconv_plan_launches(const wtconv_desc *desc, int op, wtconv_launch *out, in
             FusedArgs fa{};
             const auto ps = plans_for(d);
             if (ps->plane) {
-                add("plane_fwd", 0, plane_grid(d, ps->pa, ps->pcfg), kPlaneThreads,
+                add("plane_fwd", 0, plane_grid(d, ps->pa, ps->pcfg), kFwdThreads,
                     (size_t)ps->pa.lds_floats * sizeof(float));
             } else if (plan_fused(d, vec_width(d.w, d.dtype, aligned_ptr), fa)) {
                 add("fused_fwd", 0, (long long)d.c * fa.nblk, kThreads, (size_t)fa.lds_floats * sizeof(float));
@@ -1453,7 +1456,7 @@ int wtconv_plan_launches(const wtconv_desc *desc, int op, wtconv_launch *out, in
                     add("dw_level", l, grid_of(p.lvl[l - 1], d.c), kThreads, lds_bytes(Kind::DwLevel, d.k, p.lvl[l - 1]));
             }
             if (p.dwb) {
-                add("plane_dwb", 0, (long long)d.c * p.ba.k, kPlaneThreads, (size_t)p.ba.lds_floats * sizeof(float));
+                add("plane_dwb", 0, (long long)d.c * p.ba.k, kDwbThreads, (size_t)p.ba.lds_floats * sizeof(float));
             } else {
                 Tiling t = p.base;
                 t.VW = vec_width(d.w, d.dtype, aligned_ptr);

@@ -46,10 +46,12 @@
 
 namespace wtc {
 
-constexpr int kPlaneThreads = 128;
+constexpr int kFwdThreads = 128;  // threads of a forward workgroup
 constexpr int kPlaneCO = 4;         // first data cell of every grid row (left halo)
 constexpr int kPlaneRHd = 2;        // level rows of a deep-level item
 constexpr int kPlaneMaxWords = 16;  // prefetch registers per thread
+constexpr int kPlaneTabFields = 8;  // per deep level: dend, width, 1/width, band stride, band offset,
+                                    // pattern stride, pattern offset, rows
 
 // Exact n / d for 0 <= n < 2^16 and 1 <= d < 2^15 with m = ceil(2^31 / d): one
 // multiply-high and no special case for d = 1 (checked exhaustively on the host).
@@ -78,6 +80,8 @@ struct PlaneArgs {
     int sq[kMaxLevels], offq[kMaxLevels];  // sign patterns: row stride (floats), offset (floats)
     int dend[kMaxLevels];                  // cumulative deep items (strips x width) by level
     int wt;                                // weight table (floats)
+    int zero_floats;                       // floats cleared at the start (bands, patterns, weights)
+    int tab;                               // deep-level geometry table (kPlaneTabFields ints per level)
     int lds_floats;
     uint32_t m_gw, m_h1, m_strip, m_w1;    // udiv16 reciprocals of Gw, H1, PB*W1, W1
     uint32_t m_wls[kMaxLevels];            // ... of the deep widths
@@ -157,10 +161,14 @@ __device__ __forceinline__ int opaque(int v) {
     asm volatile("" : "+s"(v));
     return v;
 }
-// The same for a value that may differ between lanes.
-__device__ __forceinline__ int opaque_lane(int v) {
-    asm volatile("" : "+v"(v));
-    return v;
+// A wave-uniform pointer to global memory held in scalar registers (in the global
+// address space, so that loads through it are global, not flat, loads).
+typedef const __attribute__((address_space(1))) float gfloat;
+__device__ __forceinline__ gfloat *opaque_ptr(const float *p) {
+    uint64_t v = reinterpret_cast<uint64_t>(p);
+    uint32_t lo = __builtin_amdgcn_readfirstlane((uint32_t)v), hi = __builtin_amdgcn_readfirstlane((uint32_t)(v >> 32));
+    asm volatile("" : "+s"(lo), "+s"(hi));
+    return reinterpret_cast<gfloat *>(((uint64_t)hi << 32) | lo);
 }
 
 // z[b][i] += sum_{u,v} wt[v][u].b * win[(i + u) * stride + v].b for the four bands b.
@@ -192,7 +200,7 @@ template <int K, typename T, int CW, int RH>
 __device__ __forceinline__ void plane_fwd_body(const PlaneArgs &args) {
     constexpr int R = (K - 1) / 2, KK = K * K;
     constexpr int RC = (R + 1) / 2;  // cells a pixel tap reaches beyond its own cell
-    constexpr int NT = kPlaneThreads;
+    constexpr int NT = kFwdThreads;
     using IO = PatchIO<T, CW>;
     constexpr int SLOTS = kPlaneMaxWords / (2 * IO::kWords) > 0 ? kPlaneMaxWords / (2 * IO::kWords) : 1;
     extern __shared__ float smem[];
@@ -200,10 +208,25 @@ __device__ __forceinline__ void plane_fwd_body(const PlaneArgs &args) {
     const PlaneArgs &a0 = args;
     const int tid = threadIdx.x;
     const int HW = a0.H * a0.W, CHW = a0.C * HW, PB = a0.PB;
-    constexpr int WSLOTS = 4;  // weight-table entries per thread carried in registers
+    constexpr int WSLOTS = 3;  // weight-table entries per thread carried in registers
 
-    for (int i = tid * 4; i < a0.lds_floats; i += NT * 4)
+    for (int i = tid * 4; i < a0.zero_floats; i += NT * 4)
         *reinterpret_cast<float4 *>(smem + i) = make_float4(0.f, 0.f, 0.f, 0.f);
+    // Geometry of the deep levels, for the deep phase, whose lanes take items of
+    // different levels: read from LDS there, it costs no vector-memory wait (which
+    // would also wait for the prefetch in flight).  Visible after the first barrier.
+    int *tab = reinterpret_cast<int *>(smem + a0.tab);
+    if (tid < a0.L - 1) {
+        int *t = tab + tid * kPlaneTabFields;
+        t[0] = a0.dend[tid];
+        t[1] = a0.wls[tid];
+        t[2] = (int)a0.m_wls[tid];
+        t[3] = a0.syd[tid];
+        t[4] = a0.offd[tid];
+        t[5] = a0.sq[tid];
+        t[6] = a0.offq[tid];
+        t[7] = a0.hl[tid];
+    }
 
     // A unit is PB images of one channel: unit u = (channel u / NG, images
     // [(u % NG) PB, ...)).  Workgroup w takes units w, w + G, w + 2G, ...
@@ -218,39 +241,54 @@ __device__ __forceinline__ void plane_fwd_body(const PlaneArgs &args) {
         p = udiv16(q, A.m_h1);
         i = q - p * A.H1;
     };
+    // The loads are unconditional, from clamped addresses (the commit zeroes what
+    // lies outside the images): a register that a load may or may not fill would
+    // make the compiler wait for every load in flight before touching it.
     auto load_patch = [&](const auto &A, uint32_t (&r)[2][IO::kWords], const T *xb, int live, int g) {
-#pragma unroll
-        for (int w = 0; w < IO::kWords; ++w) r[0][w] = r[1][w] = 0;
         int p, i, m;
-        patch_of(A, g, p, i, m);
-        if (p >= live) return;
+        patch_of(A, min(g, A.commit_items - 1), p, i, m);
+        p = min(p, live - 1);
         const int col0 = 2 * CW * m;
         const T *src = xb + (p * CHW + (2 * i) * A.W + col0);
         IO::load_row(r[0], src, A.vec, col0, A.W);
-        if (2 * i + 1 < A.H) IO::load_row(r[1], src + A.W, A.vec, col0, A.W);
+        IO::load_row(r[1], src + (2 * i + 1 < A.H ? A.W : 0), A.vec, col0, A.W);
     };
-    // Weight-table entry e of channel c: the two factors of its folded value.
-    // Level l, band b: s(l,b) 4^-l W(l,b) (Eq. 8 scale, the 2^-l of the unscaled
-    // pyramid and the 2^-l synthesis weight), as [l][v][u] float4 over b; base:
-    // s0 W0 / 4 as [v][u] (the base conv runs on 4x, rebuilt from S1).  Kernels are
-    // turned by 180 degrees for the input gradient.
+    // Zero the rows of a loaded patch that lie outside the images.
+    auto mask_patch = [&](uint32_t (&r)[2][IO::kWords], int live, int p, int i, int H) {
+#pragma unroll
+        for (int w = 0; w < IO::kWords; ++w) {
+            if (p >= live) r[0][w] = 0;
+            if (p >= live || 2 * i + 1 >= H) r[1][w] = 0;
+        }
+    };
+    // Weight-table entry e of channel c: the two raw factors of its folded value
+    // (loaded here, folded by fold_weight).  Level l, band b: s(l,b) 4^-l W(l,b)
+    // (Eq. 8 scale, the 2^-l of the unscaled pyramid and the 2^-l synthesis
+    // weight), as [l][v][u] float4 over b; base: s0 W0 / 4 as [v][u] (the base conv
+    // runs on 4x, rebuilt from S1).  Kernels are turned by 180 degrees for the input
+    // gradient.  The parameter pointers are taken as wave-uniform values, so each
+    // lane loads through its own address and nothing waits for the loads here.
+    // Entry (4L + 1) K^2, after the weights, is the folded bias s0 b.
     auto weight_factors = [&](const auto &A, int c, int e, float &f0, float &f1) {
+        const gfloat *sl = opaque_ptr(A.sl), *wl = opaque_ptr(A.wl);
+        const gfloat *s0 = opaque_ptr(A.s0), *w0 = opaque_ptr(A.w0), *b0 = opaque_ptr(A.b0);
+        const int nl = 4 * A.L;
         const int lb = e / KK, tap = e - lb * KK;  // tap = v K + u (column-major)
         const int v = tap / K, u = tap - v * K;
         const int src = A.rotate ? (K - 1 - u) * K + (K - 1 - v) : u * K + v;
-        if (lb < 4 * A.L) {
-            const int l = lb >> 2, b = lb & 3;
-            const size_t pc = ((size_t)l * A.C + c) * 4 + b;
-            f0 = ldexpf(A.sl[pc], -2 * (l + 1));
-            f1 = A.wl[pc * KK + src];
-        } else {
-            f0 = 0.25f * A.s0[c];
-            f1 = A.w0[(size_t)c * KK + src];
-        }
+        const size_t pc = lb < nl ? (size_t)((lb >> 2) * A.C + c) * 4 + (lb & 3) : 0;
+        const gfloat *p0 = lb < nl ? sl + pc : s0 + c;
+        const gfloat *p1 = lb < nl ? wl + pc * KK + src : (lb == nl ? w0 + (size_t)c * KK + src : (b0 ? b0 : s0) + c);
+        f0 = *p0;
+        f1 = *p1;
+    };
+    auto fold_weight = [&](const auto &A, int e, float f0, float f1) {
+        const int lb = e / KK, nl = 4 * A.L;
+        return lb < nl ? ldexpf(f0, -2 * ((lb >> 2) + 1)) * f1 : (lb == nl ? 0.25f * f0 * f1 : (A.b0 ? f0 * f1 : 0.f));
     };
     auto weight_slot = [&](const auto &A, int e) {  // LDS float index of entry e
         const int lb = e / KK, tap = e - lb * KK;
-        return lb < 4 * A.L ? A.wt + ((lb >> 2) * KK + tap) * 4 + (lb & 3) : A.wt + 4 * A.L * KK + tap;
+        return lb < 4 * A.L ? A.wt + ((lb >> 2) * KK + tap) * 4 + (lb & 3) : A.wt + 4 * A.L * KK + (lb - 4 * A.L) * KK + tap;
     };
 
     uint32_t raw[SLOTS][2][IO::kWords];
@@ -261,21 +299,11 @@ __device__ __forceinline__ void plane_fwd_body(const PlaneArgs &args) {
         const int live = min(A.PB, A.n - n0);
         const T *xb = static_cast<const T *>(A.x) + ((size_t)n0 * A.C + c) * HW;
 #pragma unroll
-        for (int k = 0; k < SLOTS; ++k) {
-            const int g = tid + k * NT;
-            if (g < A.commit_items) load_patch(A, raw[k], xb, live, g);
-        }
+        for (int k = 0; k < SLOTS; ++k) load_patch(A, raw[k], xb, live, tid + k * NT);
 #pragma unroll
-        for (int k = 0; k < WSLOTS; ++k) {
-            const int e = tid + k * NT;
-            if (e < (4 * A.L + 1) * KK) weight_factors(A, c, e, wf0[k], wf1[k]);
-        }
+        for (int k = 0; k < WSLOTS; ++k) weight_factors(A, c, min(tid + k * NT, (4 * A.L + 1) * KK), wf0[k], wf1[k]);
     };
-    if ((int)blockIdx.x < a0.U) {
-        prefetch(args, blockIdx.x);
-#pragma unroll
-        for (int k = 0; k < WSLOTS; ++k) wf0[k] *= wf1[k];
-    }
+    if ((int)blockIdx.x < a0.U) prefetch(args, blockIdx.x);
 
     for (int u = blockIdx.x; u < a0.U; u += gridDim.x) {
         // Every argument below is read through a pointer made opaque per pass, so
@@ -292,16 +320,16 @@ __device__ __forceinline__ void plane_fwd_body(const PlaneArgs &args) {
         __syncthreads();  // the previous pass is done with every array
         // 1. commit: this unit's weight table and level-1 bands
         {
-            const int nw = (4 * L + 1) * KK;
+            const int nw = (4 * L + 1) * KK + 1;  // weights and the bias
 #pragma unroll
             for (int k = 0; k < WSLOTS; ++k) {
                 const int e = tid + k * NT;
-                if (e < nw) smem[weight_slot(a, e)] = wf0[k];  // the product, formed after the prefetch
+                if (e < nw) smem[weight_slot(a, e)] = fold_weight(a, e, wf0[k], wf1[k]);
             }
             for (int e = tid + WSLOTS * NT; e < nw; e += NT) {  // beyond the registers
                 float f0, f1;
                 weight_factors(a, c, e, f0, f1);
-                smem[weight_slot(a, e)] = f0 * f1;
+                smem[weight_slot(a, e)] = fold_weight(a, e, f0, f1);
             }
             const int sy1 = opaque(a.sy1), pw1 = opaque(a.Pw1);
 #pragma unroll
@@ -310,6 +338,7 @@ __device__ __forceinline__ void plane_fwd_body(const PlaneArgs &args) {
                 if (g >= a.commit_items) continue;
                 int p, i, m;
                 patch_of(a, g, p, i, m);
+                mask_patch(raw[k], live, p, i, H);
                 commit_patch<K, T, CW>(s4, sy1, pw1, raw[k], p, i, m);
             }
             const T *xb = static_cast<const T *>(a.x) + ((size_t)n0 * a.C + c) * HW;
@@ -318,12 +347,11 @@ __device__ __forceinline__ void plane_fwd_body(const PlaneArgs &args) {
                 load_patch(a, r, xb, live, g);
                 int p, i, m;
                 patch_of(a, g, p, i, m);
+                mask_patch(r, live, p, i, H);
                 commit_patch<K, T, CW>(s4, sy1, pw1, r, p, i, m);
             }
         }
         __syncthreads();
-        if (u + (int)gridDim.x < a.U) prefetch(a, u + gridDim.x);
-        T *yb = static_cast<T *>(a.y) + ((size_t)n0 * a.C + c) * HW;
 
         // 2. Haar analysis of levels 2..L (unscaled butterflies of the low-pass band)
         for (int l = 2; l <= L; ++l) {
@@ -342,35 +370,29 @@ __device__ __forceinline__ void plane_fwd_body(const PlaneArgs &args) {
             __syncthreads();
         }
 
-        // the next unit's weight factors have arrived by now: keep their products
-        // only, which frees registers for the final phase
-        if (u + (int)gridDim.x < a.U) {
-#pragma unroll
-            for (int k = 0; k < WSLOTS; ++k) wf0[k] *= wf1[k];
-        }
-
         // 3. deep levels: filtered bands -> sign patterns Q_l; items of all levels
         //    are spread over all lanes
         if (L >= 2) {
             for (int it = tid; it < a.dend[L - 2]; it += NT) {
                 int li = 0;
-                while (it >= a.dend[li]) ++li;
-                const int loc = it - (li ? a.dend[li - 1] : 0), Wls = a.wls[li];
-                const int s = udiv16(loc, a.m_wls[li]), j = loc - s * Wls;
-                const int syd = opaque_lane(a.syd[li]);  // items of several levels share a wavefront
+                while (it >= tab[li * kPlaneTabFields]) ++li;
+                const int *tl = tab + li * kPlaneTabFields;
+                const int loc = it - (li ? tl[-kPlaneTabFields] : 0), Wls = tl[1];
+                const int s = udiv16(loc, (uint32_t)tl[2]), j = loc - s * Wls;
+                const int syd = tl[3];
                 float z[4][kPlaneRHd];
 #pragma unroll
                 for (int b = 0; b < 4; ++b)
 #pragma unroll
                     for (int i = 0; i < kPlaneRHd; ++i) z[b][i] = 0.f;
-                conv_bands<K, kPlaneRHd>(s4 + a.offd[li] + (s * kPlaneRHd) * syd + j + kPlaneCO - R, syd,
+                conv_bands<K, kPlaneRHd>(s4 + tl[4] + (s * kPlaneRHd) * syd + j + kPlaneCO - R, syd,
                                          s4 + (opaque(a.wt) >> 2) + (li + 1) * KK, z);
-                const int sq = a.sq[li];
-                float *q = smem + a.offq[li] + 2 * j;
+                const int sq = tl[5], hl = tl[7];
+                float *q = smem + tl[6] + 2 * j;
 #pragma unroll
                 for (int i = 0; i < kPlaneRHd; ++i) {
                     const int row = s * kPlaneRHd + i;
-                    if (row >= a.hl[li]) break;
+                    if (row >= hl) break;
                     const float a0v = z[0][i] + z[1][i], a1v = z[0][i] - z[1][i];
                     const float b0 = z[2][i] + z[3][i], b1 = z[2][i] - z[3][i];
                     *reinterpret_cast<float2 *>(q + (2 * row) * sq) = make_float2(a0v + b0, a0v - b0);
@@ -380,9 +402,15 @@ __device__ __forceinline__ void plane_fwd_body(const PlaneArgs &args) {
             __syncthreads();
         }
 
+        // The next unit's loads are issued only now, while no phase of this pass
+        // waits for vector memory any more: a wait for anything loaded after them
+        // (or for a register that one of them fills) would wait for all of them.
+        if (u + (int)gridDim.x < a.U) prefetch(a, u + gridDim.x);
+        T *yb = static_cast<T *>(a.y) + ((size_t)n0 * a.C + c) * HW;
+
         // 4. level 1 + base conv + deeper patterns, one store per pixel pair
         {
-            const float bias = a.b0 ? a.s0[c] * a.b0[c] : 0.f;
+            const float bias = smem[a.wt + (4 * L + 1) * KK];
             for (int t = tid; t < a.final_items; t += NT) {
                 // opaque per item: the weight-table reads stay next to their use
                 const int sy1 = opaque(a.sy1), wt = opaque(a.wt);
@@ -503,7 +531,7 @@ __device__ __forceinline__ void plane_fwd_body(const PlaneArgs &args) {
 }
 
 template <int K, typename T, int CW, int RH>
-__global__ __launch_bounds__(kPlaneThreads, 3) void plane_fwd_kernel(PlaneArgs a) {
+__global__ __launch_bounds__(kFwdThreads, 3) void plane_fwd_kernel(PlaneArgs a) {
     plane_fwd_body<K, T, CW, RH>(a);
 }
 

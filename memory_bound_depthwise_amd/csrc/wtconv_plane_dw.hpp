@@ -31,6 +31,8 @@
 
 namespace wtc {
 
+constexpr int kDwbThreads = 128;  // threads of a base weight-gradient workgroup
+
 struct PlaneDwbArgs {
     const void *x, *dy;
     float *partial;        // [C][k][K*K + 1]
@@ -54,10 +56,10 @@ __device__ __forceinline__ float cell_comp(const float4 &q, int comp) {
 }
 
 template <int K, typename T, int CW, int RH>
-__global__ __launch_bounds__(kPlaneThreads, 2) void plane_dwb_kernel(PlaneDwbArgs a) {
+__global__ __launch_bounds__(kDwbThreads, 2) void plane_dwb_kernel(PlaneDwbArgs a) {
     constexpr int R = (K - 1) / 2, KK = K * K;
     constexpr int RC = (R + 1) / 2;
-    constexpr int NT = kPlaneThreads;
+    constexpr int NT = kDwbThreads;
     using IO = PatchIO<T, CW>;
     constexpr int SLOTS = kPlaneMaxWords / (2 * IO::kWords) > 0 ? kPlaneMaxWords / (2 * IO::kWords) : 1;
     extern __shared__ float smem[];
