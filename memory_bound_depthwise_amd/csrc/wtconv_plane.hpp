@@ -136,6 +136,31 @@ struct PatchIO {
     }
 };
 
+// Loads of a prefetched patch (rows 2i, 2i + 1 of plane p, elements [2CW m, 2CW m +
+// 2CW)) from addresses clamped into the images, with no register cleared first;
+// mask_patch zeroes what lies outside once the data is used.  A register that is
+// cleared and then maybe loaded makes the compiler wait for every load in flight
+// before it clears that register again, which would serialize the prefetch.
+template <typename T, int CW>
+using PatchRegs = uint32_t[2][PatchIO<T, CW>::kWords];
+template <typename T, int CW>
+__device__ __forceinline__ void load_patch_clamped(PatchRegs<T, CW> &r, const T *base, int p, int i, int m, int live,
+                                                   int CHW, int H, int W, bool vec) {
+    p = min(p, live - 1);
+    const int col0 = 2 * CW * m;
+    const T *src = base + (p * CHW + (2 * i) * W + col0);
+    PatchIO<T, CW>::load_row(r[0], src, vec, col0, W);
+    PatchIO<T, CW>::load_row(r[1], src + (2 * i + 1 < H ? W : 0), vec, col0, W);
+}
+template <typename T, int CW>
+__device__ __forceinline__ void mask_patch(PatchRegs<T, CW> &r, int p, int i, int live, int H) {
+#pragma unroll
+    for (int w = 0; w < PatchIO<T, CW>::kWords; ++w) {
+        if (p >= live) r[0][w] = 0;
+        if (p >= live || 2 * i + 1 >= H) r[1][w] = 0;
+    }
+}
+
 // One commit item: patch rows 2i, 2i+1 of plane p, level-1 cells [CW m, CW m + CW):
 // the level-1 butterflies of each cell.
 template <int K, typename T, int CW>
@@ -241,25 +266,12 @@ __device__ __forceinline__ void plane_fwd_body(const PlaneArgs &args) {
         p = udiv16(q, A.m_h1);
         i = q - p * A.H1;
     };
-    // The loads are unconditional, from clamped addresses (the commit zeroes what
-    // lies outside the images): a register that a load may or may not fill would
-    // make the compiler wait for every load in flight before touching it.
+    // lanes past the last item load the last item again (their registers are not
+    // used): all loads unconditional measured faster here than skipping them
     auto load_patch = [&](const auto &A, uint32_t (&r)[2][IO::kWords], const T *xb, int live, int g) {
         int p, i, m;
         patch_of(A, min(g, A.commit_items - 1), p, i, m);
-        p = min(p, live - 1);
-        const int col0 = 2 * CW * m;
-        const T *src = xb + (p * CHW + (2 * i) * A.W + col0);
-        IO::load_row(r[0], src, A.vec, col0, A.W);
-        IO::load_row(r[1], src + (2 * i + 1 < A.H ? A.W : 0), A.vec, col0, A.W);
-    };
-    // Zero the rows of a loaded patch that lie outside the images.
-    auto mask_patch = [&](uint32_t (&r)[2][IO::kWords], int live, int p, int i, int H) {
-#pragma unroll
-        for (int w = 0; w < IO::kWords; ++w) {
-            if (p >= live) r[0][w] = 0;
-            if (p >= live || 2 * i + 1 >= H) r[1][w] = 0;
-        }
+        load_patch_clamped<T, CW>(r, xb, p, i, m, live, CHW, A.H, A.W, A.vec);
     };
     // Weight-table entry e of channel c: the two raw factors of its folded value
     // (loaded here, folded by fold_weight).  Level l, band b: s(l,b) 4^-l W(l,b)
@@ -338,7 +350,7 @@ __device__ __forceinline__ void plane_fwd_body(const PlaneArgs &args) {
                 if (g >= a.commit_items) continue;
                 int p, i, m;
                 patch_of(a, g, p, i, m);
-                mask_patch(raw[k], live, p, i, H);
+                mask_patch<T, CW>(raw[k], p, i, live, H);
                 commit_patch<K, T, CW>(s4, sy1, pw1, raw[k], p, i, m);
             }
             const T *xb = static_cast<const T *>(a.x) + ((size_t)n0 * a.C + c) * HW;
@@ -347,7 +359,7 @@ __device__ __forceinline__ void plane_fwd_body(const PlaneArgs &args) {
                 load_patch(a, r, xb, live, g);
                 int p, i, m;
                 patch_of(a, g, p, i, m);
-                mask_patch(r, live, p, i, H);
+                mask_patch<T, CW>(r, p, i, live, H);
                 commit_patch<K, T, CW>(s4, sy1, pw1, r, p, i, m);
             }
         }
@@ -411,7 +423,7 @@ __device__ __forceinline__ void plane_fwd_body(const PlaneArgs &args) {
         // 4. level 1 + base conv + deeper patterns, one store per pixel pair
         {
             const float bias = smem[a.wt + (4 * L + 1) * KK];
-            for (int t = tid; t < a.final_items; t += NT) {
+            auto final_item = [&](int t) __attribute__((always_inline)) {
                 // opaque per item: the weight-table reads stay next to their use
                 const int sy1 = opaque(a.sy1), wt = opaque(a.wt);
                 const int s = udiv16(t, a.m_strip), r = t - s * (PB * a.W1);
@@ -525,7 +537,8 @@ __device__ __forceinline__ void plane_fwd_body(const PlaneArgs &args) {
                         }
                     }
                 }
-            }
+            };
+            for (int t = tid; t < a.final_items; t += NT) final_item(t);
         }
     }
 }

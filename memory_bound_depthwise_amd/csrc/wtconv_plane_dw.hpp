@@ -80,16 +80,13 @@ __global__ __launch_bounds__(kDwbThreads, 2) void plane_dwb_kernel(PlaneDwbArgs 
         p = udiv16(q, a.m_h1);
         i = q - p * a.H1;
     };
+    // loads from clamped addresses (see load_patch_clamped); lanes past the last
+    // item load nothing (their registers are not used)
     auto load_patch = [&](uint32_t (&rw)[2][IO::kWords], const T *base, int live, int g) {
-#pragma unroll
-        for (int w = 0; w < IO::kWords; ++w) rw[0][w] = rw[1][w] = 0;
+        if (g >= a.commit_items) return;
         int p, i, m;
         patch_of(g, p, i, m);
-        if (p >= live) return;
-        const int col0 = 2 * CW * m;
-        const T *src = base + (p * CHW + (2 * i) * a.W + col0);
-        IO::load_row(rw[0], src, a.vec, col0, a.W);
-        if (2 * i + 1 < a.H) IO::load_row(rw[1], src + a.W, a.vec, col0, a.W);
+        load_patch_clamped<T, CW>(rw, base, p, i, m, live, CHW, a.H, a.W, a.vec);
     };
     // polyphase cells of a patch: CW cells from (row i, cell m CW) of plane p
     auto store_patch = [&](float4 *arr, int stride, int row_off, int col_off, const uint32_t (&rw)[2][IO::kWords],
@@ -106,10 +103,8 @@ __global__ __launch_bounds__(kDwbThreads, 2) void plane_dwb_kernel(PlaneDwbArgs 
         const int n0 = g * PB, live = min(PB, a.n - n0);
 #pragma unroll
         for (int k = 0; k < SLOTS; ++k) {
-            const int e = tid + k * NT;
-            if (e >= a.commit_items) continue;
-            load_patch(xr[k], xc + (size_t)n0 * CHW, live, e);
-            load_patch(dr[k], dc + (size_t)n0 * CHW, live, e);
+            load_patch(xr[k], xc + (size_t)n0 * CHW, live, tid + k * NT);
+            load_patch(dr[k], dc + (size_t)n0 * CHW, live, tid + k * NT);
         }
     };
 
@@ -129,6 +124,8 @@ __global__ __launch_bounds__(kDwbThreads, 2) void plane_dwb_kernel(PlaneDwbArgs 
                 if (e >= a.commit_items) continue;
                 int p, i, m;
                 patch_of(e, p, i, m);
+                mask_patch<T, CW>(xr[k], p, i, live, a.H);
+                mask_patch<T, CW>(dr[k], p, i, live, a.H);
                 store_patch(s4, sx, RC, kPlaneCO, xr[k], p, i, m);
                 store_patch(s4 + ax, sd, 0, 0, dr[k], p, i, m);
             }
@@ -137,8 +134,10 @@ __global__ __launch_bounds__(kDwbThreads, 2) void plane_dwb_kernel(PlaneDwbArgs 
                 int p, i, m;
                 patch_of(e, p, i, m);
                 load_patch(rw, xc + (size_t)n0 * CHW, live, e);
+                mask_patch<T, CW>(rw, p, i, live, a.H);
                 store_patch(s4, sx, RC, kPlaneCO, rw, p, i, m);
                 load_patch(rw, dc + (size_t)n0 * CHW, live, e);
+                mask_patch<T, CW>(rw, p, i, live, a.H);
                 store_patch(s4 + ax, sd, 0, 0, rw, p, i, m);
             }
         }
@@ -282,16 +281,13 @@ __global__ __launch_bounds__(kDwlThreads, 3) void plane_dwl_kernel(PlaneDwlArgs 
         p = udiv16(q, a.m_gw);
         m = q - p * a.Gw;
     };
+    // loads from clamped addresses (see load_patch_clamped); lanes past the last
+    // item load nothing (their registers are not used)
     auto load_patch = [&](uint32_t (&rw)[2][IO::kWords], const T *base, int live, int g) {
-#pragma unroll
-        for (int w = 0; w < IO::kWords; ++w) rw[0][w] = rw[1][w] = 0;
+        if (g >= a.commit_items) return;
         int p, i, m;
         patch_of(g, p, i, m);
-        if (p >= live) return;
-        const int col0 = 2 * CW * m;
-        const T *src = base + (p * CHW + (2 * i) * a.W + col0);
-        IO::load_row(rw[0], src, a.vec, col0, a.W);
-        if (2 * i + 1 < a.H) IO::load_row(rw[1], src + a.W, a.vec, col0, a.W);
+        load_patch_clamped<T, CW>(rw, base, p, i, m, live, CHW, a.H, a.W, a.vec);
     };
     // level-1 bands of a patch's CW cells: element (row, col + q) of each band
     // (column stride cs, band size bs)
@@ -314,10 +310,8 @@ __global__ __launch_bounds__(kDwlThreads, 3) void plane_dwl_kernel(PlaneDwlArgs 
         const int n0 = g * PB, live = min(PB, a.n - n0);
 #pragma unroll
         for (int k = 0; k < SLOTS; ++k) {
-            const int e = tid + k * NT;
-            if (e >= a.commit_items) continue;
-            load_patch(xr[k], xc + (size_t)n0 * CHW, live, e);
-            load_patch(dr[k], dc + (size_t)n0 * CHW, live, e);
+            load_patch(xr[k], xc + (size_t)n0 * CHW, live, tid + k * NT);
+            load_patch(dr[k], dc + (size_t)n0 * CHW, live, tid + k * NT);
         }
     };
 
@@ -349,6 +343,8 @@ __global__ __launch_bounds__(kDwlThreads, 3) void plane_dwl_kernel(PlaneDwlArgs 
                 if (e >= a.commit_items) continue;
                 int p, i, m;
                 patch_of(e, p, i, m);
+                mask_patch<T, CW>(xr[k], p, i, live, a.H);
+                mask_patch<T, CW>(dr[k], p, i, live, a.H);
                 store_bands(xbase, xs, xb, xr[k], i, p * pw1 + m * CW);
                 store_bands(gbase, gs, gb, dr[k], i, p * pw1 + m * CW);
             }
@@ -357,8 +353,10 @@ __global__ __launch_bounds__(kDwlThreads, 3) void plane_dwl_kernel(PlaneDwlArgs 
                 int p, i, m;
                 patch_of(e, p, i, m);
                 load_patch(rw, xc + (size_t)n0 * CHW, live, e);
+                mask_patch<T, CW>(rw, p, i, live, a.H);
                 store_bands(xbase, xs, xb, rw, i, p * pw1 + m * CW);
                 load_patch(rw, dc + (size_t)n0 * CHW, live, e);
+                mask_patch<T, CW>(rw, p, i, live, a.H);
                 store_bands(gbase, gs, gb, rw, i, p * pw1 + m * CW);
             }
         }
