@@ -74,7 +74,8 @@ def _family(short: str) -> str:
 
 def traffic(workload, fetch_db, write_db, copy_fetch_db, copy_write_db, copy_bytes):
     """Measured HBM bytes per launch for every kernel of the workload's launch plan:
-    a counter row matches a planned launch by kernel family and grid size."""
+    a counter row matches a planned launch by kernel family and grid size (by family
+    alone when the family ran with one grid size only)."""
     import os
     root = os.path.dirname(os.path.abspath(__file__))
     sys.path.insert(0, root)
@@ -95,6 +96,13 @@ def traffic(workload, fetch_db, write_db, copy_fetch_db, copy_write_db, copy_byt
             for e in wt.wtconv_plan_launches(desc, op):
                 fam = e["name"].split("<")[0]
                 match = rows.get((fam, e["workgroups"] * e["threads"]))
+                if not match:
+                    # A persistent kernel's grid follows the device's occupancy, which
+                    # the host-side plan does not know: take the family's rows when
+                    # they all share one grid.
+                    grids = {g for (f, g) in rows if f == fam}
+                    if len(grids) == 1:
+                        match = rows[(fam, grids.pop())]
                 if not match or match[0]["write_bytes"] is None:
                     continue
                 r = match[0]
