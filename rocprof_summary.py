@@ -8,6 +8,9 @@
     python rocprof_summary.py traffic <workload> <fetch.db> <write.db> <copy_fetch.db> <copy_write.db> <copy_bytes>
         the same, keyed by the library's kernel names for the workload's launch plan
         (the record bench.py reads from profiles/traffic_<workload>.txt)
+    python rocprof_summary.py sq <results.db> ...
+        shader-sequencer counters (SQ_*) per kernel, averaged over dispatches; several
+        runs (one counter group each) are merged
 """
 from __future__ import annotations
 
@@ -130,6 +133,26 @@ def counters_md(rec):
     return "\n".join(out)
 
 
+def sq(*dbs):
+    """Per kernel (plane-resident and fused kernels of the library): every SQ_ counter
+    found in the given runs, averaged over its dispatches."""
+    agg = collections.defaultdict(dict)
+    for db in dbs:
+        for (k, c, _g), v in _counter(db).items():
+            if c.startswith("SQ_") and k.startswith("wtc::"):
+                agg[k][c] = v
+    return agg
+
+
+def sq_md(agg):
+    names = sorted({c for v in agg.values() for c in v})
+    out = ["| kernel | " + " | ".join(n.removeprefix("SQ_") for n in names) + " |",
+           "|---|" + "---|" * len(names)]
+    for k, v in sorted(agg.items()):
+        out.append(f"| `{k}` | " + " | ".join(f"{v[n]:.4g}" if n in v else "" for n in names) + " |")
+    return "\n".join(out)
+
+
 if __name__ == "__main__":
     md = "--md" in sys.argv
     if md:
@@ -142,3 +165,6 @@ if __name__ == "__main__":
         print(counters_md(rec) if md else json.dumps(rec, indent=1))
     elif sys.argv[1] == "traffic":
         print(json.dumps(traffic(sys.argv[2], *sys.argv[3:7], float(sys.argv[7])), indent=1))
+    elif sys.argv[1] == "sq":
+        agg = sq(*sys.argv[2:])
+        print(sq_md(agg) if md else json.dumps(agg, indent=1))
