@@ -39,6 +39,8 @@ WORKLOADS = {
     "hires_L4": ["hires_L4"], "hires_L5": ["hires_L5"],
     "stack": ["stack_1", "stack_2", "stack_3", "stack_4"],
     "tiny": ["tiny"],
+    # plain depthwise convolutions (levels = 0) on the stage1 shape, for comparison
+    "dw5": ["dw5"], "dw7": ["dw7"],
 }
 
 
@@ -222,6 +224,11 @@ def main():
     case_ls = {c.name: case_launches(c) for c in cases}
     step_bytes = sum(b for c in cases for _, _, b, _ in case_ls[c.name])
     step_flops = sum(f for c in cases for _, _, _, f in case_ls[c.name])
+    # context: the bytes the same step moves when it follows the paper's pass
+    # structure (one analysis + conv launch per level, coefficients through HBM,
+    # one synthesis pass with the base conv fused in; the per-level kernels here)
+    per_level_bytes = sum(b for c in cases
+                          for _, _, b, _ in traffic.launches(c.n, c.c, c.h, c.w, c.k, c.levels, es(c)))
 
     for i in range(args.warmup):
         run_step(layers, i, wt)
@@ -307,6 +314,13 @@ def main():
         "config": {"workload": args.workload, "shapes": describe(cases), "pass": "forward + dx + dW",
                    "rotate_buffer_sets": args.rotate, "step_bytes": step_bytes, "step_flops": step_flops},
         "hbm_frac": round(value / HBM_PEAK_GBS, 4),
+        "per_level_model": {
+            "step_bytes": per_level_bytes,
+            "gbs": round(per_level_bytes / (ms_per_step * 1e-3) / 1e9, 1),
+            "hbm_frac": round(per_level_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
+            "note": "bytes of the per-level pass structure over the measured step time: the bandwidth "
+                    "a per-level implementation would need to match this step; not moved by these kernels",
+        },
         "source_digest": digest,
         "kernels": kernels,
         "roofline": roof,

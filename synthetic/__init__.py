@@ -155,6 +155,9 @@ def baseline_cases() -> dict:
     stage1/stage2/stage3: WTConvNeXt-T stage shapes at batch 64 (bf16).
     hires_L1..L5: x[8,128,256,256] bf16 for L = 1..5.
     stack_1..stack_4: the four WTConvNeXt-T stage layers at batch 128 (bf16).
+    dw5, dw7: plain depthwise convolutions (levels = 0) on the stage1 shape, k = 5
+    (the wavelet path's own kernel size) and k = 7 (the kernel a WTConv layer
+    replaces in ConvNeXt): the two comparison protocols of the paper's §5.
     """
     cases = {
         "tiny": Case(1, 8, 16, 16, 5, 2, "f32", 0, w_std=0.1, b_std=0.0, name="tiny"),
@@ -166,4 +169,6 @@ def baseline_cases() -> dict:
         cases[f"hires_L{L}"] = Case(8, 128, 256, 256, 5, L, "bf16", 0, name=f"hires_L{L}")
     for i, (c, hw, L) in enumerate([(96, 56, 3), (192, 28, 2), (384, 14, 1), (768, 7, 1)], 1):
         cases[f"stack_{i}"] = Case(128, c, hw, hw, 5, L, "bf16", 0, name=f"stack_{i}")
+    for k in (5, 7):
+        cases[f"dw{k}"] = Case(64, 96, 56, 56, k, 0, "bf16", 0, name=f"dw{k}")
     return cases

@@ -117,8 +117,8 @@ def _sampled_check(case, planes, channels):
     del torch
 
 
-FULL = ["stage1", "stage2", "stage3", "hires_L1", "hires_L3", "hires_L5",
-        "stack_1", "stack_2", "stack_3", "stack_4"]
+FULL = ["stage1", "stage2", "stage3", "hires_L1", "hires_L2", "hires_L3", "hires_L4", "hires_L5",
+        "stack_1", "stack_2", "stack_3", "stack_4", "dw5", "dw7"]
 
 
 @pytest.mark.parametrize("name", FULL)
