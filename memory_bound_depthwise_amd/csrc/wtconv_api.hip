@@ -164,6 +164,8 @@ Tiling pick_tiling(Kind kind, int K, int n, int C, int Ho, int Wo, int VW) {
         if (sp_max == 1 || lds_bytes(kind, K, t) <= kLdsBudget) break;
         sp_max = std::max(1, sp_max / 2);
     }
+    // the synthesis kernel reads the deep levels per strip of kRH rows aligned to kRH
+    if (kind == Kind::Synth) t.TY = t.SP * kRH;
     // plane stacking: best lane occupancy, then the smaller PB
     const long long min_blocks = 512;
     double best = -1.0;

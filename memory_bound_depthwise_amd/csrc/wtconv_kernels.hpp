@@ -264,44 +264,187 @@ __host__ __device__ __forceinline__ int stage_width(int TX, int R, int VW) {
 // written to the next carrier.
 // ---------------------------------------------------------------------------
 
+// Staging loops take their indices in batches of kStageBatch per thread: every load
+// of a batch is issued, from an address clamped into the tensor, before any of them
+// is used (out-of-range values are masked afterwards).  A load that is converted or
+// tested right after it is issued makes the wavefront wait for it alone, and a
+// loop of such loads pays one memory latency per iteration.
+constexpr int kStageBatch = 4;
+
+// The four raw elements of one 2 x 2 pixel block: with `pairs`, one two-element
+// load per row (bfloat16: one word per row in w[0], w[1]; float32: w[0..3]);
+// otherwise one element per word, (x00, x01, x10, x11).
+template <typename T>
+__device__ __forceinline__ void block_load_raw(const T *src, size_t o0, size_t o1, int dc, bool pairs,
+                                               uint32_t (&w)[4]) {
+    if (pairs) {
+        if constexpr (sizeof(T) == 2) {
+            w[0] = *reinterpret_cast<const uint32_t *>(src + o0);
+            w[1] = *reinterpret_cast<const uint32_t *>(src + o1);
+        } else {
+            const uint2 a = *reinterpret_cast<const uint2 *>(src + o0), b = *reinterpret_cast<const uint2 *>(src + o1);
+            w[0] = a.x;
+            w[1] = a.y;
+            w[2] = b.x;
+            w[3] = b.y;
+        }
+    } else {
+        if constexpr (sizeof(T) == 2) {
+            const uint16_t *s16 = reinterpret_cast<const uint16_t *>(src);
+            w[0] = s16[o0];
+            w[1] = s16[o0 + dc];
+            w[2] = s16[o1];
+            w[3] = s16[o1 + dc];
+        } else {
+            const uint32_t *s32 = reinterpret_cast<const uint32_t *>(src);
+            w[0] = s32[o0];
+            w[1] = s32[o0 + dc];
+            w[2] = s32[o1];
+            w[3] = s32[o1 + dc];
+        }
+    }
+}
+template <typename T>
+__device__ __forceinline__ void block_unpack(const uint32_t (&w)[4], bool pairs, float &x00, float &x01, float &x10,
+                                             float &x11) {
+    if (pairs && sizeof(T) == 2) {
+        x00 = __uint_as_float(w[0] << 16);
+        x01 = __uint_as_float(w[0] & 0xffff0000u);
+        x10 = __uint_as_float(w[1] << 16);
+        x11 = __uint_as_float(w[1] & 0xffff0000u);
+    } else if (sizeof(T) == 2) {
+        x00 = __uint_as_float(w[0] << 16);
+        x01 = __uint_as_float(w[1] << 16);
+        x10 = __uint_as_float(w[2] << 16);
+        x11 = __uint_as_float(w[3] << 16);
+    } else {
+        x00 = __uint_as_float(w[0]);
+        x01 = __uint_as_float(w[1]);
+        x10 = __uint_as_float(w[2]);
+        x11 = __uint_as_float(w[3]);
+    }
+}
+
+// q / d and q % d for 0 <= q < 2^23, d >= 1, given rd = 1 / d in float: the float
+// quotient of q + 1/2 is within one of the true one, and the remainder fixes it.
+__device__ __forceinline__ void small_divmod(int q, int d, float rd, int &quo, int &rem) {
+    int v = (int)(((float)q + 0.5f) * rd);
+    int r = q - v * d;
+    if (r < 0) {
+        --v;
+        r += d;
+    } else if (r >= d) {
+        ++v;
+        r -= d;
+    }
+    quo = v;
+    rem = r;
+}
+
+// Threads walk a staged grid with a fixed column each: thread t takes column
+// t % cols and rows t / cols, t / cols + step, ... (step = threads / cols; cols is
+// at most the thread count), so nothing is divided per element.
 template <typename T>
 __device__ __forceinline__ void haar_stage(const T *__restrict__ in, T *__restrict__ carrier, float *bands,
                                            int bandsz, int stride, int PB, int rows, int cols, int r0, int c0,
                                            int n0, int n_end, int c, int C, int Hi, int Wi, int Ho, int Wo,
                                            int vr1, int cr0, int cr1, int cc0, int cc1, int pairs) {
-    const int per_plane = rows * cols;
     const size_t in_plane = (size_t)Hi * Wi, out_plane = (size_t)Ho * Wo;
-    for (int idx = threadIdx.x; idx < PB * per_plane; idx += blockDim.x) {
-        const int p = idx / per_plane, rem = idx - p * per_plane;
-        const int ci = rem / cols, cj = rem - ci * cols;
-        const int nn = n0 + p, gi = r0 + ci, gj = c0 + cj;
-        float x00 = 0.f, x01 = 0.f, x10 = 0.f, x11 = 0.f;
-        const bool inside = nn < n_end && gi >= 0 && gi < vr1 && gj >= 0 && gj < Wo;
-        if (inside) {
-            const T *src = in + ((size_t)nn * C + c) * in_plane;
-            const size_t o0 = (size_t)(2 * gi) * Wi + 2 * gj;
-            const bool r1 = 2 * gi + 1 < Hi;
-            if (pairs) {
-                act_load2(src, o0, x00, x01);
-                if (r1) act_load2(src, o0 + Wi, x10, x11);
-            } else {
-                const bool c1 = 2 * gj + 1 < Wi;
-                x00 = act_load(src, o0);
-                if (c1) x01 = act_load(src, o0 + 1);
-                if (r1) {
-                    x10 = act_load(src, o0 + Wi);
-                    if (c1) x11 = act_load(src, o0 + Wi + 1);
-                }
+    const int step = blockDim.x / cols, cj = threadIdx.x % cols, rs = threadIdx.x / cols;
+    if (rs >= step) return;
+    const int gj = c0 + cj, gjc = min(max(gj, 0), Wo - 1);
+    const bool col_in = gj >= 0 && gj < Wo, c1 = 2 * gjc + 1 < Wi;
+    const bool carry_col = carrier && col_in && gj >= cc0 && gj < cc1;
+    for (int p = 0; p < PB; ++p) {
+        const int nn = n0 + p;
+        const bool plane_in = nn < n_end && col_in;
+        const T *src = in + ((size_t)min(nn, n_end - 1) * C + c) * in_plane + 2 * gjc;
+        float *dst0 = bands + (size_t)p * 4 * bandsz + cj;
+        for (int base = rs; base < rows; base += kStageBatch * step) {
+            uint32_t raw[kStageBatch][4];
+#pragma unroll
+            for (int k = 0; k < kStageBatch; ++k) {
+                // clamped into the image: the block itself when it is inside
+                const int gi = min(max(r0 + min(base + k * step, rows - 1), 0), Ho - 1);
+                const size_t o0 = (size_t)(2 * gi) * Wi, o1 = 2 * gi + 1 < Hi ? o0 + Wi : o0;
+                block_load_raw<T>(src, o0, o1, c1 ? 1 : 0, pairs, raw[k]);
+            }
+            __builtin_amdgcn_sched_barrier(0);  // keep the batch's loads ahead of every use
+            // rows past the end repeat the last row (the same values to the same
+            // place): no branch, so the loads are not sunk into one
+#pragma unroll
+            for (int k = 0; k < kStageBatch; ++k) {
+                const int ci = min(base + k * step, rows - 1);
+                const int gi = r0 + ci;
+                const bool inside = plane_in && gi >= 0 && gi < vr1;
+                float x00, x01, x10, x11;
+                block_unpack<T>(raw[k], pairs, x00, x01, x10, x11);
+                const bool r1 = 2 * gi + 1 < Hi;
+                x00 = inside ? x00 : 0.f;
+                x01 = inside && c1 ? x01 : 0.f;
+                x10 = inside && r1 ? x10 : 0.f;
+                x11 = inside && r1 && c1 ? x11 : 0.f;
+                const float s0 = x00 + x01, s1 = x10 + x11, d0 = x00 - x01, d1 = x10 - x11;
+                float *dst = dst0 + ci * stride;
+                dst[0] = s0 + s1;           // 2 LL
+                dst[bandsz] = s0 - s1;      // 2 LH
+                dst[2 * bandsz] = d0 + d1;  // 2 HL
+                dst[3 * bandsz] = d0 - d1;  // 2 HH
+                if (carry_col && inside && gi >= cr0 && gi < cr1 && base + k * step < rows)
+                    act_store(carrier, ((size_t)nn * C + c) * out_plane + (size_t)gi * Wo + gj, 0.5f * (s0 + s1));
             }
         }
-        const float s0 = x00 + x01, s1 = x10 + x11, d0 = x00 - x01, d1 = x10 - x11;
-        float *dst = bands + (size_t)p * 4 * bandsz + ci * stride + cj;
-        dst[0] = s0 + s1;           // 2 LL
-        dst[bandsz] = s0 - s1;      // 2 LH
-        dst[2 * bandsz] = d0 + d1;  // 2 HL
-        dst[3 * bandsz] = d0 - d1;  // 2 HH
-        if (carrier && inside && gi >= cr0 && gi < cr1 && gj >= cc0 && gj < cc1)
-            act_store(carrier, ((size_t)nn * C + c) * out_plane + (size_t)gi * Wo + gj, 0.5f * (s0 + s1));
+    }
+}
+
+// Raw words of VW consecutive elements (converted once the batch is in flight).
+template <int VW, typename T>
+struct RawVec {
+    static constexpr int kWords = (VW * (int)sizeof(T) + 3) / 4;
+    uint32_t w[kWords];
+};
+template <int VW, typename T>
+__device__ __forceinline__ void raw_load(const T *p, RawVec<VW, T> &r) {
+    constexpr int bytes = VW * (int)sizeof(T);
+    if constexpr (bytes == 16) {
+        const uint4 q = *reinterpret_cast<const uint4 *>(p);
+        r.w[0] = q.x;
+        r.w[1] = q.y;
+        r.w[2] = q.z;
+        r.w[3] = q.w;
+    } else if constexpr (bytes == 8) {
+        const uint2 q = *reinterpret_cast<const uint2 *>(p);
+        r.w[0] = q.x;
+        r.w[1] = q.y;
+    } else if constexpr (bytes == 4) {
+        r.w[0] = *reinterpret_cast<const uint32_t *>(p);
+    } else {
+        static_assert(bytes == 2, "one bfloat16");
+        r.w[0] = *reinterpret_cast<const uint16_t *>(p);
+    }
+}
+template <int VW, typename T>
+__device__ __forceinline__ float raw_elem(const RawVec<VW, T> &r, int e) {
+    if constexpr (sizeof(T) == 2) {
+        const uint32_t wv = r.w[e >> 1];
+        return __uint_as_float((e & 1) ? (wv & 0xffff0000u) : (wv << 16));
+    } else {
+        return __uint_as_float(r.w[e]);
+    }
+}
+
+// VW floats to LDS in 16-byte (or narrower) writes.
+template <int VW>
+__device__ __forceinline__ void lds_store(float *d, const float *v) {
+    if constexpr (VW == 8) {
+        reinterpret_cast<float4 *>(d)[0] = make_float4(v[0], v[1], v[2], v[3]);
+        reinterpret_cast<float4 *>(d)[1] = make_float4(v[4], v[5], v[6], v[7]);
+    } else if constexpr (VW == 4) {
+        *reinterpret_cast<float4 *>(d) = make_float4(v[0], v[1], v[2], v[3]);
+    } else if constexpr (VW == 2) {
+        *reinterpret_cast<float2 *>(d) = make_float2(v[0], v[1]);
+    } else {
+        d[0] = v[0];
     }
 }
 
@@ -309,27 +452,48 @@ __device__ __forceinline__ void haar_stage(const T *__restrict__ in, T *__restri
 // zero outside the plane, at or below row row_hi (<= H), and, when mask_lo <
 // mask_hi, outside those columns;
 // converted to float32 in LDS with row stride `width`.  c0 and width are multiples
-// of VW and W is a multiple of VW, so each vector is wholly inside or outside.
+// of VW and W is a multiple of VW, so each vector is wholly inside or outside; dst
+// is aligned to VW floats.  Thread t stages vector column t % (width / VW).
 template <int VW, typename T>
 __device__ __forceinline__ void pixel_stage_v(const T *__restrict__ src, float *dst, int PB, int rows, int width,
                                               int r0, int c0, int n0, int n_end, int c, int C, int H, int W,
                                               int row_hi, int mask_lo, int mask_hi) {
-    const int vpr = width / VW, per_plane = rows * vpr;
+    const int vpr = width / VW;
+    const int step = blockDim.x / vpr, vc = threadIdx.x % vpr, rs = threadIdx.x / vpr;
+    if (rs >= step) return;
     const size_t plane = (size_t)H * W;
-    for (int idx = threadIdx.x; idx < PB * per_plane; idx += blockDim.x) {
-        const int p = idx / per_plane, rem = idx - p * per_plane;
-        const int ri = rem / vpr, vc = rem - ri * vpr;
-        const int nn = n0 + p, gi = r0 + ri, gc = c0 + vc * VW;
-        float v[VW];
+    const int gc = c0 + vc * VW, gcc = min(max(gc, 0), W - VW);
+    bool keep[VW];
 #pragma unroll
-        for (int e = 0; e < VW; ++e) v[e] = 0.f;
-        if (nn < n_end && gi >= 0 && gi < row_hi && gc >= 0 && gc < W)
-            act_loadv<VW>(src + ((size_t)nn * C + c) * plane, (size_t)gi * W + gc, v);
-        float *d = dst + (size_t)p * rows * width + ri * width + vc * VW;
+    for (int e = 0; e < VW; ++e) {
+        const int col = gc + e;
+        keep[e] = gc >= 0 && gc < W && !(mask_lo < mask_hi && (col < mask_lo || col >= mask_hi));
+    }
+    for (int p = 0; p < PB; ++p) {
+        const int nn = n0 + p;
+        const bool plane_in = nn < n_end;
+        const T *sp = src + ((size_t)min(nn, n_end - 1) * C + c) * plane + gcc;
+        float *dp = dst + (size_t)p * rows * width + vc * VW;
+        for (int base = rs; base < rows; base += kStageBatch * step) {
+            RawVec<VW, T> raw[kStageBatch];
 #pragma unroll
-        for (int e = 0; e < VW; ++e) {
-            const int col = gc + e;
-            d[e] = (mask_lo < mask_hi && (col < mask_lo || col >= mask_hi)) ? 0.f : v[e];
+            for (int k = 0; k < kStageBatch; ++k) {
+                const int gi = min(max(r0 + min(base + k * step, rows - 1), 0), H - 1);
+                raw_load<VW, T>(sp + (size_t)gi * W, raw[k]);
+            }
+            __builtin_amdgcn_sched_barrier(0);  // keep the batch's loads ahead of every use
+            // rows past the end repeat the last row (the same values to the same
+            // place): no branch, so the loads are not sunk into one
+#pragma unroll
+            for (int k = 0; k < kStageBatch; ++k) {
+                const int ri = min(base + k * step, rows - 1);
+                const int gi = r0 + ri;
+                const bool rin = plane_in && gi >= 0 && gi < row_hi;
+                float v[VW];
+#pragma unroll
+                for (int e = 0; e < VW; ++e) v[e] = rin && keep[e] ? raw_elem<VW, T>(raw[k], e) : 0.f;
+                lds_store<VW>(dp + (size_t)ri * width, v);
+            }
         }
     }
 }
@@ -421,10 +585,12 @@ __global__ __launch_bounds__(256) void level_fwd_kernel(LevelArgs a) {
     }
     __syncthreads();
 
-    const int per_plane = t.SP * t.TX;
-    for (int it = lane; it < t.PB * per_plane; it += kWave) {
-        const int p = it / per_plane, rem = it - p * per_plane;
-        const int s = rem / t.TX, j = rem - s * t.TX;
+    // lane: column lane % TX, strips (plane, strip) = lane / TX, + kWave / TX, ...
+    const int wstep = kWave / t.TX, j = lane % t.TX, q0 = lane / t.TX, nq = t.PB * t.SP;
+    const float rsp = 1.f / (float)t.SP;
+    for (int q = q0 < wstep ? q0 : nq; q < nq; q += wstep) {
+        int p, s;
+        small_divmod(q, t.SP, rsp, p, s);
         float acc[kRH];
 #pragma unroll
         for (int i = 0; i < kRH; ++i) acc[i] = 0.f;
@@ -441,9 +607,12 @@ __global__ __launch_bounds__(256) void level_fwd_kernel(LevelArgs a) {
     const int Wq = 2 * a.Wo;
     const size_t q_plane = (size_t)4 * a.Ho * a.Wo, zb = (size_t)t.PB * t.TY * t.TX;
     const int per_tile = t.TY * t.TX;
-    for (int idx = threadIdx.x; idx < t.PB * per_tile; idx += blockDim.x) {
-        const int p = idx / per_tile, rem = idx - p * per_tile;
-        const int r = rem / t.TX, j = rem - r * t.TX;
+    const int cstep = blockDim.x / t.TX, cj = threadIdx.x % t.TX, r0 = threadIdx.x / t.TX, nr = t.PB * t.TY;
+    const float rty = 1.f / (float)t.TY;
+    for (int qr = r0 < cstep ? r0 : nr; qr < nr; qr += cstep) {
+        int p, r;
+        small_divmod(qr, t.TY, rty, p, r);
+        const int j = cj, rem = r * t.TX + j;
         const int nn = n0 + p, gi = bp.ty0 + r, gj = bp.tx0 + j;
         if (nn >= a.n || gi >= a.Ho || gj >= a.Wo) continue;
         const float *z = zbuf + (size_t)p * per_tile + rem;
@@ -485,29 +654,62 @@ __global__ __launch_bounds__(256) void synth_kernel(SynthArgs a) {
 
     T *y = static_cast<T *>(a.y);
     const size_t plane = (size_t)a.H * a.W;
-    const int per_plane = t.SP * t.TX;
-    for (int it = threadIdx.x; it < t.PB * per_plane; it += blockDim.x) {
-        const int p = it / per_plane, rem = it - p * per_plane;
-        const int s = rem / t.TX, j = rem - s * t.TX;
+    // thread: column threadIdx.x % TX, strips (plane, strip) = threadIdx.x / TX, + step, ...
+    const int step = blockDim.x / t.TX, j = threadIdx.x % t.TX, q0 = threadIdx.x / t.TX, nq = t.PB * t.SP;
+    const float rsp = 1.f / (float)t.SP;
+    for (int q = q0 < step ? q0 : nq; q < nq; q += step) {
+        int p, s;
+        small_divmod(q, t.SP, rsp, p, s);
         const int nn = n0 + p, gx = bp.tx0 + j, gy0 = bp.ty0 + s * kRH;
         if (nn >= a.n || gx >= a.W) continue;
         const int rows = min(kRH, min(a.H, bp.ty0 + t.TY) - gy0);  // rows of this strip in the tile
         const size_t pidx = (size_t)nn * a.C + c;
-        // Eq. 7: level l contributes Q(l)[y >> (l-1)][x >> (l-1)]
+        // Eq. 7: level l + 1 contributes Q(l+1)[y >> l][x >> l].  gy0 is a multiple of
+        // kRH = 8 (the tiling keeps TY one), so row i of the strip reads row
+        // (gy0 >> l) + (i >> l) of level l + 1: 8, 4, 2, then 1 distinct values.  They
+        // are loaded raw (row clamped into the plane) before the conv and added after
+        // it, so that their latency overlaps the conv.
+        uint32_t qraw[kMaxLevels][kRH];
+        const int ylast = a.H - 1;
+#pragma unroll
+        for (int l = 0; l < kMaxLevels; ++l) {
+            if (l < a.L) {
+                const T *ql = static_cast<const T *>(a.q[l]) + pidx * (size_t)a.qplane[l] + (gx >> l);
+#pragma unroll
+                for (int r = 0; r < (kRH >> l > 0 ? kRH >> l : 1); ++r) {
+                    const int row = min((gy0 >> l) + r, ylast >> l);
+                    if constexpr (sizeof(T) == 2)  // widened after the conv: no wait here
+                        qraw[l][r] = reinterpret_cast<const uint16_t *>(ql)[(size_t)row * a.wq[l]];
+                    else
+                        qraw[l][r] = reinterpret_cast<const uint32_t *>(ql)[(size_t)row * a.wq[l]];
+                }
+            }
+        }
+        __builtin_amdgcn_sched_barrier(0);  // the loads above stay ahead of the conv
         float acc[kRH];
 #pragma unroll
-        for (int i = 0; i < kRH; ++i) acc[i] = bias;
-        for (int l = 0; l < a.L; ++l) {
-            const T *ql = static_cast<const T *>(a.q[l]) + pidx * (size_t)a.qplane[l] + (gx >> l);
+        for (int i = 0; i < kRH; ++i) acc[i] = 0.f;
+        conv_strip<K>(smem + (size_t)p * plsz + (s * kRH) * HXW + j + off, HXW, w, acc);
+        __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+        for (int i = 0; i < kRH; ++i) {
+            float qsum = bias;
+#pragma unroll
+            for (int l = 0; l < kMaxLevels; ++l)
+                if (l < a.L) qsum += __uint_as_float(sizeof(T) == 2 ? qraw[l][i >> l] << 16 : qraw[l][i >> l]);
+            acc[i] += qsum;
+        }
+        T *yp = y + pidx * plane + (size_t)gy0 * a.W + gx;
+        // a whole strip stores without a branch per row, so that the conv is not sunk
+        // into per-row blocks (and the coefficient loads not waited for before it)
+        if (rows == kRH) {
+#pragma unroll
+            for (int i = 0; i < kRH; ++i) act_store(yp, (size_t)i * a.W, acc[i]);
+        } else {
 #pragma unroll
             for (int i = 0; i < kRH; ++i)
-                if (i < rows) acc[i] += act_load(ql, (size_t)((gy0 + i) >> l) * a.wq[l]);
+                if (i < rows) act_store(yp, (size_t)i * a.W, acc[i]);
         }
-        conv_strip<K>(smem + (size_t)p * plsz + (s * kRH) * HXW + j + off, HXW, w, acc);
-        T *yp = y + pidx * plane + (size_t)gy0 * a.W + gx;
-#pragma unroll
-        for (int i = 0; i < kRH; ++i)
-            if (i < rows) act_store(yp, (size_t)i * a.W, acc[i]);
     }
 }
 
@@ -545,7 +747,9 @@ __global__ __launch_bounds__(256) void dw_level_kernel(DwLevelArgs a) {
 #pragma unroll
     for (int i = 0; i < KK; ++i) acc[i] = 0.f;
 
-    const int per_plane = t.SP * t.TX;
+    // lane: column lane % TX, strips (plane, strip) = lane / TX, + kWave / TX, ...
+    const int wstep = kWave / t.TX, j = lane % t.TX, q0 = lane / t.TX, nq = t.PB * t.SP;
+    const float rsp = 1.f / (float)t.SP;
     for (int n0 = n_begin; n0 < n_end; n0 += t.PB) {
         __syncthreads();
         haar_stage<T>(xin, static_cast<T *>(a.xc), ys, ysz, HXP, t.PB, HY, HXP, bp.ty0 - R, bp.tx0 - R, n0, n_end,
@@ -555,9 +759,9 @@ __global__ __launch_bounds__(256) void dw_level_kernel(DwLevelArgs a) {
                       a.C, a.Hi, a.Wi, a.Ho, a.Wo, min(a.Ho, bp.ty0 + t.TY), bp.ty0, bp.ty0 + t.TY, bp.tx0,
                       bp.tx0 + t.TX, a.pairs);
         __syncthreads();
-        for (int it = lane; it < t.PB * per_plane; it += kWave) {
-            const int p = it / per_plane, rem = it - p * per_plane;
-            const int s = rem / t.TX, j = rem - s * t.TX;
+        for (int q = q0 < wstep ? q0 : nq; q < nq; q += wstep) {
+            int p, s;
+            small_divmod(q, t.SP, rsp, p, s);
             const float *gp = gs + (size_t)(p * 4 + b) * gsz + (s * kRH) * t.TX + j;
             float g[kRH];
 #pragma unroll
@@ -608,7 +812,9 @@ __global__ __launch_bounds__(256) void dw_base_kernel(DwBaseArgs a) {
 #pragma unroll
     for (int i = 0; i <= KK; ++i) acc[i] = 0.f;
 
-    const int per_plane = t.SP * t.TX;
+    // thread: column threadIdx.x % TX, strips (plane, strip) = threadIdx.x / TX, + step, ...
+    const int step = blockDim.x / t.TX, j = threadIdx.x % t.TX, q0 = threadIdx.x / t.TX, nq = t.PB * t.SP;
+    const float rsp = 1.f / (float)t.SP;
     for (int n0 = n_begin; n0 < n_end; n0 += t.PB) {
         __syncthreads();
         pixel_stage<T>(x, xs, t.VW, t.PB, HY, HXW, bp.ty0 - R, ca, n0, n_end, c, a.C, a.H, a.W, a.H, 0, 0);
@@ -616,9 +822,9 @@ __global__ __launch_bounds__(256) void dw_base_kernel(DwBaseArgs a) {
         pixel_stage<T>(dy, gs, t.VW, t.PB, GY, GW, bp.ty0, ga, n0, n_end, c, a.C, a.H, a.W, row_end, bp.tx0,
                        bp.tx0 + t.TX);
         __syncthreads();
-        for (int it = threadIdx.x; it < t.PB * per_plane; it += blockDim.x) {
-            const int p = it / per_plane, rem = it - p * per_plane;
-            const int s = rem / t.TX, j = rem - s * t.TX;
+        for (int q = q0 < step ? q0 : nq; q < nq; q += step) {
+            int p, s;
+            small_divmod(q, t.SP, rsp, p, s);
             const float *gp = gs + (size_t)p * gsz + (s * kRH) * GW + j + goff;
             float g[kRH];
 #pragma unroll
