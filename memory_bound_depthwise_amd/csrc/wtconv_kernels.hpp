@@ -575,13 +575,19 @@ __global__ __launch_bounds__(256) void level_fwd_kernel(LevelArgs a) {
     const int lane = threadIdx.x & (kWave - 1);
     float w[KK];
     {
-        const float sc = a.sl[c * 4 + b] * a.wscale;
+        // every load first, then one wait: not one memory latency per weight
         const float *wb = a.wl + (size_t)(c * 4 + b) * KK;
+        float raw[KK];
 #pragma unroll
         for (int i = 0; i < KK; ++i) {
             const int u = i / K, v = i - u * K;
-            w[i] = uniform(sc * wb[a.rotate ? (K - 1 - u) * K + (K - 1 - v) : i]);
+            raw[i] = wb[a.rotate ? (K - 1 - u) * K + (K - 1 - v) : i];
         }
+        const float sraw = a.sl[c * 4 + b];
+        __builtin_amdgcn_sched_barrier(0);
+        const float sc = sraw * a.wscale;
+#pragma unroll
+        for (int i = 0; i < KK; ++i) w[i] = uniform(sc * raw[i]);
     }
     __syncthreads();
 
@@ -596,9 +602,14 @@ __global__ __launch_bounds__(256) void level_fwd_kernel(LevelArgs a) {
         for (int i = 0; i < kRH; ++i) acc[i] = 0.f;
         conv_strip<K>(band + (size_t)(p * 4 + b) * bandsz + (s * kRH) * HXP + j, HXP, w, acc);
         float *z = zbuf + ((size_t)(b * t.PB + p) * t.TY + s * kRH) * t.TX + j;
+        if (s * kRH + kRH <= t.TY) {  // whole strip: no branch per row
 #pragma unroll
-        for (int i = 0; i < kRH; ++i)
-            if (s * kRH + i < t.TY) z[i * t.TX] = acc[i];
+            for (int i = 0; i < kRH; ++i) z[i * t.TX] = acc[i];
+        } else {
+#pragma unroll
+            for (int i = 0; i < kRH; ++i)
+                if (s * kRH + i < t.TY) z[i * t.TX] = acc[i];
+        }
     }
     __syncthreads();
 
@@ -642,14 +653,18 @@ __global__ __launch_bounds__(256) void synth_kernel(SynthArgs a) {
     pixel_stage<T>(static_cast<const T *>(a.x), smem, t.VW, t.PB, HY, HXW, bp.ty0 - R, ca, n0, a.n, c, a.C, a.H,
                    a.W, a.H, 0, 0);
 
-    float w[KK];
-    const float sc = a.s0[c];
+    // every load first, then one wait: not one memory latency per weight
+    float w[KK], raw[KK];
 #pragma unroll
     for (int i = 0; i < KK; ++i) {
         const int u = i / K, v = i - u * K;
-        w[i] = uniform(sc * a.w0[(size_t)c * KK + (a.rotate ? (K - 1 - u) * K + (K - 1 - v) : i)]);
+        raw[i] = a.w0[(size_t)c * KK + (a.rotate ? (K - 1 - u) * K + (K - 1 - v) : i)];
     }
-    const float bias = a.b0 ? uniform(sc * a.b0[c]) : 0.f;
+    const float sc = a.s0[c], braw = a.b0 ? a.b0[c] : 0.f;
+    __builtin_amdgcn_sched_barrier(0);
+#pragma unroll
+    for (int i = 0; i < KK; ++i) w[i] = uniform(sc * raw[i]);
+    const float bias = uniform(sc * braw);
     __syncthreads();
 
     T *y = static_cast<T *>(a.y);
