@@ -41,7 +41,9 @@ WORKLOADS = {
     "tiny": ["tiny"],
     # plain depthwise convolutions (levels = 0) on the stage1 shape, for comparison
     "dw5": ["dw5"], "dw7": ["dw7"],
+    "stage1_f16": ["stage1_f16"],
 }
+DTYPE_CODE = {"f32": 0, "bf16": 1, "f16": 2}  # the library's activation dtype codes
 
 
 def describe(cases):
@@ -65,7 +67,7 @@ class Layer:
     def __init__(self, case, rotate, torch, wt):
         from synthetic import normal
         self.case = case
-        dt = torch.bfloat16 if case.dtype == "bf16" else torch.float32
+        dt = {"bf16": torch.bfloat16, "f16": torch.float16}.get(case.dtype, torch.float32)
         dev = "cuda"
         self.sets = []
         for r in range(rotate):
@@ -85,7 +87,7 @@ class Layer:
                       "ds0": torch.empty((C,), dtype=f32, device=dev),
                       "dwl": torch.empty((L, C, 4, k, k), dtype=f32, device=dev),
                       "dsl": torch.empty((L, C, 4), dtype=f32, device=dev)}
-        desc = wt.make_desc(case.n, case.c, case.h, case.w, k, L, wt.BF16 if case.dtype == "bf16" else wt.F32)
+        desc = wt.make_desc(case.n, case.c, case.h, case.w, k, L, DTYPE_CODE[case.dtype])
         nbytes = max(wt.wtconv_workspace_size(desc, op) for op in range(3))
         self.ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
 
@@ -211,11 +213,11 @@ def main():
     cases = [allc[name] for name in WORKLOADS[args.workload]]
     print(f"# bench: {args.workload}: {describe(cases)}", file=sys.stderr, flush=True)
     layers = [Layer(c, args.rotate, torch, wt) for c in cases]
-    es = lambda c: 2 if c.dtype == "bf16" else 4
+    es = lambda c: 4 if c.dtype == "f32" else 2
 
     def case_launches(c):
         # the kernels the library enqueues for this shape, priced by the byte model
-        desc = wt.make_desc(c.n, c.c, c.h, c.w, c.k, c.levels, wt.BF16 if c.dtype == "bf16" else wt.F32)
+        desc = wt.make_desc(c.n, c.c, c.h, c.w, c.k, c.levels, DTYPE_CODE[c.dtype])
         plan = {p: [e["name"] for e in wt.wtconv_plan_launches(desc, op)]
                 for p, op in (("forward", wt.OP_FORWARD), ("backward_input", wt.OP_BACKWARD_INPUT),
                               ("backward_weight", wt.OP_BACKWARD_WEIGHT))}

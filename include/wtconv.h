@@ -28,8 +28,9 @@
  * parameter gradients are float32, contiguous:
  *   w0 [C][k][k], b0 [C] (may be NULL = no bias), s0 [C],
  *   wl [levels][C][4][k][k], sl [levels][C][4]  (may be NULL when levels == 0).
- * bf16 values are stored as IEEE bfloat16 bit patterns (uint16); arithmetic is
- * float32 throughout; bf16 results are rounded to nearest, ties to even.
+ * bf16 values are stored as bfloat16 bit patterns and f16 values as IEEE
+ * binary16 bit patterns (16 bits each); arithmetic is float32 throughout; 16-bit
+ * results are rounded to nearest, ties to even.
  * Intermediates in the workspace use the activation dtype.
  *
  * Streams: each call enqueues its kernels on `stream` (a hipStream_t; NULL is
@@ -53,7 +54,7 @@ extern "C" {
 #define WTCONV_MAX_LEVELS 8
 
 /* Activation storage type. */
-enum wtconv_dtype { WTCONV_F32 = 0, WTCONV_BF16 = 1 };
+enum wtconv_dtype { WTCONV_F32 = 0, WTCONV_BF16 = 1, WTCONV_F16 = 2 };
 
 /* Operation selector for wtconv_workspace_size. */
 enum wtconv_op { WTCONV_OP_FORWARD = 0, WTCONV_OP_BACKWARD_INPUT = 1, WTCONV_OP_BACKWARD_WEIGHT = 2 };

@@ -68,8 +68,18 @@ hipEvent_t pooled_event() {
     return e;
 }
 
+// Name of an activation dtype as the launch records and plans spell it.
+const char *dtype_name(int dtype) {
+    return dtype == WTCONV_BF16 ? "bf16" : (dtype == WTCONV_F16 ? "f16" : "f32");
+}
+// Activation dtype of a storage type.
+template <typename T>
+constexpr int dtype_of() {
+    return std::is_same<T, uint16_t>::value ? WTCONV_BF16 : (std::is_same<T, wtc_f16>::value ? WTCONV_F16 : WTCONV_F32);
+}
+
 template <typename Kern, typename Args>
-int launch(const char *family, int K, int is_bf16, int level, Kern kern, dim3 grid, dim3 block, size_t shmem,
+int launch(const char *family, int K, int dtype, int level, Kern kern, dim3 grid, dim3 block, size_t shmem,
            hipStream_t stream, const Args &args) {
     if (grid.x == 0 || grid.y == 0) return WTCONV_OK;
     hipEvent_t ev0 = nullptr, ev1 = nullptr;
@@ -89,9 +99,9 @@ int launch(const char *family, int K, int is_bf16, int level, Kern kern, dim3 gr
         (void)hipEventRecord(ev1, stream);
         char name[64];
         if (level > 0)
-            snprintf(name, sizeof(name), "%s<%d,%s>#%d", family, K, is_bf16 ? "bf16" : "f32", level);
+            snprintf(name, sizeof(name), "%s<%d,%s>#%d", family, K, dtype_name(dtype), level);
         else
-            snprintf(name, sizeof(name), "%s<%d,%s>", family, K, is_bf16 ? "bf16" : "f32");
+            snprintf(name, sizeof(name), "%s<%d,%s>", family, K, dtype_name(dtype));
         std::lock_guard<std::mutex> lock(g_prof_mu);
         g_prof.push_back({name, ev0, ev1});
     }
@@ -202,12 +212,12 @@ bool tiling_fits(Kind kind, int K, const Tiling &t) { return lds_bytes(kind, K, 
 
 // Widest vector (elements) for staging rows of length W at pointer p.
 int vec_width(int W, int dtype, const void *p) {
-    int vw = dtype == WTCONV_BF16 ? 8 : 4;
-    const size_t es = dtype == WTCONV_BF16 ? 2 : 4;
+    int vw = dtype != WTCONV_F32 ? 8 : 4;
+    const size_t es = dtype != WTCONV_F32 ? 2 : 4;
     while (vw > 1 && (W % vw != 0 || ((uintptr_t)p % (vw * es)) != 0)) vw /= 2;
     return vw;
 }
-int max_vec_width(int dtype) { return dtype == WTCONV_BF16 ? 8 : 4; }
+int max_vec_width(int dtype) { return dtype != WTCONV_F32 ? 8 : 4; }
 
 long long grid_of(const Tiling &t, int C) { return (long long)t.tiles * C * t.nblk; }
 
@@ -268,9 +278,9 @@ int fused_tail_floats(const FusedArgs &a) {
 }
 
 int fused_prefetch_capacity(int dtype, int VE) {
-    // prefetch words per thread (8 for bf16, 16 for f32), 256 threads
-    const int es = dtype == WTCONV_BF16 ? 2 : 4;
-    const int words = dtype == WTCONV_BF16 ? 8 : 16;
+    // prefetch words per thread (8 for 16-bit activations, 16 for f32), 256 threads
+    const int es = dtype != WTCONV_F32 ? 2 : 4;
+    const int words = dtype != WTCONV_F32 ? 8 : 16;
     const int words_per_vec = (VE * es + 3) / 4;
     return (words / words_per_vec) * kThreads * VE;
 }
@@ -752,7 +762,7 @@ bool plan_fused_dw(const wtconv_desc &d, FusedDwArgs &a) {
     // reads for discarded rows run up to 8 (+4) rows past the last region
     const int tail = (kRH + 4) * std::max(b.wl_[L], b.ys[L - 1]) + 64;
     b.blocks = b.hl[1] * b.wl_[1];
-    const int capacity = d.dtype == WTCONV_BF16 ? 2048 : 1024;  // level-1 blocks prefetched per pass
+    const int capacity = d.dtype != WTCONV_F32 ? 2048 : 1024;  // level-1 blocks prefetched per pass
     long long per_pair[kMaxLevels];
     for (int l = 0; l < L; ++l) per_pair[l] = (long long)b.sp[l + 1] * b.wl_[l + 1];
     const int KK = K * K;
@@ -831,7 +841,7 @@ struct DwPlan {
     size_t bytes;
 };
 
-size_t elem_size(int dtype) { return dtype == WTCONV_BF16 ? 2 : 4; }
+size_t elem_size(int dtype) { return dtype != WTCONV_F32 ? 2 : 4; }
 
 FwdPlan build_forward_plan(const wtconv_desc &d) {
     FwdPlan p{};
@@ -943,7 +953,7 @@ int check_desc(const wtconv_desc *d) {
     if (d->n < 0 || d->c < 0 || d->h < 0 || d->w < 0 || d->reserved != 0) return WTCONV_ERR_SHAPE;
     if (d->k != 3 && d->k != 5 && d->k != 7) return WTCONV_ERR_KERNEL;
     if (d->levels < 0 || d->levels > kMaxLevels) return WTCONV_ERR_LEVELS;
-    if (d->dtype != WTCONV_F32 && d->dtype != WTCONV_BF16) return WTCONV_ERR_DTYPE;
+    if (d->dtype != WTCONV_F32 && d->dtype != WTCONV_BF16 && d->dtype != WTCONV_F16) return WTCONV_ERR_DTYPE;
     // every workgroup count must fit a 1-D grid; plane offsets are 64-bit
     const long long planes = (long long)d->n * d->c;
     if ((long long)d->h * d->w > (1LL << 31) - 1) return WTCONV_ERR_SHAPE;
@@ -973,7 +983,7 @@ bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
 template <int K, typename T>
 int run_fused_forward(const wtconv_desc &d, FusedArgs a, const void *x, const float *w0, const float *b0,
                       const float *s0, const float *wl, const float *sl, void *y, hipStream_t st, int rotate) {
-    const int bf = std::is_same<T, uint16_t>::value;
+    const int bf = dtype_of<T>();  // dtype code, for the launch records
     a.x = x;
     a.y = y;
     a.w0 = w0;
@@ -1014,12 +1024,15 @@ const void *plane_kernel(const PlaneCfg &cfg) {
 }
 
 const void *plane_kernel_for(const wtconv_desc &d, const PlaneCfg &cfg) {
-    const bool bf = d.dtype == WTCONV_BF16;
+#define WTC_PK(KV) \
+    (d.dtype == WTCONV_BF16 ? plane_kernel<KV, uint16_t>(cfg) \
+                            : d.dtype == WTCONV_F16 ? plane_kernel<KV, wtc_f16>(cfg) : plane_kernel<KV, float>(cfg))
     switch (d.k) {
-        case 3: return bf ? plane_kernel<3, uint16_t>(cfg) : plane_kernel<3, float>(cfg);
-        case 5: return bf ? plane_kernel<5, uint16_t>(cfg) : plane_kernel<5, float>(cfg);
-        default: return bf ? plane_kernel<7, uint16_t>(cfg) : plane_kernel<7, float>(cfg);
+        case 3: return WTC_PK(3);
+        case 5: return WTC_PK(5);
+        default: return WTC_PK(7);
     }
+#undef WTC_PK
 }
 
 // Persistent grid: as many workgroups as can be resident at once on the current
@@ -1070,7 +1083,7 @@ int run_plane_forward(const wtconv_desc &d, PlaneArgs a, const PlaneCfg &cfg, co
     a.pair_store = d.w % 2 == 0 && aligned(y, 2 * sizeof(T)) ? 1 : 0;
     const dim3 grid((unsigned)plane_grid(d, a, cfg));
     const size_t shm = (size_t)a.lds_floats * sizeof(float);
-    const int bf = std::is_same<T, uint16_t>::value;
+    const int bf = dtype_of<T>();  // dtype code, for the launch records
 #define WTC_PLANE_LAUNCH(CW_, RH_) \
     launch("plane_fwd", K, bf, 0, plane_fwd_kernel<K, T, CW_, RH_>, grid, dim3(kFwdThreads), shm, st, a)
     switch (cfg.CW * 16 + cfg.RH) {
@@ -1096,7 +1109,7 @@ int run_plane_dwb(const wtconv_desc &d, PlaneDwbArgs a, const PlaneCfg &cfg, con
     a.vec = d.w % (2 * cfg.CW) == 0 && aligned(x, 2 * cfg.CW * sizeof(T)) && aligned(dy, 2 * cfg.CW * sizeof(T)) ? 1 : 0;
     const dim3 grid((unsigned)((long long)d.c * a.k));
     const size_t shm = (size_t)a.lds_floats * sizeof(float);
-    const int bf = std::is_same<T, uint16_t>::value;
+    const int bf = dtype_of<T>();  // dtype code, for the launch records
 #define WTC_DWB_LAUNCH(CW_, RH_) \
     launch("plane_dwb", K, bf, 0, plane_dwb_kernel<K, T, CW_, RH_>, grid, dim3(kDwbThreads), shm, st, a)
     switch (cfg.CW * 16 + cfg.RH) {
@@ -1125,7 +1138,7 @@ int run_plane_dwl(const wtconv_desc &d, const DwPlan &p, const void *x, const vo
     a.vec = d.w % (2 * cfg.CW) == 0 && aligned(x, 2 * cfg.CW * sizeof(T)) && aligned(dy, 2 * cfg.CW * sizeof(T)) ? 1 : 0;
     const dim3 grid((unsigned)((long long)d.c * a.k));
     const size_t shm = (size_t)a.lds_floats * sizeof(float);
-    const int bf = std::is_same<T, uint16_t>::value;
+    const int bf = dtype_of<T>();  // dtype code, for the launch records
 #define WTC_DWL_LAUNCH(CW_, RH_) \
     launch("plane_dwl", K, bf, 0, plane_dwl_kernel<K, T, CW_, RH_>, grid, dim3(kDwlThreads), shm, st, a)
     switch (cfg.CW) {
@@ -1149,7 +1162,7 @@ int run_forward(const wtconv_desc &d, const void *x, const float *w0, const floa
             return run_fused_forward<K, T>(d, fa, x, w0, b0, s0, wl, sl, y, st, rotate);
     }
     const FwdPlan p = plan_forward(d);
-    const int bf = std::is_same<T, uint16_t>::value;
+    const int bf = dtype_of<T>();  // dtype code, for the launch records
 
     const int L = d.levels;
     for (int l = 1; l <= L; ++l) {
@@ -1203,7 +1216,7 @@ int run_backward_weight(const wtconv_desc &d, const void *x, const void *dy, con
                         const float *s0, const float *wl, const float *sl, float *dw0, float *db0, float *ds0,
                         float *dwl, float *dsl, char *ws, hipStream_t st) {
     const DwPlan p = plan_backward_weight(d);
-    const int bf = std::is_same<T, uint16_t>::value;
+    const int bf = dtype_of<T>();  // dtype code, for the launch records
     const int L = d.levels;
     float *partial = reinterpret_cast<float *>(ws + p.part_off);
     if (!empty(d) && p.dwl && L > 0) {
@@ -1300,11 +1313,14 @@ int run_backward_weight(const wtconv_desc &d, const void *x, const void *dy, con
 
 #define WTC_DISPATCH(KVAL, DTYPE, FN, ...)                                   \
     do {                                                                    \
-        const bool bf16_ = (DTYPE) == WTCONV_BF16;                          \
+        const int dt_ = (DTYPE);                                            \
         switch (KVAL) {                                                     \
-            case 3: return bf16_ ? FN<3, uint16_t>(__VA_ARGS__) : FN<3, float>(__VA_ARGS__); \
-            case 5: return bf16_ ? FN<5, uint16_t>(__VA_ARGS__) : FN<5, float>(__VA_ARGS__); \
-            case 7: return bf16_ ? FN<7, uint16_t>(__VA_ARGS__) : FN<7, float>(__VA_ARGS__); \
+            case 3: return dt_ == WTCONV_BF16 ? FN<3, uint16_t>(__VA_ARGS__) \
+                         : dt_ == WTCONV_F16 ? FN<3, wtc_f16>(__VA_ARGS__) : FN<3, float>(__VA_ARGS__); \
+            case 5: return dt_ == WTCONV_BF16 ? FN<5, uint16_t>(__VA_ARGS__) \
+                         : dt_ == WTCONV_F16 ? FN<5, wtc_f16>(__VA_ARGS__) : FN<5, float>(__VA_ARGS__); \
+            case 7: return dt_ == WTCONV_BF16 ? FN<7, uint16_t>(__VA_ARGS__) \
+                         : dt_ == WTCONV_F16 ? FN<7, wtc_f16>(__VA_ARGS__) : FN<7, float>(__VA_ARGS__); \
             default: return WTCONV_ERR_KERNEL;                              \
         }                                                                   \
     } while (0)
@@ -1413,7 +1429,7 @@ int wtconv_plan_launches(const wtconv_desc *desc, int op, wtconv_launch *out, in
     if (op != WTCONV_OP_FORWARD && op != WTCONV_OP_BACKWARD_INPUT && op != WTCONV_OP_BACKWARD_WEIGHT)
         return WTCONV_ERR_OP;
     const wtconv_desc &d = *desc;
-    const char *dt = d.dtype == WTCONV_BF16 ? "bf16" : "f32";
+    const char *dt = dtype_name(d.dtype);
     const size_t es = elem_size(d.dtype);
     std::vector<wtconv_launch> v;
     auto add = [&](const char *fam, int level, long long wg, int thr, size_t lds) {

@@ -141,10 +141,10 @@ struct XPrefetch {
     // Element t of slot k as float32.
     __device__ __forceinline__ static float elem(const uint32_t *raw, int k, int t) {
         const uint32_t *r = raw + k * kWordsPerVec;
-        if constexpr (sizeof(T) == 2) {
-            if constexpr (VE == 1) return __uint_as_float(r[0] << 16);
+        if constexpr (kHalf<T>) {
+            if constexpr (VE == 1) return Act<T>::lo(r[0]);
             const uint32_t wv = r[t >> 1];
-            return __uint_as_float((t & 1) ? (wv & 0xffff0000u) : (wv << 16));
+            return (t & 1) ? Act<T>::hi(wv) : Act<T>::lo(wv);
         } else {
             return __uint_as_float(r[t]);
         }
@@ -346,10 +346,10 @@ __device__ __forceinline__ void fused_fwd_body(const FusedArgs &a) {
                 }
             }
             const int yoff = p * CHW + (s * kRH) * W + j;
-            if constexpr (sizeof(T) == 2) {
+            if constexpr (kHalf<T>) {
 #pragma unroll
                 for (int i = 0; i < kRH; i += 2) {
-                    const uint32_t pk = f32x2_to_bf16x2(acc[i], acc[i + 1]);
+                    const uint32_t pk = Act<T>::pack(acc[i], acc[i + 1]);
                     if (i < rows) reinterpret_cast<uint16_t *>(ybase)[yoff + i * W] = (uint16_t)pk;
                     if (i + 1 < rows) reinterpret_cast<uint16_t *>(ybase)[yoff + (i + 1) * W] = (uint16_t)(pk >> 16);
                 }

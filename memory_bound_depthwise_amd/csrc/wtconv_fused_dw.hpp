@@ -142,9 +142,9 @@ struct BlockPrefetch {
     // pixel t of row rr (0 or 1) of slot k as float32
     __device__ __forceinline__ static float px(const uint32_t *raw, int k, int rr, int t) {
         const uint32_t *r = raw + k * 2 * kRowWords + rr * kRowWords;
-        if constexpr (sizeof(T) == 2) {
+        if constexpr (kHalf<T>) {
             const uint32_t wv = r[t >> 1];
-            return __uint_as_float((t & 1) ? (wv & 0xffff0000u) : (wv << 16));
+            return (t & 1) ? Act<T>::hi(wv) : Act<T>::lo(wv);
         } else {
             return __uint_as_float(r[t]);
         }

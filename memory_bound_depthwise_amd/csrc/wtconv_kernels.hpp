@@ -37,6 +37,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "wtconv.h"
 
 namespace wtc {
@@ -49,21 +51,60 @@ constexpr int kRH = 8;  // rows per lane strip
 // Activation storage
 // ---------------------------------------------------------------------------
 
-__device__ __forceinline__ float bf16_bits_to_f32(uint32_t b) { return __uint_as_float(b << 16); }
-
-__device__ __forceinline__ float act_load(const float *p, size_t i) { return p[i]; }
-__device__ __forceinline__ float act_load(const uint16_t *p, size_t i) { return bf16_bits_to_f32(p[i]); }
-
-// float32 -> bfloat16, round to nearest, ties to even (gfx950 v_cvt_pk_bf16_f32).
-__device__ __forceinline__ uint32_t f32_to_bf16(float v) {
-    return __builtin_bit_cast(uint16_t, (__bf16)v);
-}
+// Three storage types: float (float32), uint16_t (bfloat16 bits) and wtc_f16
+// (IEEE half bits).  Every kernel loads the raw words of its activations and
+// converts them with Act<T>; the 16-bit types share all load and store code, and
+// differ only in the conversions below.  All arithmetic is float32.
+struct wtc_f16 {
+    uint16_t bits;
+};
 typedef float wtc_float2 __attribute__((ext_vector_type(2)));
 typedef __bf16 wtc_bf16x2 __attribute__((ext_vector_type(2)));
-// Two values packed low, high in one conversion.
-__device__ __forceinline__ uint32_t f32x2_to_bf16x2(float a, float b) {
-    const wtc_float2 v = {a, b};
-    return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, wtc_bf16x2));
+typedef _Float16 wtc_halfx2 __attribute__((ext_vector_type(2)));
+
+template <typename T>
+struct Act;
+template <>
+struct Act<float> {
+    static constexpr bool half = false;
+};
+template <>
+struct Act<uint16_t> {  // bfloat16: the high half of a float32
+    static constexpr bool half = true;
+    __device__ __forceinline__ static float lo(uint32_t w) { return __uint_as_float(w << 16); }
+    __device__ __forceinline__ static float hi(uint32_t w) { return __uint_as_float(w & 0xffff0000u); }
+    // round to nearest, ties to even (gfx950 v_cvt_pk_bf16_f32), low half = a
+    __device__ __forceinline__ static uint32_t pack(float a, float b) {
+        const wtc_float2 v = {a, b};
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, wtc_bf16x2));
+    }
+    __device__ __forceinline__ static uint16_t one(float v) { return __builtin_bit_cast(uint16_t, (__bf16)v); }
+};
+template <>
+struct Act<wtc_f16> {  // IEEE binary16
+    static constexpr bool half = true;
+    __device__ __forceinline__ static float lo(uint32_t w) {
+        return (float)__builtin_bit_cast(_Float16, (uint16_t)(w & 0xffffu));
+    }
+    __device__ __forceinline__ static float hi(uint32_t w) {
+        return (float)__builtin_bit_cast(_Float16, (uint16_t)(w >> 16));
+    }
+    // round to nearest, ties to even, low half = a
+    __device__ __forceinline__ static uint32_t pack(float a, float b) {
+        const wtc_float2 v = {a, b};
+        return __builtin_bit_cast(uint32_t, __builtin_convertvector(v, wtc_halfx2));
+    }
+    __device__ __forceinline__ static uint16_t one(float v) { return __builtin_bit_cast(uint16_t, (_Float16)v); }
+};
+template <typename T>
+constexpr bool kHalf = Act<T>::half;
+template <typename T>
+using if_half = typename std::enable_if<Act<T>::half, int>::type;
+
+__device__ __forceinline__ float act_load(const float *p, size_t i) { return p[i]; }
+template <typename T, if_half<T> = 0>
+__device__ __forceinline__ float act_load(const T *p, size_t i) {
+    return Act<T>::lo(reinterpret_cast<const uint16_t *>(p)[i]);
 }
 
 // Exact quotient n / d for n, d < 2^16, with m = ceil(2^32 / d) computed on the host
@@ -71,24 +112,29 @@ __device__ __forceinline__ uint32_t f32x2_to_bf16x2(float a, float b) {
 __device__ __forceinline__ int fdiv(int n, uint32_t m) { return m ? (int)__umulhi((uint32_t)n, m) : n; }
 
 __device__ __forceinline__ void act_store(float *p, size_t i, float v) { p[i] = v; }
-__device__ __forceinline__ void act_store(uint16_t *p, size_t i, float v) { p[i] = (uint16_t)f32_to_bf16(v); }
+template <typename T, if_half<T> = 0>
+__device__ __forceinline__ void act_store(T *p, size_t i, float v) {
+    reinterpret_cast<uint16_t *>(p)[i] = Act<T>::one(v);
+}
 
 // Two adjacent elements (element index i even, so the pair is aligned).
 __device__ __forceinline__ void act_store2(float *p, size_t i, float a, float b) {
     *reinterpret_cast<float2 *>(p + i) = make_float2(a, b);
 }
-__device__ __forceinline__ void act_store2(uint16_t *p, size_t i, float a, float b) {
-    *reinterpret_cast<uint32_t *>(p + i) = f32x2_to_bf16x2(a, b);
+template <typename T, if_half<T> = 0>
+__device__ __forceinline__ void act_store2(T *p, size_t i, float a, float b) {
+    *reinterpret_cast<uint32_t *>(p + i) = Act<T>::pack(a, b);
 }
 __device__ __forceinline__ void act_load2(const float *p, size_t i, float &a, float &b) {
     const float2 v = *reinterpret_cast<const float2 *>(p + i);
     a = v.x;
     b = v.y;
 }
-__device__ __forceinline__ void act_load2(const uint16_t *p, size_t i, float &a, float &b) {
+template <typename T, if_half<T> = 0>
+__device__ __forceinline__ void act_load2(const T *p, size_t i, float &a, float &b) {
     const uint32_t v = *reinterpret_cast<const uint32_t *>(p + i);
-    a = bf16_bits_to_f32(v & 0xffffu);
-    b = bf16_bits_to_f32(v >> 16);
+    a = Act<T>::lo(v);
+    b = Act<T>::hi(v);
 }
 
 // VW consecutive elements starting at element i (i a multiple of VW, base aligned).
@@ -109,28 +155,29 @@ __device__ __forceinline__ void act_loadv(const float *p, size_t i, float *out) 
         out[3] = v.w;
     }
 }
-template <int VW>
-__device__ __forceinline__ void act_loadv(const uint16_t *p, size_t i, float *out) {
+template <int VW, typename T, if_half<T> = 0>
+__device__ __forceinline__ void act_loadv(const T *p, size_t i, float *out) {
+    const uint16_t *q = reinterpret_cast<const uint16_t *>(p);
     if constexpr (VW == 1) {
-        out[0] = bf16_bits_to_f32(p[i]);
+        out[0] = Act<T>::lo(q[i]);
     } else if constexpr (VW == 2) {
-        const uint32_t v = *reinterpret_cast<const uint32_t *>(p + i);
-        out[0] = bf16_bits_to_f32(v & 0xffffu);
-        out[1] = bf16_bits_to_f32(v >> 16);
+        const uint32_t v = *reinterpret_cast<const uint32_t *>(q + i);
+        out[0] = Act<T>::lo(v);
+        out[1] = Act<T>::hi(v);
     } else if constexpr (VW == 4) {
-        const uint2 v = *reinterpret_cast<const uint2 *>(p + i);
-        out[0] = bf16_bits_to_f32(v.x & 0xffffu);
-        out[1] = bf16_bits_to_f32(v.x >> 16);
-        out[2] = bf16_bits_to_f32(v.y & 0xffffu);
-        out[3] = bf16_bits_to_f32(v.y >> 16);
+        const uint2 v = *reinterpret_cast<const uint2 *>(q + i);
+        out[0] = Act<T>::lo(v.x);
+        out[1] = Act<T>::hi(v.x);
+        out[2] = Act<T>::lo(v.y);
+        out[3] = Act<T>::hi(v.y);
     } else {
-        static_assert(VW == 8, "bf16 vectors are at most 16 bytes");
-        const uint4 v = *reinterpret_cast<const uint4 *>(p + i);
+        static_assert(VW == 8, "16-bit vectors are at most 16 bytes");
+        const uint4 v = *reinterpret_cast<const uint4 *>(q + i);
         const uint32_t w[4] = {v.x, v.y, v.z, v.w};
 #pragma unroll
         for (int k = 0; k < 4; ++k) {
-            out[2 * k] = bf16_bits_to_f32(w[k] & 0xffffu);
-            out[2 * k + 1] = bf16_bits_to_f32(w[k] >> 16);
+            out[2 * k] = Act<T>::lo(w[k]);
+            out[2 * k + 1] = Act<T>::hi(w[k]);
         }
     }
 }
@@ -307,16 +354,18 @@ __device__ __forceinline__ void block_load_raw(const T *src, size_t o0, size_t o
 template <typename T>
 __device__ __forceinline__ void block_unpack(const uint32_t (&w)[4], bool pairs, float &x00, float &x01, float &x10,
                                              float &x11) {
-    if (pairs && sizeof(T) == 2) {
-        x00 = __uint_as_float(w[0] << 16);
-        x01 = __uint_as_float(w[0] & 0xffff0000u);
-        x10 = __uint_as_float(w[1] << 16);
-        x11 = __uint_as_float(w[1] & 0xffff0000u);
-    } else if (sizeof(T) == 2) {
-        x00 = __uint_as_float(w[0] << 16);
-        x01 = __uint_as_float(w[1] << 16);
-        x10 = __uint_as_float(w[2] << 16);
-        x11 = __uint_as_float(w[3] << 16);
+    if constexpr (kHalf<T>) {
+        if (pairs) {
+            x00 = Act<T>::lo(w[0]);
+            x01 = Act<T>::hi(w[0]);
+            x10 = Act<T>::lo(w[1]);
+            x11 = Act<T>::hi(w[1]);
+        } else {
+            x00 = Act<T>::lo(w[0]);
+            x01 = Act<T>::lo(w[1]);
+            x10 = Act<T>::lo(w[2]);
+            x11 = Act<T>::lo(w[3]);
+        }
     } else {
         x00 = __uint_as_float(w[0]);
         x01 = __uint_as_float(w[1]);
@@ -425,9 +474,9 @@ __device__ __forceinline__ void raw_load(const T *p, RawVec<VW, T> &r) {
 }
 template <int VW, typename T>
 __device__ __forceinline__ float raw_elem(const RawVec<VW, T> &r, int e) {
-    if constexpr (sizeof(T) == 2) {
+    if constexpr (kHalf<T>) {
         const uint32_t wv = r.w[e >> 1];
-        return __uint_as_float((e & 1) ? (wv & 0xffff0000u) : (wv << 16));
+        return (e & 1) ? Act<T>::hi(wv) : Act<T>::lo(wv);
     } else {
         return __uint_as_float(r.w[e]);
     }
@@ -693,7 +742,7 @@ __global__ __launch_bounds__(256) void synth_kernel(SynthArgs a) {
 #pragma unroll
                 for (int r = 0; r < (kRH >> l > 0 ? kRH >> l : 1); ++r) {
                     const int row = min((gy0 >> l) + r, ylast >> l);
-                    if constexpr (sizeof(T) == 2)  // widened after the conv: no wait here
+                    if constexpr (kHalf<T>)  // converted after the conv: no wait here
                         qraw[l][r] = reinterpret_cast<const uint16_t *>(ql)[(size_t)row * a.wq[l]];
                     else
                         qraw[l][r] = reinterpret_cast<const uint32_t *>(ql)[(size_t)row * a.wq[l]];
@@ -711,7 +760,12 @@ __global__ __launch_bounds__(256) void synth_kernel(SynthArgs a) {
             float qsum = bias;
 #pragma unroll
             for (int l = 0; l < kMaxLevels; ++l)
-                if (l < a.L) qsum += __uint_as_float(sizeof(T) == 2 ? qraw[l][i >> l] << 16 : qraw[l][i >> l]);
+                if (l < a.L) {
+                    if constexpr (kHalf<T>)
+                        qsum += Act<T>::lo(qraw[l][i >> l]);
+                    else
+                        qsum += __uint_as_float(qraw[l][i >> l]);
+                }
             acc[i] += qsum;
         }
         T *yp = y + pidx * plane + (size_t)gy0 * a.W + gx;

@@ -127,9 +127,9 @@ struct PatchIO {
     }
 
     __device__ __forceinline__ static float elem(const uint32_t *r, int e) {
-        if constexpr (sizeof(T) == 2) {
+        if constexpr (kHalf<T>) {
             const uint32_t wv = r[e >> 1];
-            return __uint_as_float((e & 1) ? (wv & 0xffff0000u) : (wv << 16));
+            return (e & 1) ? Act<T>::hi(wv) : Act<T>::lo(wv);
         } else {
             return __uint_as_float(r[e]);
         }
@@ -526,8 +526,8 @@ __device__ __forceinline__ void plane_fwd_body(const PlaneArgs &args) {
                             if (pr >= H) break;
                             T *dst = yp + pr * W;
                             if (a.pair_store) {
-                                if constexpr (sizeof(T) == 2)
-                                    *reinterpret_cast<uint32_t *>(dst) = f32x2_to_bf16x2(P[ry][0][i], P[ry][1][i]);
+                                if constexpr (kHalf<T>)
+                                    *reinterpret_cast<uint32_t *>(dst) = Act<T>::pack(P[ry][0][i], P[ry][1][i]);
                                 else
                                     *reinterpret_cast<float2 *>(dst) = make_float2(P[ry][0][i], P[ry][1][i]);
                             } else {

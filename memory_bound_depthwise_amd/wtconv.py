@@ -12,7 +12,7 @@ import os
 PKG = os.path.dirname(os.path.abspath(__file__))
 LIB_PATH = os.path.join(PKG, "libwtconv.so")
 
-F32, BF16 = 0, 1
+F32, BF16, F16 = 0, 1, 2
 OP_FORWARD, OP_BACKWARD_INPUT, OP_BACKWARD_WEIGHT = 0, 1, 2
 MAX_LEVELS = 8
 
@@ -116,7 +116,9 @@ def _dtype_code(t) -> int:
         return F32
     if t.dtype == torch.bfloat16:
         return BF16
-    raise WTConvError(f"activation dtype {t.dtype} is not supported (float32 or bfloat16)")
+    if t.dtype == torch.float16:
+        return F16
+    raise WTConvError(f"activation dtype {t.dtype} is not supported (float32, bfloat16 or float16)")
 
 
 def _ptr(t):

@@ -94,7 +94,7 @@ def traffic(workload, fetch_db, write_db, copy_fetch_db, copy_write_db, copy_byt
     allc = baseline_cases()
     for name in bench.WORKLOADS[workload]:
         c = allc[name]
-        desc = wt.make_desc(c.n, c.c, c.h, c.w, c.k, c.levels, wt.BF16 if c.dtype == "bf16" else wt.F32)
+        desc = wt.make_desc(c.n, c.c, c.h, c.w, c.k, c.levels, bench.DTYPE_CODE[c.dtype])
         for op in (wt.OP_FORWARD, wt.OP_BACKWARD_INPUT, wt.OP_BACKWARD_WEIGHT):
             for e in wt.wtconv_plan_launches(desc, op):
                 fam = e["name"].split("<")[0]

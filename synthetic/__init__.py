@@ -90,6 +90,12 @@ def round_to_bf16(a: np.ndarray) -> np.ndarray:
     return bf16_bits_to_f32(to_bf16_bits(a))
 
 
+def round_to_f16(a: np.ndarray) -> np.ndarray:
+    """float32 values that are exactly representable in IEEE half (numpy's
+    conversion rounds to nearest, ties to even)."""
+    return np.asarray(a, dtype=np.float32).astype(np.float16).astype(np.float32)
+
+
 # ---------------------------------------------------------------------------
 # Layer inputs.  A "case" describes one WTConv layer invocation.
 # ---------------------------------------------------------------------------
@@ -98,7 +104,7 @@ class Case:
     """One synthetic layer invocation.
 
     n, c, h, w: activation shape (NCHW); k: odd kernel size; levels: Haar levels;
-    dtype: "f32" or "bf16" (activation storage; parameters are always float32).
+    dtype: "f32", "bf16" or "f16" (activation storage; parameters are always float32).
     x_std / dy_std: std of the activation and upstream-gradient draws;
     w_std: std of every depthwise kernel; b_std: std of the bias (0 -> zero bias);
     s_low/s_high: scale range.
@@ -123,7 +129,9 @@ class Case:
 
     def _act(self, tag, std):
         a = normal(self.seed, f"{self.name}/{tag}", (self.n, self.c, self.h, self.w), std)
-        return round_to_bf16(a) if self.dtype == "bf16" else a
+        if self.dtype == "bf16":
+            return round_to_bf16(a)
+        return round_to_f16(a) if self.dtype == "f16" else a
 
     def x(self) -> np.ndarray:
         """float32 activation values (already representable in the storage dtype)."""
@@ -155,6 +163,7 @@ def baseline_cases() -> dict:
     stage1/stage2/stage3: WTConvNeXt-T stage shapes at batch 64 (bf16).
     hires_L1..L5: x[8,128,256,256] bf16 for L = 1..5.
     stack_1..stack_4: the four WTConvNeXt-T stage layers at batch 128 (bf16).
+    stage1_f16: the stage1 shape with IEEE half activations.
     dw5, dw7: plain depthwise convolutions (levels = 0) on the stage1 shape, k = 5
     (the wavelet path's own kernel size) and k = 7 (the kernel a WTConv layer
     replaces in ConvNeXt): the two comparison protocols of the paper's §5.
@@ -169,6 +178,7 @@ def baseline_cases() -> dict:
         cases[f"hires_L{L}"] = Case(8, 128, 256, 256, 5, L, "bf16", 0, name=f"hires_L{L}")
     for i, (c, hw, L) in enumerate([(96, 56, 3), (192, 28, 2), (384, 14, 1), (768, 7, 1)], 1):
         cases[f"stack_{i}"] = Case(128, c, hw, hw, 5, L, "bf16", 0, name=f"stack_{i}")
+    cases["stage1_f16"] = Case(64, 96, 56, 56, 5, 3, "f16", 0, name="stage1_f16")
     for k in (5, 7):
         cases[f"dw{k}"] = Case(64, 96, 56, 56, k, 0, "bf16", 0, name=f"dw{k}")
     return cases

@@ -56,7 +56,7 @@ def _ws(desc, op):
 @pytest.mark.parametrize("fields,code", [
     ((1, 8, 16, 16, 4, 2, 0), E_KERNEL), ((1, 8, 16, 16, 9, 2, 0), E_KERNEL),
     ((1, 8, 16, 16, 5, -1, 0), E_LEVELS), ((1, 8, 16, 16, 5, 9, 0), E_LEVELS),
-    ((1, 8, 16, 16, 5, 2, 2), E_DTYPE), ((-1, 8, 16, 16, 5, 2, 0), E_SHAPE),
+    ((1, 8, 16, 16, 5, 2, 3), E_DTYPE), ((-1, 8, 16, 16, 5, 2, 0), E_SHAPE),
     ((1, 8, -16, 16, 5, 2, 0), E_SHAPE), ((1, 8, 65536, 65536, 5, 2, 0), E_SHAPE),
 ])
 def test_desc_validation(fields, code):
@@ -77,7 +77,7 @@ def test_workspace_query_errors():
 def test_workspace_sizes():
     # forward: Q(l) (4 values per coefficient block) for every level + carriers for l < L
     n, c, h, w, L = 2, 3, 37, 45, 3
-    for dt, es in [(wt.F32, 4), (wt.BF16, 2)]:
+    for dt, es in [(wt.F32, 4), (wt.BF16, 2), (wt.F16, 2)]:
         d = wt.make_desc(n, c, h, w, 5, L, dt)
         hs, ws = [h], [w]
         for _ in range(L):

@@ -11,7 +11,7 @@ import numpy as np
 import pytest
 
 from synthetic import Case, baseline_cases
-from wtc_harness import TOL, compare, gpu_all, oracle_all, rel_err, to_np, torch_act, torch_params
+from wtc_harness import TOL, compare, gpu_all, oracle_all, rel_err, tol, to_np, torch_act, torch_params
 
 pytestmark = pytest.mark.gpu
 
@@ -44,7 +44,7 @@ SMALL = [
 ]
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16"])
+@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
 @pytest.mark.parametrize("shape", SMALL, ids=[f"{s[0]}x{s[1]}x{s[2]}x{s[3]}-k{s[4]}-L{s[5]}" for s in SMALL])
 def test_small_shapes_elementwise(shape, dtype):
     _cuda()
@@ -97,12 +97,12 @@ def _sampled_check(case, planes, channels):
         gs = dy[nn:nn + 1, cc:cc + 1].astype(np.float64)
         y = oracle.forward(xs, qc, L, k)
         e = rel_err(got["y"][nn:nn + 1, cc:cc + 1], y)
-        assert e <= TOL[(case.dtype, "fwd")], (case, "y", nn, cc, e)
+        assert e <= tol(case, "fwd"), (case, "y", nn, cc, e)
         qr = dict(qc)
         qr["b0"] = None
         dx = oracle.backward(xs, gs, qr, L, k)["dx"]
         e = rel_err(got["dx"][nn:nn + 1, cc:cc + 1], dx)
-        assert e <= TOL[(case.dtype, "grad")], (case, "dx", nn, cc, e)
+        assert e <= tol(case, "grad"), (case, "dx", nn, cc, e)
     # weight gradients on sampled channels (all n)
     qc = {"w0": q["w0"][channels], "b0": q["b0"][channels], "s0": q["s0"][channels],
           "wl": q["wl"][:, channels], "sl": q["sl"][:, channels]}
@@ -112,13 +112,13 @@ def _sampled_check(case, planes, channels):
         if L == 0 and key in ("dwl", "dsl"):
             continue
         e = rel_err(got[key][sl], gw[key])
-        assert e <= TOL[(case.dtype, "grad")], (case, key, e)
+        assert e <= tol(case, "grad"), (case, key, e)
     _log(f"  ok {case}")
     del torch
 
 
 FULL = ["stage1", "stage2", "stage3", "hires_L1", "hires_L2", "hires_L3", "hires_L4", "hires_L5",
-        "stack_1", "stack_2", "stack_3", "stack_4", "dw5", "dw7"]
+        "stack_1", "stack_2", "stack_3", "stack_4", "dw5", "dw7", "stage1_f16"]
 
 
 @pytest.mark.parametrize("name", FULL)
@@ -196,4 +196,26 @@ def test_bf16_output_rounding_is_rne():
     y = wtconv_forward(torch_act(x, "bf16"), tp["w0"], tp["b0"], tp["s0"], None, None, 0)
     got = y.view(torch.int16).cpu().numpy().view(np.uint16)
     want = to_bf16_bits((x.astype(np.float32) * s).astype(np.float32))
+    np.testing.assert_array_equal(got, want)
+
+
+def test_f16_output_rounding_is_rne():
+    """IEEE half activations, levels = 0, identity kernel, zero bias: with scale
+    1 + 3 * 2^-12 (x*s is exact in float32 and lies 0.75 to 1.5 half-ulps above x,
+    ties included) the half result must be the round-to-nearest-even of x*s
+    (numpy's float32 -> float16 conversion rounds the same way)."""
+    torch = _cuda()
+    from memory_bound_depthwise_amd import wtconv_forward
+    C, k = 2, 5
+    x = Case(2, C, 16, 16, k, 0, "f16", seed=9, name="rne16").x()
+    w0 = np.zeros((C, k, k), np.float32)
+    w0[:, 2, 2] = 1.0
+    s = np.float32(1.0 + 3.0 * 2.0 ** -12)
+    p = {"w0": w0, "b0": np.zeros(C, np.float32), "s0": np.full(C, s, np.float32),
+         "wl": np.zeros((1, C, 4, k, k), np.float32), "sl": np.zeros((1, C, 4), np.float32)}
+    tp = torch_params(p)
+    y = wtconv_forward(torch_act(x, "f16"), tp["w0"], tp["b0"], tp["s0"], None, None, 0)
+    got = y.view(torch.int16).cpu().numpy().view(np.uint16)
+    want = (x.astype(np.float32) * s).astype(np.float32).astype(np.float16).view(np.uint16)
+    assert not np.array_equal(want, x.astype(np.float16).view(np.uint16))  # the scale does round
     np.testing.assert_array_equal(got, want)
