@@ -148,8 +148,8 @@ size_t lds_bytes(Kind kind, int K, const Tiling &t) {
 // the whole workgroup otherwise.
 int lane_group(Kind kind) { return (kind == Kind::LevelFwd || kind == Kind::DwLevel) ? kWave : kThreads; }
 
-// Tile an Ho x Wo output grid.  Tiles are at most 64 columns wide (a full row for
-// the small planes of the WTConvNeXt stages) and as tall as needed for about 4
+// Tile an Ho x Wo output grid.  Tiles are at most one lane group wide (a full row
+// for the small planes of the WTConvNeXt stages) and as tall as needed for about 4
 // strips per lane group; then as many planes are stacked per pass as give the
 // best lane occupancy within the LDS budget, keeping at least ~2 workgroups per
 // compute unit when the problem allows.
@@ -162,7 +162,10 @@ Tiling pick_tiling(Kind kind, int K, int n, int C, int Ho, int Wo, int VW) {
         return t;
     }
     const int U = lane_group(kind);
-    t.tiles_x = cdiv(Wo, 64);
+    // A tile is at most as wide as its lane group (a wavefront per band for the
+    // level kernels, the workgroup otherwise): wide tiles keep the halo columns and
+    // the partly used cache lines at the row ends a small share of what is staged.
+    t.tiles_x = cdiv(Wo, U);
     t.TX = cdiv(Wo, t.tiles_x);
     int sp_max = std::max(1, cdiv(4 * U, t.TX));
     for (;;) {

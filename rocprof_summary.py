@@ -95,22 +95,30 @@ def traffic(workload, fetch_db, write_db, copy_fetch_db, copy_write_db, copy_byt
     for name in bench.WORKLOADS[workload]:
         c = allc[name]
         desc = wt.make_desc(c.n, c.c, c.h, c.w, c.k, c.levels, bench.DTYPE_CODE[c.dtype])
-        for op in (wt.OP_FORWARD, wt.OP_BACKWARD_INPUT, wt.OP_BACKWARD_WEIGHT):
-            for e in wt.wtconv_plan_launches(desc, op):
-                fam = e["name"].split("<")[0]
-                match = rows.get((fam, e["workgroups"] * e["threads"]))
-                if not match:
-                    # A persistent kernel's grid follows the device's occupancy, which
-                    # the host-side plan does not know: take the family's rows when
-                    # they all share one grid.
-                    grids = {g for (f, g) in rows if f == fam}
-                    if len(grids) == 1:
-                        match = rows[(fam, grids.pop())]
-                if not match or match[0]["write_bytes"] is None:
-                    continue
-                r = match[0]
-                out[e["name"]] = {"fetch_bytes": r["fetch_bytes"], "write_bytes": r["write_bytes"],
-                                  "bytes": r["fetch_bytes"] + r["write_bytes"]}
+        plan = [e for op in (wt.OP_FORWARD, wt.OP_BACKWARD_INPUT, wt.OP_BACKWARD_WEIGHT)
+                for e in wt.wtconv_plan_launches(desc, op)]
+        # launches of one family with one grid size (two levels' kernels) share a
+        # counter row, which averages them: such launches get no record
+        names_at = collections.defaultdict(set)
+        for e in plan:
+            names_at[(e["name"].split("<")[0], e["workgroups"] * e["threads"])].add(e["name"])
+        for e in plan:
+            fam = e["name"].split("<")[0]
+            if len(names_at[(fam, e["workgroups"] * e["threads"])]) > 1:
+                continue
+            match = rows.get((fam, e["workgroups"] * e["threads"]))
+            if not match:
+                # A persistent kernel's grid follows the device's occupancy, which
+                # the host-side plan does not know: take the family's rows when
+                # they all share one grid.
+                grids = {g for (f, g) in rows if f == fam}
+                if len(grids) == 1:
+                    match = rows[(fam, grids.pop())]
+            if not match or match[0]["write_bytes"] is None:
+                continue
+            r = match[0]
+            out[e["name"]] = {"fetch_bytes": r["fetch_bytes"], "write_bytes": r["write_bytes"],
+                              "bytes": r["fetch_bytes"] + r["write_bytes"]}
     return {"workload": workload, "source_digest": bench.source_digest(),
             "fetch_scale": rec["fetch_scale"], "write_scale": rec["write_scale"], "kernels": out}
 
