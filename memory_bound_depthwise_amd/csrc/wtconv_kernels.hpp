@@ -502,46 +502,52 @@ __device__ __forceinline__ void lds_store(float *d, const float *v) {
 // mask_hi, outside those columns;
 // converted to float32 in LDS with row stride `width`.  c0 and width are multiples
 // of VW and W is a multiple of VW, so each vector is wholly inside or outside; dst
-// is aligned to VW floats.  Thread t stages vector column t % (width / VW).
+// is aligned to VW floats.  Thread t stages vector column t % (width / VW) (of each
+// chunk of at most blockDim.x columns).
 template <int VW, typename T>
 __device__ __forceinline__ void pixel_stage_v(const T *__restrict__ src, float *dst, int PB, int rows, int width,
                                               int r0, int c0, int n0, int n_end, int c, int C, int H, int W,
                                               int row_hi, int mask_lo, int mask_hi) {
-    const int vpr = width / VW;
-    const int step = blockDim.x / vpr, vc = threadIdx.x % vpr, rs = threadIdx.x / vpr;
-    if (rs >= step) return;
+    const int vpr = width / VW, nthr = blockDim.x;
     const size_t plane = (size_t)H * W;
-    const int gc = c0 + vc * VW, gcc = min(max(gc, 0), W - VW);
-    bool keep[VW];
+    // vector columns in chunks of at most one per thread (one chunk unless a row
+    // holds more vectors than the workgroup has threads)
+    for (int vc0 = 0; vc0 < vpr; vc0 += nthr) {
+        const int ncols = min(vpr - vc0, nthr);
+        const int step = nthr / ncols, vc = vc0 + (int)threadIdx.x % ncols, rs = (int)threadIdx.x / ncols;
+        if (rs >= step) continue;
+        const int gc = c0 + vc * VW, gcc = min(max(gc, 0), W - VW);
+        bool keep[VW];
 #pragma unroll
-    for (int e = 0; e < VW; ++e) {
-        const int col = gc + e;
-        keep[e] = gc >= 0 && gc < W && !(mask_lo < mask_hi && (col < mask_lo || col >= mask_hi));
-    }
-    for (int p = 0; p < PB; ++p) {
-        const int nn = n0 + p;
-        const bool plane_in = nn < n_end;
-        const T *sp = src + ((size_t)min(nn, n_end - 1) * C + c) * plane + gcc;
-        float *dp = dst + (size_t)p * rows * width + vc * VW;
-        for (int base = rs; base < rows; base += kStageBatch * step) {
-            RawVec<VW, T> raw[kStageBatch];
+        for (int e = 0; e < VW; ++e) {
+            const int col = gc + e;
+            keep[e] = gc >= 0 && gc < W && !(mask_lo < mask_hi && (col < mask_lo || col >= mask_hi));
+        }
+        for (int p = 0; p < PB; ++p) {
+            const int nn = n0 + p;
+            const bool plane_in = nn < n_end;
+            const T *sp = src + ((size_t)min(nn, n_end - 1) * C + c) * plane + gcc;
+            float *dp = dst + (size_t)p * rows * width + vc * VW;
+            for (int base = rs; base < rows; base += kStageBatch * step) {
+                RawVec<VW, T> raw[kStageBatch];
 #pragma unroll
-            for (int k = 0; k < kStageBatch; ++k) {
-                const int gi = min(max(r0 + min(base + k * step, rows - 1), 0), H - 1);
-                raw_load<VW, T>(sp + (size_t)gi * W, raw[k]);
-            }
-            __builtin_amdgcn_sched_barrier(0);  // keep the batch's loads ahead of every use
-            // rows past the end repeat the last row (the same values to the same
-            // place): no branch, so the loads are not sunk into one
+                for (int k = 0; k < kStageBatch; ++k) {
+                    const int gi = min(max(r0 + min(base + k * step, rows - 1), 0), H - 1);
+                    raw_load<VW, T>(sp + (size_t)gi * W, raw[k]);
+                }
+                __builtin_amdgcn_sched_barrier(0);  // keep the batch's loads ahead of every use
+                // rows past the end repeat the last row (the same values to the same
+                // place): no branch, so the loads are not sunk into one
 #pragma unroll
-            for (int k = 0; k < kStageBatch; ++k) {
-                const int ri = min(base + k * step, rows - 1);
-                const int gi = r0 + ri;
-                const bool rin = plane_in && gi >= 0 && gi < row_hi;
-                float v[VW];
+                for (int k = 0; k < kStageBatch; ++k) {
+                    const int ri = min(base + k * step, rows - 1);
+                    const int gi = r0 + ri;
+                    const bool rin = plane_in && gi >= 0 && gi < row_hi;
+                    float v[VW];
 #pragma unroll
-                for (int e = 0; e < VW; ++e) v[e] = rin && keep[e] ? raw_elem<VW, T>(raw[k], e) : 0.f;
-                lds_store<VW>(dp + (size_t)ri * width, v);
+                    for (int e = 0; e < VW; ++e) v[e] = rin && keep[e] ? raw_elem<VW, T>(raw[k], e) : 0.f;
+                    lds_store<VW>(dp + (size_t)ri * width, v);
+                }
             }
         }
     }

@@ -41,6 +41,7 @@ SMALL = [
     (5, 6, 9, 14, 5, 4),      # several planes stacked per workgroup
     (1, 1, 256, 9, 5, 5),     # tall and narrow
     (1, 1, 9, 200, 5, 5),     # short and wide
+    (1, 2, 9, 255, 7, 2),     # odd width: scalar loads, a staged row wider than a workgroup
 ]
 
 
