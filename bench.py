@@ -104,6 +104,23 @@ class Layer:
                                   workspace=self.ws)
 
 
+def memory_report(layers, torch):
+    """Device memory of the step: the allocator's peak over the run (every rotating
+    buffer set included) and the footprint of one training step of these layers with
+    this library: one set of x, dy, y, dx per layer, the parameters, their gradients
+    and the workspace (the forward keeps nothing for the backward)."""
+    def nb(t):
+        return 0 if t is None else t.numel() * t.element_size()
+    step = 0
+    for layer in layers:
+        step += sum(nb(t) for t in layer.sets[0])
+        step += sum(nb(t) for t in layer.p.values()) + sum(nb(t) for t in layer.grads.values()) + nb(layer.ws)
+    return {"peak_allocated_bytes": int(torch.cuda.max_memory_allocated()),
+            "step_footprint_bytes": int(step),
+            "workspace_bytes": int(sum(nb(layer.ws) for layer in layers)),
+            "rotate_buffer_sets": len(layers[0].sets)}
+
+
 def run_step(layers, i, wt):
     for layer in layers:
         layer.forward(i, wt)
@@ -232,6 +249,7 @@ def main():
     per_level_bytes = sum(b for c in cases
                           for _, _, b, _ in traffic.launches(c.n, c.c, c.h, c.w, c.k, c.levels, es(c)))
 
+    torch.cuda.reset_peak_memory_stats()
     for i in range(args.warmup):
         run_step(layers, i, wt)
     torch.cuda.synchronize()
@@ -326,6 +344,7 @@ def main():
         "source_digest": digest,
         "kernels": kernels,
         "roofline": roof,
+        "memory": memory_report(layers, torch),
     }
     if not args.no_cpu_baseline:
         def sample_bytes(c):

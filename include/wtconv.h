@@ -89,13 +89,16 @@ typedef struct wtconv_desc {
  * *bytes; 0 is possible).  Returns a status code. */
 int wtconv_workspace_size(const wtconv_desc *desc, int op, size_t *bytes);
 
-/* Forward pass, §2.1 Algorithm 1 evaluated as in §4 of the paper: per level,
- * one kernel recomputes the Haar butterfly (Eq. 5) from an LDS-staged tile of
- * the carrier and filters the four bands with scale-folded weights (Eq. 8);
- * one final kernel adds the base convolution, the bias and the bit-indexed
- * closed-form synthesis of all levels (Proposition 2, Eq. 7) and stores y.
- *   x [n][c][h][w] in, y [n][c][h][w] out (must not alias x).
- * L + 1 kernel launches. */
+/* Forward pass, §2.1 Algorithm 1 evaluated as in §4 of the paper.  Planes up to
+ * 64 x 64 with L >= 1: one launch of a kernel that keeps a plane and its whole
+ * Haar pyramid in LDS (bands recomputed with the butterfly of Eq. 5, filtered
+ * with scale-folded weights, Eq. 8, synthesised in closed form, Proposition 2 /
+ * Eq. 7, plus the base convolution and bias); no workspace.  Larger planes: per
+ * level, one kernel recomputes the butterfly from an LDS-staged tile of the
+ * carrier and filters the four bands; one final kernel adds the base
+ * convolution, the bias and the bit-indexed synthesis of all levels and stores
+ * y (L + 1 launches, coefficients and carriers in the workspace).
+ *   x [n][c][h][w] in, y [n][c][h][w] out (must not alias x). */
 int wtconv_forward(const wtconv_desc *desc, const void *x, const float *w0, const float *b0,
                    const float *s0, const float *wl, const float *sl, void *y, void *workspace,
                    size_t workspace_bytes, void *stream);
@@ -105,7 +108,7 @@ int wtconv_forward(const wtconv_desc *desc, const void *x, const float *w0, cons
  * the adjoint is the forward pipeline run on dy with every k x k kernel turned
  * by 180 degrees and no bias (scales unchanged).
  *   dy [n][c][h][w] in, dx [n][c][h][w] out (must not alias dy).
- * L + 1 kernel launches. */
+ * The same kernels and workspace as the forward pass. */
 int wtconv_backward_input(const wtconv_desc *desc, const void *dy, const float *w0, const float *s0,
                           const float *wl, const float *sl, void *dx, void *workspace,
                           size_t workspace_bytes, void *stream);
@@ -115,9 +118,10 @@ int wtconv_backward_input(const wtconv_desc *desc, const void *dy, const float *
  *   dW = s * dW~,  db = s0 * db~,  ds = <dW~, W> (+ db~ * b on the base path).
  * Outputs are overwritten (not accumulated), float32:
  *   dw0 [C][k][k], db0 [C] (may be NULL), ds0 [C], dwl [L][C][4][k][k], dsl [L][C][4].
- * Reductions are two-stage with a fixed order (wavefront DPP, then LDS, then a
- * fixed-order sum over workgroup partials), so results are bitwise repeatable
- * for a given shape.  L + 2 kernel launches. */
+ * Reductions are two-stage with a fixed order (lanes, then a fixed-order sum
+ * over workgroup partials kept in the workspace), so results are bitwise
+ * repeatable for a given shape.  Planes up to 64 x 64: three launches (levels,
+ * base, finalize); larger planes: L + 2 (one per level, base, finalize). */
 int wtconv_backward_weight(const wtconv_desc *desc, const void *x, const void *dy, const float *w0,
                            const float *b0, const float *s0, const float *wl, const float *sl,
                            float *dw0, float *db0, float *ds0, float *dwl, float *dsl,

@@ -951,6 +951,11 @@ std::shared_ptr<const PlanSet> plans_for(const wtconv_desc &d) {
 FwdPlan plan_forward(const wtconv_desc &d) { return plans_for(d)->fp; }
 DwPlan plan_backward_weight(const wtconv_desc &d) { return plans_for(d)->dp; }
 
+// Workspace of the forward-shaped passes: none when the plane-resident kernel runs
+// (a choice made from the descriptor alone), the per-level coefficients and
+// carriers otherwise.
+size_t forward_workspace_bytes(const wtconv_desc &d) { return plans_for(d)->plane ? 0 : plan_forward(d).bytes; }
+
 int check_desc(const wtconv_desc *d) {
     if (!d) return WTCONV_ERR_NULL;
     if (d->n < 0 || d->c < 0 || d->h < 0 || d->w < 0 || d->reserved != 0) return WTCONV_ERR_SHAPE;
@@ -1340,8 +1345,8 @@ int fwd_common(const wtconv_desc *desc, const void *in, const float *w0, const f
     if (!aligned(in, es) || !aligned(out, es) || !aligned(w0, 4) || !aligned(s0, 4) || (b0 && !aligned(b0, 4)) ||
         (wl && !aligned(wl, 4)) || (sl && !aligned(sl, 4)))
         return WTCONV_ERR_ALIGN;
-    const FwdPlan p = plan_forward(d);
-    if (p.bytes > 0 && (!workspace || workspace_bytes < p.bytes)) return WTCONV_ERR_WORKSPACE;
+    const size_t need = forward_workspace_bytes(d);
+    if (need > 0 && (!workspace || workspace_bytes < need)) return WTCONV_ERR_WORKSPACE;
     if (workspace && !aligned(workspace, 16)) return WTCONV_ERR_ALIGN;
     hipStream_t st = static_cast<hipStream_t>(stream);
     WTC_DISPATCH(d.k, d.dtype, run_forward, d, in, w0, b0, s0, wl, sl, out, static_cast<char *>(workspace), st,
@@ -1383,7 +1388,7 @@ int wtconv_workspace_size(const wtconv_desc *desc, int op, size_t *bytes) {
     if (op == WTCONV_OP_BACKWARD_WEIGHT) {
         *bytes = plan_backward_weight(*desc).bytes;
     } else {
-        *bytes = empty(*desc) ? 0 : plan_forward(*desc).bytes;
+        *bytes = empty(*desc) ? 0 : forward_workspace_bytes(*desc);
     }
     return WTCONV_OK;
 }

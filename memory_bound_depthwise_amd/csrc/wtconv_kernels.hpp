@@ -672,20 +672,24 @@ __global__ __launch_bounds__(256) void level_fwd_kernel(LevelArgs a) {
     T *q = static_cast<T *>(a.qout);
     const int Wq = 2 * a.Wo;
     const size_t q_plane = (size_t)4 * a.Ho * a.Wo, zb = (size_t)t.PB * t.TY * t.TX;
+    // thread: column threadIdx.x % TX of every plane, rows threadIdx.x / TX, + cstep, ...;
+    // the plane's base address is formed once, the row steps are 32-bit increments
     const int per_tile = t.TY * t.TX;
-    const int cstep = blockDim.x / t.TX, cj = threadIdx.x % t.TX, r0 = threadIdx.x / t.TX, nr = t.PB * t.TY;
-    const float rty = 1.f / (float)t.TY;
-    for (int qr = r0 < cstep ? r0 : nr; qr < nr; qr += cstep) {
-        int p, r;
-        small_divmod(qr, t.TY, rty, p, r);
-        const int j = cj, rem = r * t.TX + j;
-        const int nn = n0 + p, gi = bp.ty0 + r, gj = bp.tx0 + j;
-        if (nn >= a.n || gi >= a.Ho || gj >= a.Wo) continue;
-        const float *z = zbuf + (size_t)p * per_tile + rem;
-        const float LL = z[0], LH = z[zb], HL = z[2 * zb], HH = z[3 * zb];
-        T *qp = q + ((size_t)nn * a.C + c) * q_plane + (size_t)(2 * gi) * Wq + 2 * gj;
-        act_store2(qp, 0, (LL + LH) + (HL + HH), (LL + LH) - (HL + HH));
-        act_store2(qp, Wq, (LL - LH) + (HL - HH), (LL - LH) - (HL - HH));
+    const int cstep = blockDim.x / t.TX, cj = threadIdx.x % t.TX, r0 = threadIdx.x / t.TX;
+    const int gj = bp.tx0 + cj;
+    const int rows = min(t.TY, a.Ho - bp.ty0);  // rows of the tile inside the grid
+    if (r0 < cstep && gj < a.Wo) {
+        for (int p = 0; p < t.PB && n0 + p < a.n; ++p) {
+            T *qp = q + ((size_t)(n0 + p) * a.C + c) * q_plane + (size_t)(2 * bp.ty0) * Wq + 2 * gj;
+            const float *z = zbuf + (size_t)p * per_tile + cj;
+            for (int r = r0; r < rows; r += cstep) {
+                const float *zr = z + r * t.TX;
+                const float LL = zr[0], LH = zr[zb], HL = zr[2 * zb], HH = zr[3 * zb];
+                T *qr = qp + r * (2 * Wq);
+                act_store2(qr, 0, (LL + LH) + (HL + HH), (LL + LH) - (HL + HH));
+                act_store2(qr, Wq, (LL - LH) + (HL - HH), (LL - LH) - (HL - HH));
+            }
+        }
     }
 }
 

@@ -75,8 +75,14 @@ def test_workspace_query_errors():
 
 
 def test_workspace_sizes():
-    # forward: Q(l) (4 values per coefficient block) for every level + carriers for l < L
-    n, c, h, w, L = 2, 3, 37, 45, 3
+    # planes up to 64 x 64 stay in LDS: the forward-shaped passes need no workspace
+    for dt in (wt.F32, wt.BF16, wt.F16):
+        d = wt.make_desc(2, 3, 37, 45, 5, 3, dt)
+        assert wt.wtconv_workspace_size(d, wt.OP_FORWARD) == 0
+        assert wt.wtconv_workspace_size(d, wt.OP_BACKWARD_INPUT) == 0
+    # larger planes, per-level path: Q(l) (4 values per coefficient block) for every
+    # level + carriers for l < L
+    n, c, h, w, L = 2, 3, 137, 45, 3
     for dt, es in [(wt.F32, 4), (wt.BF16, 2), (wt.F16, 2)]:
         d = wt.make_desc(n, c, h, w, 5, L, dt)
         hs, ws = [h], [w]
@@ -129,8 +135,10 @@ def test_forward_argument_errors():
     assert f(d, x=P_ODD) == E_ALIGN
     assert f(d, y=P_ODD) == E_ALIGN
     assert f(d, w0=P_ODD) == E_ALIGN
-    assert f(d, ws=P, wsb=10) == E_WS
-    assert f(d, ws=None, wsb=1 << 30) == E_WS
+    # planes up to 64 x 64 need no workspace; a larger plane's too-small one is refused
+    big = wt.make_desc(2, 3, 130, 70, 5, 2, 0)
+    assert f(big, ws=P, wsb=10) == E_WS
+    assert f(big, ws=None, wsb=1 << 30) == E_WS
     bad = wt.make_desc(2, 3, 16, 16, 6, 2, 0)
     assert f(bad) == E_KERNEL
     # empty tensors: nothing to do, success without touching any pointer
@@ -140,7 +148,7 @@ def test_forward_argument_errors():
                                                      kw.get("dx", P), kw.get("ws", P), kw.get("wsb", 0), None)
     assert g(d, dy=None) == E_NULL
     assert g(d, dx=P_ODD) == E_ALIGN
-    assert g(d, wsb=1) == E_WS
+    assert g(big, wsb=1) == E_WS
 
 
 @needs_no_gpu
