@@ -944,8 +944,18 @@ __global__ __launch_bounds__(128) void dw_finalize_kernel(FinalizeArgs a) {
     const int G = a.G[region];
     const float *part = a.partial + a.off[region] + (size_t)c * G * slots;
     for (int i = tid; i < slots; i += blockDim.x) {
+        // the same sequential order of additions; loads eight at a time so that
+        // they are in flight together
         float s = 0.f;
-        for (int g = 0; g < G; ++g) s += part[(size_t)g * slots + i];
+        int g = 0;
+        for (; g + 8 <= G; g += 8) {
+            float v[8];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) v[k] = part[(size_t)(g + k) * slots + i];
+#pragma unroll
+            for (int k = 0; k < 8; ++k) s += v[k];
+        }
+        for (; g < G; ++g) s += part[(size_t)g * slots + i];
         sum[i] = s;
     }
     __syncthreads();
