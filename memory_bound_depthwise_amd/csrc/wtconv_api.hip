@@ -136,7 +136,7 @@ size_t lds_bytes(Kind kind, int K, const Tiling &t) {
     const size_t PB = t.PB, HY = (size_t)t.SP * kRH + K - 1, HXP = t.TX + K - 1, GY = (size_t)t.SP * kRH;
     const size_t HXW = stage_width(t.TX, R, t.VW), GW = stage_width(t.TX, 0, t.VW);
     switch (kind) {
-        case Kind::LevelFwd: return (PB * 4 * HY * HXP + 4 * PB * t.TY * t.TX) * sizeof(float);
+        case Kind::LevelFwd: return (PB * 4 * HY * HXP + 4 * KK) * sizeof(float);  // float4 cells, weight table
         case Kind::Synth: return (PB * HY * HXW) * sizeof(float);
         case Kind::DwLevel: return (PB * 4 * HY * HXP + PB * 4 * GY * t.TX + 4 * KK) * sizeof(float);
         case Kind::DwBase: return (PB * HY * HXW + PB * GY * GW + (kThreads / kWave) * (KK + 1)) * sizeof(float);

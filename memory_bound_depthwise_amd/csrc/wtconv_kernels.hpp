@@ -393,7 +393,9 @@ __device__ __forceinline__ void small_divmod(int q, int d, float rd, int &quo, i
 // Threads walk a staged grid with a fixed column each: thread t takes column
 // t % cols and rows t / cols, t / cols + step, ... (step = threads / cols; cols is
 // at most the thread count), so nothing is divided per element.
-template <typename T>
+// kCells: the four bands of a block go to one float4 cell, bands + 4 (p bandsz +
+// ci stride + cj); otherwise to four arrays of bandsz floats each.
+template <typename T, bool kCells = false>
 __device__ __forceinline__ void haar_stage(const T *__restrict__ in, T *__restrict__ carrier, float *bands,
                                            int bandsz, int stride, int PB, int rows, int cols, int r0, int c0,
                                            int n0, int n_end, int c, int C, int Hi, int Wi, int Ho, int Wo,
@@ -408,7 +410,7 @@ __device__ __forceinline__ void haar_stage(const T *__restrict__ in, T *__restri
         const int nn = n0 + p;
         const bool plane_in = nn < n_end && col_in;
         const T *src = in + ((size_t)min(nn, n_end - 1) * C + c) * in_plane + 2 * gjc;
-        float *dst0 = bands + (size_t)p * 4 * bandsz + cj;
+        float *dst0 = bands + (size_t)p * 4 * bandsz + (kCells ? 4 * cj : cj);
         for (int base = rs; base < rows; base += kStageBatch * step) {
             uint32_t raw[kStageBatch][4];
 #pragma unroll
@@ -434,11 +436,15 @@ __device__ __forceinline__ void haar_stage(const T *__restrict__ in, T *__restri
                 x10 = inside && r1 ? x10 : 0.f;
                 x11 = inside && r1 && c1 ? x11 : 0.f;
                 const float s0 = x00 + x01, s1 = x10 + x11, d0 = x00 - x01, d1 = x10 - x11;
-                float *dst = dst0 + ci * stride;
-                dst[0] = s0 + s1;           // 2 LL
-                dst[bandsz] = s0 - s1;      // 2 LH
-                dst[2 * bandsz] = d0 + d1;  // 2 HL
-                dst[3 * bandsz] = d0 - d1;  // 2 HH
+                if constexpr (kCells) {
+                    *reinterpret_cast<float4 *>(dst0 + 4 * ci * stride) = make_float4(s0 + s1, s0 - s1, d0 + d1, d0 - d1);
+                } else {
+                    float *dst = dst0 + ci * stride;
+                    dst[0] = s0 + s1;           // 2 LL
+                    dst[bandsz] = s0 - s1;      // 2 LH
+                    dst[2 * bandsz] = d0 + d1;  // 2 HL
+                    dst[3 * bandsz] = d0 - d1;  // 2 HH
+                }
                 if (carry_col && inside && gi >= cr0 && gi < cr1 && base + k * step < rows)
                     act_store(carrier, ((size_t)nn * C + c) * out_plane + (size_t)gi * Wo + gj, 0.5f * (s0 + s1));
             }
@@ -606,8 +612,12 @@ __device__ __forceinline__ void corr_strip(const float *src, int stride, const f
 
 // ---------------------------------------------------------------------------
 // Level kernel: Haar analysis + 4-band depthwise conv (+ carrier), §4.1 / Fig. 1b.
-// Output grid: the level's coefficient grid (Ho x Wo).  Wavefront b filters band b;
-// a combine pass writes the four sign patterns of each block.  256 threads.
+// Output grid: the level's coefficient grid (Ho x Wo).  The staged tile holds one
+// float4 cell of the four unscaled bands per coefficient block; a lane filters all
+// four bands of one column x kRH rows (weights of the four bands as float4 from an
+// LDS table: s(l,b) 2^-(l+1) W(l,b), Eq. 8 with the analysis 1/2 and the synthesis
+// weight 2^-l folded in) and stores the four sign patterns of each block (Eq.
+// 12/13) as a 2 x 2 block of Q(l).  256 threads.
 // ---------------------------------------------------------------------------
 
 template <int K, typename T>
@@ -617,78 +627,74 @@ __global__ __launch_bounds__(256) void level_fwd_kernel(LevelArgs a) {
     const Tiling &t = a.t;
     const BlockPos bp = block_pos(t, a.C);
     const int c = bp.c;
-    const int HY = t.SP * kRH + K - 1, HXP = t.TX + K - 1, bandsz = HY * HXP;
-    float *band = smem;                              // [PB][4][HY][HXP]
-    float *zbuf = smem + (size_t)t.PB * 4 * bandsz;  // [4][PB][TY][TX]
+    const int HY = t.SP * kRH + K - 1, HXP = t.TX + K - 1, cells = HY * HXP;
+    float4 *band = reinterpret_cast<float4 *>(smem);  // [PB][HY][HXP] cells
+    float4 *wtab = band + (size_t)t.PB * cells;         // [v][u] float4 over the bands
     const int n0 = bp.nb * t.PB;
+    const int tid = threadIdx.x;
 
-    haar_stage<T>(static_cast<const T *>(a.in), static_cast<T *>(a.cout), band, bandsz, HXP, t.PB, HY, HXP,
-                  bp.ty0 - R, bp.tx0 - R, n0, a.n, c, a.C, a.Hi, a.Wi, a.Ho, a.Wo, a.Ho, bp.ty0, bp.ty0 + t.TY,
-                  bp.tx0, bp.tx0 + t.TX, a.pairs);
-
-    const int b = __builtin_amdgcn_readfirstlane(threadIdx.x / kWave);  // this wavefront's band
-    const int lane = threadIdx.x & (kWave - 1);
-    float w[KK];
-    {
-        // every load first, then one wait: not one memory latency per weight
-        const float *wb = a.wl + (size_t)(c * 4 + b) * KK;
-        float raw[KK];
-#pragma unroll
-        for (int i = 0; i < KK; ++i) {
-            const int u = i / K, v = i - u * K;
-            raw[i] = wb[a.rotate ? (K - 1 - u) * K + (K - 1 - v) : i];
-        }
-        const float sraw = a.sl[c * 4 + b];
-        __builtin_amdgcn_sched_barrier(0);
-        const float sc = sraw * a.wscale;
-#pragma unroll
-        for (int i = 0; i < KK; ++i) w[i] = uniform(sc * raw[i]);
+    // weight table: thread e < 4 KK folds band e / KK, tap e % KK (row u, column v)
+    float wraw = 0.f, sraw = 0.f;
+    if (tid < 4 * KK) {
+        const int b = tid / KK, tap = tid - b * KK, u = tap / K, v = tap - u * K;
+        wraw = a.wl[(size_t)(c * 4 + b) * KK + (a.rotate ? (K - 1 - u) * K + (K - 1 - v) : tap)];
+        sraw = a.sl[c * 4 + b];
+    }
+    haar_stage<T, true>(static_cast<const T *>(a.in), static_cast<T *>(a.cout), smem, cells, HXP, t.PB, HY, HXP,
+                        bp.ty0 - R, bp.tx0 - R, n0, a.n, c, a.C, a.Hi, a.Wi, a.Ho, a.Wo, a.Ho, bp.ty0, bp.ty0 + t.TY,
+                        bp.tx0, bp.tx0 + t.TX, a.pairs);
+    if (tid < 4 * KK) {
+        const int b = tid / KK, tap = tid - b * KK, u = tap / K, v = tap - u * K;
+        reinterpret_cast<float *>(wtab)[(v * K + u) * 4 + b] = sraw * a.wscale * wraw;
     }
     __syncthreads();
 
-    // lane: column lane % TX, strips (plane, strip) = lane / TX, + kWave / TX, ...
-    const int wstep = kWave / t.TX, j = lane % t.TX, q0 = lane / t.TX, nq = t.PB * t.SP;
-    const float rsp = 1.f / (float)t.SP;
-    for (int q = q0 < wstep ? q0 : nq; q < nq; q += wstep) {
-        int p, s;
-        small_divmod(q, t.SP, rsp, p, s);
-        float acc[kRH];
-#pragma unroll
-        for (int i = 0; i < kRH; ++i) acc[i] = 0.f;
-        conv_strip<K>(band + (size_t)(p * 4 + b) * bandsz + (s * kRH) * HXP + j, HXP, w, acc);
-        float *z = zbuf + ((size_t)(b * t.PB + p) * t.TY + s * kRH) * t.TX + j;
-        if (s * kRH + kRH <= t.TY) {  // whole strip: no branch per row
-#pragma unroll
-            for (int i = 0; i < kRH; ++i) z[i * t.TX] = acc[i];
-        } else {
-#pragma unroll
-            for (int i = 0; i < kRH; ++i)
-                if (s * kRH + i < t.TY) z[i * t.TX] = acc[i];
-        }
-    }
-    __syncthreads();
-
-    // Combine: q[ry][rx] = LL + (-1)^ry LH + (-1)^rx HL + (-1)^(ry+rx) HH (Eq. 12/13).
+    // thread: column threadIdx.x % TX, strips (plane, strip) = threadIdx.x / TX, + step, ...
     T *q = static_cast<T *>(a.qout);
     const int Wq = 2 * a.Wo;
-    const size_t q_plane = (size_t)4 * a.Ho * a.Wo, zb = (size_t)t.PB * t.TY * t.TX;
-    // thread: column threadIdx.x % TX of every plane, rows threadIdx.x / TX, + cstep, ...;
-    // the plane's base address is formed once, the row steps are 32-bit increments
-    const int per_tile = t.TY * t.TX;
-    const int cstep = blockDim.x / t.TX, cj = threadIdx.x % t.TX, r0 = threadIdx.x / t.TX;
-    const int gj = bp.tx0 + cj;
-    const int rows = min(t.TY, a.Ho - bp.ty0);  // rows of the tile inside the grid
-    if (r0 < cstep && gj < a.Wo) {
-        for (int p = 0; p < t.PB && n0 + p < a.n; ++p) {
-            T *qp = q + ((size_t)(n0 + p) * a.C + c) * q_plane + (size_t)(2 * bp.ty0) * Wq + 2 * gj;
-            const float *z = zbuf + (size_t)p * per_tile + cj;
-            for (int r = r0; r < rows; r += cstep) {
-                const float *zr = z + r * t.TX;
-                const float LL = zr[0], LH = zr[zb], HL = zr[2 * zb], HH = zr[3 * zb];
-                T *qr = qp + r * (2 * Wq);
-                act_store2(qr, 0, (LL + LH) + (HL + HH), (LL + LH) - (HL + HH));
-                act_store2(qr, Wq, (LL - LH) + (HL - HH), (LL - LH) - (HL - HH));
-            }
+    const size_t q_plane = (size_t)4 * a.Ho * a.Wo;
+    const int step = blockDim.x / t.TX, j = tid % t.TX, q0 = tid / t.TX, nq = t.PB * t.SP;
+    const float rsp = 1.f / (float)t.SP;
+    const int gj = bp.tx0 + j;
+    for (int qi = q0 < step ? q0 : nq; qi < nq; qi += step) {
+        int p, s;
+        small_divmod(qi, t.SP, rsp, p, s);
+        float z[4][kRH];
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+#pragma unroll
+            for (int i = 0; i < kRH; ++i) z[b][i] = 0.f;
+        const float4 *win = band + (size_t)p * cells + (s * kRH) * HXP + j;
+#pragma unroll 1
+        for (int v = 0; v < K; ++v) {  // rolled: unrolled, every column's reads go out up front
+            float4 wb[K];
+#pragma unroll
+            for (int u = 0; u < K; ++u) wb[u] = wtab[v * K + u];
+            float4 cl[kRH + K - 1];
+#pragma unroll
+            for (int tt = 0; tt < kRH + K - 1; ++tt) cl[tt] = win[tt * HXP + v];
+#pragma unroll
+            for (int u = 0; u < K; ++u)
+#pragma unroll
+                for (int i = 0; i < kRH; ++i) {
+                    z[0][i] = fmaf(wb[u].x, cl[i + u].x, z[0][i]);
+                    z[1][i] = fmaf(wb[u].y, cl[i + u].y, z[1][i]);
+                    z[2][i] = fmaf(wb[u].z, cl[i + u].z, z[2][i]);
+                    z[3][i] = fmaf(wb[u].w, cl[i + u].w, z[3][i]);
+                }
+        }
+        // q[ry][rx] = LL + (-1)^ry LH + (-1)^rx HL + (-1)^(ry+rx) HH (Eq. 12/13)
+        const int nn = n0 + p, gi0 = bp.ty0 + s * kRH;
+        const int rows = min(kRH, min(a.Ho, bp.ty0 + t.TY) - gi0);
+        if (nn >= a.n || gj >= a.Wo || rows <= 0) continue;
+        T *qp = q + ((size_t)nn * a.C + c) * q_plane + (size_t)(2 * gi0) * Wq + 2 * gj;
+#pragma unroll
+        for (int i = 0; i < kRH; ++i) {
+            if (i >= rows) break;
+            const float a0 = z[0][i] + z[1][i], a1 = z[0][i] - z[1][i];
+            const float b0 = z[2][i] + z[3][i], b1 = z[2][i] - z[3][i];
+            act_store2(qp + 2 * i * Wq, 0, a0 + b0, a0 - b0);
+            act_store2(qp + (2 * i + 1) * Wq, 0, a1 + b1, a1 - b1);
         }
     }
 }
