@@ -771,17 +771,23 @@ __global__ __launch_bounds__(256) void synth_kernel(SynthArgs a) {
         for (int i = 0; i < kRH; ++i) acc[i] = 0.f;
         conv_strip<K>(smem + (size_t)p * plsz + (s * kRH) * HXW + j + off, HXW, w, acc);
         __builtin_amdgcn_sched_barrier(0);
+        auto qval = [&](uint32_t w) {
+            if constexpr (kHalf<T>)
+                return Act<T>::lo(w);
+            else
+                return __uint_as_float(w);
+        };
+        // levels 4 and deeper read one row for the whole strip: summed once
+        float deep = bias;
+#pragma unroll
+        for (int l = 3; l < kMaxLevels; ++l)
+            if (l < a.L) deep += qval(qraw[l][0]);
 #pragma unroll
         for (int i = 0; i < kRH; ++i) {
-            float qsum = bias;
+            float qsum = deep;
 #pragma unroll
-            for (int l = 0; l < kMaxLevels; ++l)
-                if (l < a.L) {
-                    if constexpr (kHalf<T>)
-                        qsum += Act<T>::lo(qraw[l][i >> l]);
-                    else
-                        qsum += __uint_as_float(qraw[l][i >> l]);
-                }
+            for (int l = 0; l < 3; ++l)
+                if (l < a.L) qsum += qval(qraw[l][i >> l]);
             acc[i] += qsum;
         }
         T *yp = y + pidx * plane + (size_t)gy0 * a.W + gx;
