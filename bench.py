@@ -52,11 +52,17 @@ def describe(cases):
 
 
 def source_digest():
+    """Digest of the kernel sources' code (comments and blank lines left out), so that
+    a measurement record is recognised as stale exactly when the code changed."""
+    import re
     h = hashlib.sha256()
     csrc = os.path.join(ROOT, "memory_bound_depthwise_amd", "csrc")
     for name in sorted(os.listdir(csrc)):
-        with open(os.path.join(csrc, name), "rb") as f:
-            h.update(name.encode() + f.read())
+        with open(os.path.join(csrc, name), encoding="utf-8") as f:
+            text = f.read()
+        text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+        code = [re.sub(r"//.*$", "", line).rstrip() for line in text.splitlines()]
+        h.update(name.encode() + "\n".join(line for line in code if line.strip()).encode())
     return h.hexdigest()[:16]
 
 

@@ -24,13 +24,16 @@
 // Compute layout (all convolution-shaped kernels).  A lane owns one column of the
 // output tile and a strip of RH = 8 consecutive rows; consecutive lanes own
 // consecutive columns.  For each horizontal tap v the lane reads its 8 + K - 1
-// column values from LDS (consecutive lanes read consecutive words: no bank
-// conflicts) and applies the K vertical taps from registers, so one LDS read feeds
-// 8K/(8+K-1) FMAs.  The folded k x k weights of a channel (and band) are the same
-// for a whole wavefront and are moved to scalar registers with readfirstlane: each
-// multiply-accumulate is one v_fmac_f32 with a scalar operand.
+// column values from LDS (consecutive lanes read consecutive words or cells: no
+// bank conflicts) and applies the K vertical taps from registers, so one LDS read
+// feeds 8K/(8+K-1) FMAs.  In the synthesis and base-gradient kernels the folded
+// k x k weights of a channel are the same for the whole workgroup and sit in scalar
+// registers (readfirstlane): each multiply-accumulate is one v_fmac_f32 with a
+// scalar operand.  The level kernel stages one float4 cell of the four bands per
+// coefficient block and reads the four bands' weights as float4 from LDS.
 //
-// All arithmetic is float32; activations are float32 or bfloat16 in memory.
+// All arithmetic is float32; activations are float32, bfloat16 or IEEE half in
+// memory.
 
 #pragma once
 
