@@ -719,7 +719,19 @@ bool plan_dwl(const wtconv_desc &d, PlaneDwlArgs &a, PlaneCfg &cfg) {
     }
     if (!dwl_layout(d, cfg, best_pb, a)) return false;
     a.NG = cdiv(d.n, a.PB);
-    a.k = dw_blocks_per_channel(d, a.NG, a.lds_floats);
+    // Among the workgroup counts per channel that are all resident at once, the one
+    // with the least work on the busiest compute unit: workgroups per CU times image
+    // groups per workgroup (ties: more workgroups).  Measured on the stage shapes,
+    // e.g. x[64,192,28,28] L=2 takes 4 per channel, not the 5 that fit (46 -> 35 us).
+    const int kmax = dw_blocks_per_channel(d, a.NG, a.lds_floats);
+    long long best_load = -1;
+    for (int k = 1; k <= kmax; ++k) {
+        const long long load = cdiv((long long)d.c * k, 256) * cdiv(a.NG, k);
+        if (best_load < 0 || load <= best_load) {
+            best_load = load;
+            a.k = k;
+        }
+    }
     return (long long)d.c * a.k < (1LL << 31);
 }
 
