@@ -209,7 +209,7 @@ def main():
 
     if args.gpus != 1:
         print(f"bench.py runs on one GPU only; --gpus {args.gpus} is not supported "
-              f"(the layer has no multi-GPU path in this build)", file=sys.stderr)
+              f"(the layer runs on one GPU; its data-parallel sharding is a design, not code)", file=sys.stderr)
         sys.exit(2)
 
     import torch
