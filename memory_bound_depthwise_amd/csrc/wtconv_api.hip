@@ -406,10 +406,12 @@ bool plane_layout(const wtconv_desc &d, const PlaneCfg &cfg, int pb, PlaneArgs &
     a.W1 = (d.w + 1) / 2;
     a.S1 = cdiv(a.H1, RH);
     a.Gw = cdiv(a.W1, CW);
+    // the level-1 grid is laid out also for L = 0 (cells of 2 x 2 pixels)
+    const int Lg = std::max(L, 1);
     int hs[kMaxLevels + 1], ws[kMaxLevels + 1];
     hs[0] = d.h;
     ws[0] = d.w;
-    for (int l = 1; l <= L; ++l) {
+    for (int l = 1; l <= Lg; ++l) {
         hs[l] = (hs[l - 1] + 1) / 2;
         ws[l] = (ws[l - 1] + 1) / 2;
     }
@@ -418,9 +420,9 @@ bool plane_layout(const wtconv_desc &d, const PlaneCfg &cfg, int pb, PlaneArgs &
         a.Pw1 = a.W1;
     } else {
         int pwL = 1;
-        for (int l = 1; l <= L; ++l) pwL = std::max(pwL, cdiv(ws[l] + R, 1LL << (L - l)));
-        while (((long long)pwL << (L - 1)) % CW) ++pwL;
-        a.Pw1 = pwL << (L - 1);
+        for (int l = 1; l <= Lg; ++l) pwL = std::max(pwL, cdiv(ws[l] + R, 1LL << (Lg - l)));
+        while (((long long)pwL << (Lg - 1)) % CW) ++pwL;
+        a.Pw1 = pwL << (Lg - 1);
     }
     const int W1s = pb == 1 ? a.W1 : pb * a.Pw1;
     a.commit_items = pb * a.H1 * a.Gw;
@@ -469,7 +471,7 @@ bool plane_layout(const wtconv_desc &d, const PlaneCfg &cfg, int pb, PlaneArgs &
 // Choose the variant (CW, RH), PB and the planes per workgroup; false when the
 // shape is outside the kernel's range.
 bool plan_plane(const wtconv_desc &d, PlaneArgs &a, PlaneCfg &cfg) {
-    if (d.levels < 1 || d.n <= 0 || d.c <= 0 || d.h <= 0 || d.w <= 0) return false;
+    if (d.levels < 0 || d.n <= 0 || d.c <= 0 || d.h <= 0 || d.w <= 0) return false;
     if (d.h > kFusedMaxSide || d.w > kFusedMaxSide) return false;
     const int H1 = (d.h + 1) / 2;
     cfg.RH = H1 % 7 == 0 ? 7 : (H1 <= 4 ? 4 : 8);
@@ -486,7 +488,7 @@ bool plan_plane(const wtconv_desc &d, PlaneArgs &a, PlaneCfg &cfg) {
         // wave-instructions per pass: a final item is ~(4 + 4) RH K^2 FMAs plus
         // ~60 RH others, a deep item 4 kPlaneRHd K^2; commit and Haar ~30 per item;
         // ~400 fixed
-        const double fin = cdiv(t.final_items, kFwdThreads) * 2.0 * (8.0 * cfg.RH * K * K + 60.0 * cfg.RH);
+        const double fin = cdiv(t.final_items, kFwdThreads) * 2.0 * ((d.levels ? 8.0 : 4.0) * cfg.RH * K * K + 60.0 * cfg.RH);
         const int deep_items = d.levels >= 2 ? t.dend[d.levels - 2] : 0;
         const double deep = cdiv(deep_items, kFwdThreads) * 2.0 * (4.0 * kPlaneRHd * K * K + 60.0);
         const double misc = cdiv(t.commit_items, kFwdThreads) * 40.0 + 400.0;
@@ -1026,27 +1028,31 @@ int run_fused_forward(const wtconv_desc &d, FusedArgs a, const void *x, const fl
 }
 
 template <int K, typename T, int CW>
-const void *plane_kernel_rh(int RH) {
+const void *plane_kernel_rh(int RH, bool base) {
+#define WTC_PKR(RH_) base ? reinterpret_cast<const void *>(plane_fwd_kernel<K, T, CW, RH_, true>) \
+                          : reinterpret_cast<const void *>(plane_fwd_kernel<K, T, CW, RH_, false>)
     switch (RH) {
-        case 7: return reinterpret_cast<const void *>(plane_fwd_kernel<K, T, CW, 7>);
-        case 4: return reinterpret_cast<const void *>(plane_fwd_kernel<K, T, CW, 4>);
-        default: return reinterpret_cast<const void *>(plane_fwd_kernel<K, T, CW, 8>);
+        case 7: return WTC_PKR(7);
+        case 4: return WTC_PKR(4);
+        default: return WTC_PKR(8);
     }
+#undef WTC_PKR
 }
 
 template <int K, typename T>
-const void *plane_kernel(const PlaneCfg &cfg) {
+const void *plane_kernel(const PlaneCfg &cfg, bool base) {
     switch (cfg.CW) {
-        case 4: return plane_kernel_rh<K, T, 4>(cfg.RH);
-        case 2: return plane_kernel_rh<K, T, 2>(cfg.RH);
-        default: return plane_kernel_rh<K, T, 1>(cfg.RH);
+        case 4: return plane_kernel_rh<K, T, 4>(cfg.RH, base);
+        case 2: return plane_kernel_rh<K, T, 2>(cfg.RH, base);
+        default: return plane_kernel_rh<K, T, 1>(cfg.RH, base);
     }
 }
 
 const void *plane_kernel_for(const wtconv_desc &d, const PlaneCfg &cfg) {
+    const bool base = d.levels == 0;
 #define WTC_PK(KV) \
-    (d.dtype == WTCONV_BF16 ? plane_kernel<KV, uint16_t>(cfg) \
-                            : d.dtype == WTCONV_F16 ? plane_kernel<KV, wtc_f16>(cfg) : plane_kernel<KV, float>(cfg))
+    (d.dtype == WTCONV_BF16 ? plane_kernel<KV, uint16_t>(cfg, base) \
+                            : d.dtype == WTCONV_F16 ? plane_kernel<KV, wtc_f16>(cfg, base) : plane_kernel<KV, float>(cfg, base))
     switch (d.k) {
         case 3: return WTC_PK(3);
         case 5: return WTC_PK(5);
@@ -1104,8 +1110,10 @@ int run_plane_forward(const wtconv_desc &d, PlaneArgs a, const PlaneCfg &cfg, co
     const dim3 grid((unsigned)plane_grid(d, a, cfg));
     const size_t shm = (size_t)a.lds_floats * sizeof(float);
     const int bf = dtype_of<T>();  // dtype code, for the launch records
-#define WTC_PLANE_LAUNCH(CW_, RH_) \
-    launch("plane_fwd", K, bf, 0, plane_fwd_kernel<K, T, CW_, RH_>, grid, dim3(kFwdThreads), shm, st, a)
+#define WTC_PLANE_LAUNCH(CW_, RH_)                                                                                \
+    (d.levels == 0                                                                                               \
+         ? launch("plane_fwd", K, bf, 0, plane_fwd_kernel<K, T, CW_, RH_, true>, grid, dim3(kFwdThreads), shm, st, a) \
+         : launch("plane_fwd", K, bf, 0, plane_fwd_kernel<K, T, CW_, RH_, false>, grid, dim3(kFwdThreads), shm, st, a))
     switch (cfg.CW * 16 + cfg.RH) {
         case 4 * 16 + 7: return WTC_PLANE_LAUNCH(4, 7);
         case 4 * 16 + 4: return WTC_PLANE_LAUNCH(4, 4);

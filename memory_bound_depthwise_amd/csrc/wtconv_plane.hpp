@@ -162,8 +162,8 @@ __device__ __forceinline__ void mask_patch(PatchRegs<T, CW> &r, int p, int i, in
 }
 
 // One commit item: patch rows 2i, 2i+1 of plane p, level-1 cells [CW m, CW m + CW):
-// the level-1 butterflies of each cell.
-template <int K, typename T, int CW>
+// the level-1 butterflies of each cell (kBase: the four pixels themselves).
+template <int K, typename T, int CW, bool kBase>
 __device__ __forceinline__ void commit_patch(float4 *s4, int sy1, int pw1,
                                              const uint32_t (&raw)[2][PatchIO<T, CW>::kWords], int p, int i, int m) {
     constexpr int R = (K - 1) / 2;
@@ -173,8 +173,12 @@ __device__ __forceinline__ void commit_patch(float4 *s4, int sy1, int pw1,
     for (int q = 0; q < CW; ++q) {
         const float x00 = IO::elem(raw[0], 2 * q), x01 = IO::elem(raw[0], 2 * q + 1);
         const float x10 = IO::elem(raw[1], 2 * q), x11 = IO::elem(raw[1], 2 * q + 1);
-        const float s0 = x00 + x01, s1 = x10 + x11, d0 = x00 - x01, d1 = x10 - x11;
-        d[q] = make_float4(s0 + s1, s0 - s1, d0 + d1, d0 - d1);
+        if constexpr (kBase) {
+            d[q] = make_float4(x00, x01, x10, x11);
+        } else {
+            const float s0 = x00 + x01, s1 = x10 + x11, d0 = x00 - x01, d1 = x10 - x11;
+            d[q] = make_float4(s0 + s1, s0 - s1, d0 + d1, d0 - d1);
+        }
     }
 }
 
@@ -221,7 +225,9 @@ __device__ __forceinline__ void conv_bands(const float4 *win, int stride, const 
     }
 }
 
-template <int K, typename T, int CW, int RH>
+// kBase: levels = 0 (a plain depthwise conv); cells hold the four pixels of each
+// 2 x 2 block as loaded, and there is no level to filter.
+template <int K, typename T, int CW, int RH, bool kBase>
 __device__ __forceinline__ void plane_fwd_body(const PlaneArgs &args) {
     constexpr int R = (K - 1) / 2, KK = K * K;
     constexpr int RC = (R + 1) / 2;  // cells a pixel tap reaches beyond its own cell
@@ -296,7 +302,8 @@ __device__ __forceinline__ void plane_fwd_body(const PlaneArgs &args) {
     };
     auto fold_weight = [&](const auto &A, int e, float f0, float f1) {
         const int lb = e / KK, nl = 4 * A.L;
-        return lb < nl ? ldexpf(f0, -2 * ((lb >> 2) + 1)) * f1 : (lb == nl ? 0.25f * f0 * f1 : (A.b0 ? f0 * f1 : 0.f));
+        return lb < nl ? ldexpf(f0, -2 * ((lb >> 2) + 1)) * f1
+                       : (lb == nl ? (kBase ? 1.f : 0.25f) * f0 * f1 : (A.b0 ? f0 * f1 : 0.f));
     };
     auto weight_slot = [&](const auto &A, int e) {  // LDS float index of entry e
         const int lb = e / KK, tap = e - lb * KK;
@@ -351,7 +358,7 @@ __device__ __forceinline__ void plane_fwd_body(const PlaneArgs &args) {
                 int p, i, m;
                 patch_of(a, g, p, i, m);
                 mask_patch<T, CW>(raw[k], p, i, live, H);
-                commit_patch<K, T, CW>(s4, sy1, pw1, raw[k], p, i, m);
+                commit_patch<K, T, CW, kBase>(s4, sy1, pw1, raw[k], p, i, m);
             }
             const T *xb = static_cast<const T *>(a.x) + ((size_t)n0 * a.C + c) * HW;
             for (int g = tid + SLOTS * NT; g < a.commit_items; g += NT) {  // beyond the registers
@@ -360,7 +367,7 @@ __device__ __forceinline__ void plane_fwd_body(const PlaneArgs &args) {
                 int p, i, m;
                 patch_of(a, g, p, i, m);
                 mask_patch<T, CW>(r, p, i, live, H);
-                commit_patch<K, T, CW>(s4, sy1, pw1, r, p, i, m);
+                commit_patch<K, T, CW, kBase>(s4, sy1, pw1, r, p, i, m);
             }
         }
         __syncthreads();
@@ -438,7 +445,7 @@ __device__ __forceinline__ void plane_fwd_body(const PlaneArgs &args) {
                 const float4 *win = s4 + row0 * sy1 + col + kPlaneCO - R;
                 const float4 *wt1 = s4 + (wt >> 2);
 #pragma unroll 1
-                for (int v = 0; v < K; ++v) {  // rolled: see conv_bands
+                for (int v = 0; v < (kBase ? 0 : K); ++v) {  // rolled: see conv_bands
                     float4 wb[K];
 #pragma unroll
                     for (int u = 0; u < K; ++u) wb[u] = wt1[v * K + u];
@@ -485,8 +492,12 @@ __device__ __forceinline__ void plane_fwd_body(const PlaneArgs &args) {
 #pragma unroll
                     for (int tt = 0; tt < RH + 2 * RC; ++tt) {
                         const float4 c4 = xwin[tt * sy1 + dj];
-                        const float A = c4.x + c4.y, B = c4.x - c4.y, C = c4.z + c4.w, D = c4.z - c4.w;
-                        xq[tt] = make_float4(A + C, A - C, B + D, B - D);
+                        if constexpr (kBase) {
+                            xq[tt] = c4;
+                        } else {
+                            const float A = c4.x + c4.y, B = c4.x - c4.y, C = c4.z + c4.w, D = c4.z - c4.w;
+                            xq[tt] = make_float4(A + C, A - C, B + D, B - D);
+                        }
                     }
 #pragma unroll
                     for (int px = 0; px < 2; ++px)
@@ -543,9 +554,9 @@ __device__ __forceinline__ void plane_fwd_body(const PlaneArgs &args) {
     }
 }
 
-template <int K, typename T, int CW, int RH>
+template <int K, typename T, int CW, int RH, bool kBase>
 __global__ __launch_bounds__(kFwdThreads, 3) void plane_fwd_kernel(PlaneArgs a) {
-    plane_fwd_body<K, T, CW, RH>(a);
+    plane_fwd_body<K, T, CW, RH, kBase>(a);
 }
 
 }  // namespace wtc
