@@ -1,18 +1,29 @@
 """Benchmark of the WTConv layer on one MI355X: forward + input gradient + weight
 gradients per step, on synthetic WTConvNeXt-shaped tensors.
 
-    python bench.py [--steps K] [--warmup W] [--workload stage1] [--gpus 1]
+    python bench.py [--steps K] [--warmup W] [--workload stack] [--gpus 1]
 
-Prints one JSON line.  `value` is the step's algorithmic HBM bytes (the sum over
-its kernel launches, see memory_bound_depthwise_amd/traffic.py) divided by the
-measured step time, in GB/s; `ms_per_step` is the time of one forward + backward.
+Prints one JSON line.  The default workload is the four-layer WTConvNeXt-T-shaped
+stack at batch 128 (forward of layers 1..4, then the backward of layers 4..1).
+
+* `value`: the step's modeled HBM bytes divided by the measured step time, in GB/s
+  (`hbm_frac` = value / 8 TB/s).  The modeled bytes are those of the paper's
+  per-level pass structure (memory_bound_depthwise_amd/traffic.py: model_bytes),
+  the figure the layer's bandwidth target is stated in.  The bytes the kernels
+  this library launches must move (`moved_bytes`; the plane-resident kernels move
+  only their inputs and outputs) are reported next to it.
+* `ms_per_step`: one forward + backward of the workload's layers; the per-step
+  event times also give `ms_per_step_median`, and each pass is timed on its own
+  (`per_pass_ms`).
 Inputs are resident in device memory before the timed region; `--rotate` buffer
 sets (default 3) are cycled so consecutive steps do not find their inputs in the
 256 MB last-level cache.
 
-The `roofline` object covers the kernel family with the largest share of the step
-time, timed with hipEvents the library records around each launch on its launch
-stream; `cpu_baseline` times the float64 CPU oracle on a bounded sample.
+The `roofline` object covers the kernel with the largest share of the step time,
+timed with hipEvents the library records around each launch on its launch stream,
+against the bound that takes longer at peak for its algorithmic bytes and FLOPs:
+HBM at 8 TB/s, or the vector ALU at the FP32 FMA rate the kernels can issue (see
+VALU_PEAK_TFLOPS).  `cpu_baseline` times the float64 CPU oracle on a bounded sample.
 """
 from __future__ import annotations
 
@@ -20,6 +31,7 @@ import argparse
 import hashlib
 import json
 import os
+import statistics
 import sys
 import time
 
@@ -28,10 +40,12 @@ sys.path.insert(0, ROOT)
 
 METRIC = "WTConv layer fwd+bwd ms and achieved HBM GB/s (% of 8 TB/s), 1 GPU"
 HBM_PEAK_GBS = 8000.0
-# MI355X's published FP32 vector peak (256 CUs x 2.4 GHz x 256 FLOP per clock).  The
-# library issues no packed FP32, but a register-only v_fmac_f32 loop already runs
-# above the single-issue figure (78.6), so only the published peak bounds it.
-ALU_PEAK_TFLOPS = 157.3
+# FP32 FMA peak of MI355X for single-issue vector FMAs: 256 CUs x 4 SIMDs x 16 lanes x
+# 2 FLOP x 2.4 GHz = 78.6 TFLOP/s.  The published 157.3 TFLOP/s counts the packed
+# dual-FP32 FMA (two FMAs per lane per instruction), which these kernels do not issue
+# (packed FP32 instruction selection is switched off in the build).
+VALU_PEAK_TFLOPS = 78.6
+PUBLISHED_FP32_TFLOPS = 157.3
 
 WORKLOADS = {
     "stage1": ["stage1"], "stage2": ["stage2"], "stage3": ["stage3"],
@@ -44,6 +58,7 @@ WORKLOADS = {
     "stage1_f16": ["stage1_f16"],
 }
 DTYPE_CODE = {"f32": 0, "bf16": 1, "f16": 2}  # the library's activation dtype codes
+PASSES = ("forward", "backward_input", "backward_weight")
 
 
 def describe(cases):
@@ -102,12 +117,20 @@ class Layer:
         p, L = self.p, self.case.levels
         wt.wtconv_forward(x, p["w0"], p["b0"], p["s0"], p["wl"], p["sl"], L, out=y, workspace=self.ws)
 
-    def backward(self, i, wt):
-        x, dy, _, dx = self.sets[i % len(self.sets)]
+    def backward_input(self, i, wt):
+        _, dy, _, dx = self.sets[i % len(self.sets)]
         p, L = self.p, self.case.levels
         wt.wtconv_backward_input(dy, p["w0"], p["s0"], p["wl"], p["sl"], L, out=dx, workspace=self.ws)
+
+    def backward_weight(self, i, wt):
+        x, dy, _, _ = self.sets[i % len(self.sets)]
+        p, L = self.p, self.case.levels
         wt.wtconv_backward_weight(x, dy, p["w0"], p["b0"], p["s0"], p["wl"], p["sl"], L, out=self.grads,
                                   workspace=self.ws)
+
+    def backward(self, i, wt):
+        self.backward_input(i, wt)
+        self.backward_weight(i, wt)
 
 
 def memory_report(layers, torch):
@@ -134,15 +157,19 @@ def run_step(layers, i, wt):
         layer.backward(i, wt)
 
 
-def cpu_baseline(cases, budget_s, model_bytes_fn):
-    """Time the float64 CPU oracle (forward + backward) on a bounded sample of the
-    workload: the first planes of each layer's batch (all channels), grown by
-    doubling until one pass takes about budget_s / 8 or covers the whole batch,
-    then repeated until about budget_s / 2 has run.  Returns the oracle's rate in
-    the GPU value's units (algorithmic bytes of the sampled work per second)."""
+def cpu_baseline(cases, budget_s):
+    """Time the float64 CPU oracle on a bounded sample of the workload: the first
+    images of each layer's batch (all channels), grown by doubling until one
+    forward + backward takes about budget_s / 8 or covers the whole batch; then the
+    forward, the input gradient and the weight gradients are each repeated until
+    about budget_s / 6 has run.  Rates are in the GPU value's units: the sampled
+    images' share of the modeled bytes, per second.  The per-pass milliseconds are
+    extrapolated to the full batch."""
     import oracle
+    from memory_bound_depthwise_amd import traffic
     from synthetic import Case
-    total_s, total_bytes, samples, full_ms = 0.0, 0.0, [], 0.0
+    total_s, total_bytes, samples = 0.0, 0.0, []
+    pass_ms = {p: 0.0 for p in PASSES}
     per_layer = budget_s / len(cases)
     for case in cases:
         ns = 1
@@ -158,24 +185,34 @@ def cpu_baseline(cases, budget_s, model_bytes_fn):
             if dt > per_layer / 8 or ns >= case.n:
                 break
             ns = min(case.n, 2 * ns)
-        reps, spent = 1, dt
-        while spent < per_layer / 2:
-            t0 = time.perf_counter()
-            oracle.forward(x, q, case.levels, case.k)
-            oracle.backward(x, dy, q, case.levels, case.k)
-            spent += time.perf_counter() - t0
-            reps += 1
-        total_s += spent
-        total_bytes += reps * model_bytes_fn(sub)
-        samples.append(f"{case.name}: n={ns} of {case.n}, {reps} passes")
-        full_ms += 1e3 * spent / reps * case.n / ns
+        mb = traffic.model_bytes(ns, case.c, case.h, case.w, case.levels, 2 if case.dtype != "f32" else 4)
+        runs = {
+            "forward": lambda: oracle.forward(x, q, case.levels, case.k),
+            "backward_input": lambda: oracle.backward(x, dy, q, case.levels, case.k, outputs=("dx",)),
+            "backward_weight": lambda: oracle.backward(x, dy, q, case.levels, case.k,
+                                                       outputs=("dw0", "db0", "ds0", "dwl", "dsl")),
+        }
+        reps_note = []
+        for name, fn in runs.items():
+            times = []
+            while sum(times) < per_layer / 6 or not times:
+                t0 = time.perf_counter()
+                fn()
+                times.append(time.perf_counter() - t0)
+            total_s += sum(times)
+            total_bytes += len(times) * mb[name]
+            pass_ms[name] += 1e3 * statistics.median(times) * case.n / ns
+            reps_note.append(f"{name} x{len(times)}")
+        samples.append(f"{case.name}: n={ns} of {case.n} ({', '.join(reps_note)})")
     return {
         "value": round(total_bytes / total_s / 1e9, 4),
         "unit": "GB/s",
         "cores": oracle.threads(),
+        "nproc": os.cpu_count(),
         "kind": "oracle",
-        "sample": "; ".join(samples) + " (all channels; forward + backward in float64)",
-        "ms_per_step_extrapolated": round(full_ms, 1),
+        "sample": "; ".join(samples) + " (all channels, float64)",
+        "per_pass_ms_extrapolated": {k: round(v, 1) for k, v in pass_ms.items()},
+        "ms_per_step_extrapolated": round(sum(pass_ms.values()), 1),
         "seconds": round(total_s, 2),
     }
 
@@ -194,12 +231,28 @@ def load_traffic(kernel, workload, digest):
     return rec.get("kernels", {}).get(kernel)
 
 
+def timed(fn, steps, torch):
+    """Run fn(i) for i in range(steps) with an event before each step and after the
+    last; returns (wall ms, list of per-step ms)."""
+    stream = torch.cuda.current_stream()
+    evs = [torch.cuda.Event(enable_timing=True) for _ in range(steps + 1)]
+    torch.cuda.synchronize()
+    t0 = time.perf_counter()
+    for i in range(steps):
+        evs[i].record(stream)
+        fn(i)
+    evs[steps].record(stream)
+    torch.cuda.synchronize()
+    wall_ms = (time.perf_counter() - t0) * 1e3
+    return wall_ms, [evs[i].elapsed_time(evs[i + 1]) for i in range(steps)]
+
+
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
     ap.add_argument("--steps", type=int, default=20)
     ap.add_argument("--warmup", type=int, default=5)
-    ap.add_argument("--workload", default="stage1", choices=sorted(WORKLOADS))
+    ap.add_argument("--workload", default="stack", choices=sorted(WORKLOADS))
     ap.add_argument("--rotate", type=int, default=3)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=30.0, help="seconds for the oracle leg")
@@ -242,18 +295,14 @@ def main():
         # the kernels the library enqueues for this shape, priced by the byte model
         desc = wt.make_desc(c.n, c.c, c.h, c.w, c.k, c.levels, DTYPE_CODE[c.dtype])
         plan = {p: [e["name"] for e in wt.wtconv_plan_launches(desc, op)]
-                for p, op in (("forward", wt.OP_FORWARD), ("backward_input", wt.OP_BACKWARD_INPUT),
-                              ("backward_weight", wt.OP_BACKWARD_WEIGHT))}
+                for p, op in zip(PASSES, (wt.OP_FORWARD, wt.OP_BACKWARD_INPUT, wt.OP_BACKWARD_WEIGHT))}
         return traffic.launches_from_plan(c.n, c.c, c.h, c.w, c.k, c.levels, es(c), plan)
 
     case_ls = {c.name: case_launches(c) for c in cases}
-    step_bytes = sum(b for c in cases for _, _, b, _ in case_ls[c.name])
+    moved_bytes = sum(b for c in cases for _, _, b, _ in case_ls[c.name])
     step_flops = sum(f for c in cases for _, _, _, f in case_ls[c.name])
-    # context: the bytes the same step moves when it follows the paper's pass
-    # structure (one analysis + conv launch per level, coefficients through HBM,
-    # one synthesis pass with the base conv fused in; the per-level kernels here)
-    per_level_bytes = sum(b for c in cases
-                          for _, _, b, _ in traffic.launches(c.n, c.c, c.h, c.w, c.k, c.levels, es(c)))
+    model = {p: sum(traffic.model_bytes(c.n, c.c, c.h, c.w, c.levels, es(c))[p] for c in cases)
+             for p in PASSES + ("step",)}
 
     torch.cuda.reset_peak_memory_stats()
     for i in range(args.warmup):
@@ -261,19 +310,20 @@ def main():
     torch.cuda.synchronize()
 
     # timed region: exactly `steps` steps, synchronised on both sides
-    stream = torch.cuda.current_stream()
-    ev0, ev1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-    torch.cuda.synchronize()
-    t0 = time.perf_counter()
-    ev0.record(stream)
-    for i in range(args.steps):
-        run_step(layers, i, wt)
-    ev1.record(stream)
-    torch.cuda.synchronize()
-    wall_ms = (time.perf_counter() - t0) * 1e3
-    gpu_ms = ev0.elapsed_time(ev1)
+    wall_ms, step_ms = timed(lambda i: run_step(layers, i, wt), args.steps, torch)
+    gpu_ms = sum(step_ms)
     ms_per_step = max(wall_ms, gpu_ms) / args.steps
     print(f"# timed {args.steps} steps: {ms_per_step:.4f} ms/step", file=sys.stderr, flush=True)
+
+    # each pass on its own (forward of every layer, then input gradients, then weight gradients)
+    per_pass = {}
+    for name in PASSES:
+        fn = {"forward": lambda i: [l.forward(i, wt) for l in layers],
+              "backward_input": lambda i: [l.backward_input(i, wt) for l in reversed(layers)],
+              "backward_weight": lambda i: [l.backward_weight(i, wt) for l in reversed(layers)]}[name]
+        _, ms = timed(fn, args.steps, torch)
+        per_pass[name] = {"mean_ms": round(statistics.mean(ms), 5), "median_ms": round(statistics.median(ms), 5),
+                          "model_gbs": round(model[name] / (statistics.mean(ms) * 1e-3) / 1e9, 1)}
 
     # per-kernel durations: the same steps again with the library's event pairs
     wt.profile_begin()
@@ -282,7 +332,7 @@ def main():
     torch.cuda.synchronize()
     kstats = wt.profile_end()
 
-    # algorithmic bytes / flops per kernel family (summed over layers and passes)
+    # algorithmic bytes / flops per kernel name (summed over layers and passes)
     fam = {}
     for c in cases:
         for key, _pass, b, f in case_ls[c.name]:
@@ -307,23 +357,29 @@ def main():
     kernels.sort(key=lambda k: -k["ms_per_step"])
     dom = kernels[0]
     t_hbm = dom["bytes_per_launch"] / (HBM_PEAK_GBS * 1e9)
-    t_alu = dom["flops_per_launch"] / (ALU_PEAK_TFLOPS * 1e12)
+    t_alu = dom["flops_per_launch"] / (VALU_PEAK_TFLOPS * 1e12)
     digest = source_digest()
     if t_hbm >= t_alu:
         roof = {"bound": "hbm", "achieved": dom["gbs"], "peak": HBM_PEAK_GBS, "unit": "GB/s",
                 "frac": round(dom["gbs"] / HBM_PEAK_GBS, 4)}
     else:
-        roof = {"bound": "alu", "achieved": dom["tflops"], "peak": ALU_PEAK_TFLOPS, "unit": "TFLOP/s",
-                "frac": round(dom["tflops"] / ALU_PEAK_TFLOPS, 4)}
+        roof = {"bound": "alu", "achieved": dom["tflops"], "peak": VALU_PEAK_TFLOPS, "unit": "TFLOP/s",
+                "frac": round(dom["tflops"] / VALU_PEAK_TFLOPS, 4),
+                "frac_of_published_fp32_peak": round(dom["tflops"] / PUBLISHED_FP32_TFLOPS, 4),
+                "peak_note": "single-issue FP32 FMA: 256 CUs x 4 SIMDs x 16 lanes x 2 FLOP x 2.4 GHz; "
+                             "the published 157.3 TFLOP/s needs packed FP32, which the build does not emit"}
     roof["kernel"] = dom["kernel"]
     roof["avg_launch_ms"] = dom["avg_ms"]
+    roof["algorithmic_bytes_per_launch"] = dom["bytes_per_launch"]
+    roof["algorithmic_flops_per_launch"] = dom["flops_per_launch"]
     measured = load_traffic(dom["kernel"], args.workload, digest)
     roof["traffic"] = None if measured is None else measured["bytes"]
     if measured is not None:
         roof["traffic_fetch_write"] = [measured["fetch_bytes"], measured["write_bytes"]]
         roof["traffic_vs_algorithmic"] = round(measured["bytes"] / dom["bytes_per_launch"], 3)
 
-    value = step_bytes / (ms_per_step * 1e-3) / 1e9
+    value = model["step"] / (ms_per_step * 1e-3) / 1e9
+    moved_gbs = moved_bytes / (ms_per_step * 1e-3) / 1e9
     result = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -338,26 +394,25 @@ def main():
         "dtype": cases[0].dtype,
         "data": "synthetic",
         "config": {"workload": args.workload, "shapes": describe(cases), "pass": "forward + dx + dW",
-                   "rotate_buffer_sets": args.rotate, "step_bytes": step_bytes, "step_flops": step_flops},
+                   "rotate_buffer_sets": args.rotate, "model_step_bytes": model["step"],
+                   "moved_step_bytes": moved_bytes, "step_flops": step_flops},
         "hbm_frac": round(value / HBM_PEAK_GBS, 4),
-        "per_level_model": {
-            "step_bytes": per_level_bytes,
-            "gbs": round(per_level_bytes / (ms_per_step * 1e-3) / 1e9, 1),
-            "hbm_frac": round(per_level_bytes / (ms_per_step * 1e-3) / 1e9 / HBM_PEAK_GBS, 4),
-            "note": "bytes of the per-level pass structure over the measured step time: the bandwidth "
-                    "a per-level implementation would need to match this step; not moved by these kernels",
-        },
+        "ms_per_step_median": round(statistics.median(step_ms), 5),
+        "per_pass_ms": per_pass,
+        "moved_bytes": {"gbs": round(moved_gbs, 1), "hbm_frac": round(moved_gbs / HBM_PEAK_GBS, 4),
+                        "note": "bytes the launched kernels must move (plane-resident kernels: inputs and "
+                                "outputs only) over the step time"},
+        "valu": {"step_tflops": round(step_flops / (ms_per_step * 1e-3) / 1e12, 2),
+                 "frac": round(step_flops / (ms_per_step * 1e-3) / 1e12 / VALU_PEAK_TFLOPS, 4),
+                 "note": "convolution FLOPs of the step over the step time, against the single-issue FP32 FMA peak"},
         "source_digest": digest,
         "kernels": kernels,
         "roofline": roof,
         "memory": memory_report(layers, torch),
     }
     if not args.no_cpu_baseline:
-        def sample_bytes(c):
-            # the sample runs the full workload's shapes, so its bytes are the step's
-            return sum(b for _, _, b, _ in case_ls[c.name])
         print("# cpu baseline (oracle) ...", file=sys.stderr, flush=True)
-        result["cpu_baseline"] = cpu_baseline(cases, args.cpu_budget, sample_bytes)
+        result["cpu_baseline"] = cpu_baseline(cases, args.cpu_budget)
     print(json.dumps(result), flush=True)
 
 

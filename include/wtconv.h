@@ -53,6 +53,13 @@ extern "C" {
 #define WTCONV_VERSION 1
 #define WTCONV_MAX_LEVELS 8
 
+/* Symbols of the library's C interface (everything else in it is hidden). */
+#if defined(__GNUC__)
+#define WTCONV_API __attribute__((visibility("default")))
+#else
+#define WTCONV_API
+#endif
+
 /* Activation storage type. */
 enum wtconv_dtype { WTCONV_F32 = 0, WTCONV_BF16 = 1, WTCONV_F16 = 2 };
 
@@ -87,7 +94,7 @@ typedef struct wtconv_desc {
 
 /* Bytes of device workspace the operation needs for this shape (written to
  * *bytes; 0 is possible).  Returns a status code. */
-int wtconv_workspace_size(const wtconv_desc *desc, int op, size_t *bytes);
+WTCONV_API int wtconv_workspace_size(const wtconv_desc *desc, int op, size_t *bytes);
 
 /* Forward pass, §2.1 Algorithm 1 evaluated as in §4 of the paper.  Planes up to
  * 64 x 64 with L >= 1: one launch of a kernel that keeps a plane and its whole
@@ -99,7 +106,7 @@ int wtconv_workspace_size(const wtconv_desc *desc, int op, size_t *bytes);
  * convolution, the bias and the bit-indexed synthesis of all levels and stores
  * y (L + 1 launches, coefficients and carriers in the workspace).
  *   x [n][c][h][w] in, y [n][c][h][w] out (must not alias x). */
-int wtconv_forward(const wtconv_desc *desc, const void *x, const float *w0, const float *b0,
+WTCONV_API int wtconv_forward(const wtconv_desc *desc, const void *x, const float *w0, const float *b0,
                    const float *s0, const float *wl, const float *sl, void *y, void *workspace,
                    size_t workspace_bytes, void *stream);
 
@@ -109,7 +116,7 @@ int wtconv_forward(const wtconv_desc *desc, const void *x, const float *w0, cons
  * by 180 degrees and no bias (scales unchanged).
  *   dy [n][c][h][w] in, dx [n][c][h][w] out (must not alias dy).
  * The same kernels and workspace as the forward pass. */
-int wtconv_backward_input(const wtconv_desc *desc, const void *dy, const float *w0, const float *s0,
+WTCONV_API int wtconv_backward_input(const wtconv_desc *desc, const void *dy, const float *w0, const float *s0,
                           const float *wl, const float *sl, void *dx, void *workspace,
                           size_t workspace_bytes, void *stream);
 
@@ -122,7 +129,7 @@ int wtconv_backward_input(const wtconv_desc *desc, const void *dy, const float *
  * over workgroup partials kept in the workspace), so results are bitwise
  * repeatable for a given shape.  Planes up to 64 x 64: three launches (levels,
  * base, finalize); larger planes: L + 2 (one per level, base, finalize). */
-int wtconv_backward_weight(const wtconv_desc *desc, const void *x, const void *dy, const float *w0,
+WTCONV_API int wtconv_backward_weight(const wtconv_desc *desc, const void *x, const void *dy, const float *w0,
                            const float *b0, const float *s0, const float *wl, const float *sl,
                            float *dw0, float *db0, float *ds0, float *dwl, float *dsl,
                            void *workspace, size_t workspace_bytes, void *stream);
@@ -133,20 +140,24 @@ int wtconv_backward_weight(const wtconv_desc *desc, const void *x, const void *d
  * Writes up to max_entries entries and the total count to *n_entries.  Host only:
  * nothing is enqueued.  Returns a status code. */
 typedef struct wtconv_launch {
-    char name[64];       /* kernel family, k, dtype and level, e.g. "fused_fwd<5,bf16>" */
+    char name[64];       /* kernel family, k, dtype and level, e.g. "level_fwd<5,bf16>#2" */
     int64_t workgroups;  /* grid size in workgroups */
     int32_t threads;     /* workgroup size */
     int32_t lds_bytes;   /* dynamic LDS per workgroup */
+    int32_t variant;     /* plane-resident kernels: the compiled variant, 16 CW + RH (cells per
+                            staging item, cell rows per item), plus 256 for the base-only
+                            forward of levels = 0; 0 for the other kernels */
+    int32_t reserved;    /* 0 */
 } wtconv_launch;
 
-int wtconv_plan_launches(const wtconv_desc *desc, int op, wtconv_launch *out, int max_entries,
+WTCONV_API int wtconv_plan_launches(const wtconv_desc *desc, int op, wtconv_launch *out, int max_entries,
                          int *n_entries);
 
 /* Human-readable text of a status code (static storage). */
-const char *wtconv_status_string(int status);
+WTCONV_API const char *wtconv_status_string(int status);
 
 /* Library version (WTCONV_VERSION). */
-int wtconv_version(void);
+WTCONV_API int wtconv_version(void);
 
 /* ---- Per-kernel timing (tracing) ----------------------------------------
  * While profiling is on, every kernel launch is bracketed by two hipEvents
@@ -161,8 +172,8 @@ typedef struct wtconv_kernel_time {
     double min_ms, max_ms;
 } wtconv_kernel_time;
 
-int wtconv_profile_begin(void);
-int wtconv_profile_end(wtconv_kernel_time *out, int max_entries, int *n_entries);
+WTCONV_API int wtconv_profile_begin(void);
+WTCONV_API int wtconv_profile_end(wtconv_kernel_time *out, int max_entries, int *n_entries);
 
 #ifdef __cplusplus
 }

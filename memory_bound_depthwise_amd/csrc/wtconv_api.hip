@@ -1,12 +1,15 @@
-// Host side of libwtconv.so: argument checks, workspace plan, tiling, launches
-// and the C ABI declared in include/wtconv.h.
+// Host side of libwtconv.so: argument checks, launch plans, workspace sizes,
+// profiling records and the C ABI declared in include/wtconv.h.  The launch
+// sequences themselves are compiled once per kernel size and activation type
+// (wtconv_inst.hip, wtconv_run.hpp) and called through wtconv_host.hpp.
 //
 // Paper: "Fast and Memory-Efficient Wavelet Convolutions via I/O-Aware
 // Reformulation".  Launch sequence per call:
-//   forward / backward_input : level kernel for l = 1..L (§4.1), then the
-//                              closed-form synthesis + base kernel (§4.2-4.4);
-//   backward_weight          : level gradient kernel for l = 1..L, base gradient
-//                              kernel, finalize (fixed-order sums + Eq. 9).
+//   forward / backward_input : the plane-resident kernel, or the level kernel for
+//                              l = 1..L (§4.1) and the closed-form synthesis +
+//                              base kernel (§4.2-4.4);
+//   backward_weight          : level gradient kernel(s), base gradient kernel,
+//                              finalize (fixed-order sums + Eq. 9).
 
 #include <hip/hip_runtime.h>
 
@@ -17,35 +20,25 @@
 #include <memory>
 #include <mutex>
 #include <string>
-#include <type_traits>
 #include <vector>
 
 #include "wtconv.h"
-#include "wtconv_fused.hpp"
-#include "wtconv_fused_dw.hpp"
-#include "wtconv_plane.hpp"
-#include "wtconv_plane_dw.hpp"
-#include "wtconv_kernels.hpp"
+#include "wtconv_host.hpp"
 
 namespace wtc {
-namespace {
 
-constexpr int kThreads = 256;
-constexpr size_t kLdsBudget = 64 * 1024;   // bytes of LDS per workgroup we allow
+constexpr size_t kLdsBudget = 64 * 1024;   // bytes of LDS per workgroup of the per-level kernels
 constexpr int kDwTargetBlocks = 2048;      // workgroups wanted for the gradient kernels
-constexpr size_t kAlign = 256;
+constexpr int kPlaneMaxSide = 64;          // largest plane side of the plane-resident kernels
 
-inline size_t align_up(size_t v) { return (v + kAlign - 1) / kAlign * kAlign; }
-
-// Multiply-high reciprocal for fdiv (divisor and dividends below 2^16); 0 encodes 1.
-inline uint32_t magic_of(int d) { return d <= 1 ? 0u : (uint32_t)((0x100000000ULL + (uint64_t)d - 1) / (uint64_t)d); }
-inline int cdiv(long long a, long long b) { return (int)((a + b - 1) / b); }
 // Reciprocal for udiv16 (exact n / d for n < 2^16, d < 2^15): ceil(2^31 / d).
 inline uint32_t magic31_of(int d) { return (uint32_t)(((1ULL << 31) + (uint64_t)d - 1) / (uint64_t)d); }
 
 // ---------------------------------------------------------------------------
 // Profiling: hipEvent pairs around each launch, on the launch stream.
 // ---------------------------------------------------------------------------
+
+namespace {
 
 struct ProfRecord {
     std::string name;
@@ -68,53 +61,32 @@ hipEvent_t pooled_event() {
     return e;
 }
 
-// Name of an activation dtype as the launch records and plans spell it.
-const char *dtype_name(int dtype) {
-    return dtype == WTCONV_BF16 ? "bf16" : (dtype == WTCONV_F16 ? "f16" : "f32");
-}
-// Activation dtype of a storage type.
-template <typename T>
-constexpr int dtype_of() {
-    return std::is_same<T, uint16_t>::value ? WTCONV_BF16 : (std::is_same<T, wtc_f16>::value ? WTCONV_F16 : WTCONV_F32);
+
+}  // namespace
+
+bool prof_events(hipEvent_t &ev0, hipEvent_t &ev1) {
+    std::lock_guard<std::mutex> lock(g_prof_mu);
+    if (!g_prof_on) return false;
+    ev0 = pooled_event();
+    ev1 = pooled_event();
+    return ev0 && ev1;
 }
 
-template <typename Kern, typename Args>
-int launch(const char *family, int K, int dtype, int level, Kern kern, dim3 grid, dim3 block, size_t shmem,
-           hipStream_t stream, const Args &args) {
-    if (grid.x == 0 || grid.y == 0) return WTCONV_OK;
-    hipEvent_t ev0 = nullptr, ev1 = nullptr;
-    bool prof = false;
-    {
-        std::lock_guard<std::mutex> lock(g_prof_mu);
-        if (g_prof_on) {
-            ev0 = pooled_event();
-            ev1 = pooled_event();
-            prof = ev0 && ev1;
-        }
-    }
-    if (prof) (void)hipEventRecord(ev0, stream);
-    hipLaunchKernelGGL(kern, grid, block, shmem, stream, args);
-    hipError_t err = hipGetLastError();
-    if (prof) {
-        (void)hipEventRecord(ev1, stream);
-        char name[64];
-        if (level > 0)
-            snprintf(name, sizeof(name), "%s<%d,%s>#%d", family, K, dtype_name(dtype), level);
-        else
-            snprintf(name, sizeof(name), "%s<%d,%s>", family, K, dtype_name(dtype));
-        std::lock_guard<std::mutex> lock(g_prof_mu);
-        g_prof.push_back({name, ev0, ev1});
-    }
-    return err == hipSuccess ? WTCONV_OK : WTCONV_ERR_HIP;
+void prof_record(const char *family, int K, int dtype, int level, hipEvent_t ev0, hipEvent_t ev1) {
+    char name[64];
+    if (level > 0)
+        snprintf(name, sizeof(name), "%s<%d,%s>#%d", family, K, dtype_name(dtype), level);
+    else
+        snprintf(name, sizeof(name), "%s<%d,%s>", family, K, dtype_name(dtype));
+    std::lock_guard<std::mutex> lock(g_prof_mu);
+    g_prof.push_back({name, ev0, ev1});
 }
+
+namespace {
 
 // ---------------------------------------------------------------------------
-// Shapes, tiling and the workspace plan
+// Shapes, tiling and the workspace plan of the per-level kernels
 // ---------------------------------------------------------------------------
-
-struct LevelDims {
-    int H[kMaxLevels + 1], W[kMaxLevels + 1];  // H[0] = h; H[l] = ceil(H[l-1] / 2)
-};
 
 LevelDims level_dims(const wtconv_desc &d) {
     LevelDims ld;
@@ -125,23 +97,6 @@ LevelDims level_dims(const wtconv_desc &d) {
         ld.W[l] = (ld.W[l - 1] + 1) / 2;
     }
     return ld;
-}
-
-// Bytes of LDS a kernel needs for a tiling (HY rows staged per 8-row strip set
-// plus the K - 1 halo; see the kernels for the layouts).
-enum class Kind { LevelFwd, Synth, DwLevel, DwBase };
-
-size_t lds_bytes(Kind kind, int K, const Tiling &t) {
-    const int R = (K - 1) / 2, KK = K * K;
-    const size_t PB = t.PB, HY = (size_t)t.SP * kRH + K - 1, HXP = t.TX + K - 1, GY = (size_t)t.SP * kRH;
-    const size_t HXW = stage_width(t.TX, R, t.VW), GW = stage_width(t.TX, 0, t.VW);
-    switch (kind) {
-        case Kind::LevelFwd: return (PB * 4 * HY * HXP + 4 * KK) * sizeof(float);  // float4 cells, weight table
-        case Kind::Synth: return (PB * HY * HXW) * sizeof(float);
-        case Kind::DwLevel: return (PB * 4 * HY * HXP + PB * 4 * GY * t.TX + 4 * KK) * sizeof(float);
-        case Kind::DwBase: return (PB * HY * HXW + PB * GY * GW + (kThreads / kWave) * (KK + 1)) * sizeof(float);
-    }
-    return 0;
 }
 
 // Lanes that work on one item stream: a wavefront per band for the level kernels,
@@ -213,148 +168,12 @@ Tiling pick_tiling(Kind kind, int K, int n, int C, int Ho, int Wo, int VW) {
 
 bool tiling_fits(Kind kind, int K, const Tiling &t) { return lds_bytes(kind, K, t) <= kLdsBudget; }
 
-// Widest vector (elements) for staging rows of length W at pointer p.
-int vec_width(int W, int dtype, const void *p) {
-    int vw = dtype != WTCONV_F32 ? 8 : 4;
-    const size_t es = dtype != WTCONV_F32 ? 2 : 4;
-    while (vw > 1 && (W % vw != 0 || ((uintptr_t)p % (vw * es)) != 0)) vw /= 2;
-    return vw;
-}
-int max_vec_width(int dtype) { return dtype != WTCONV_F32 ? 8 : 4; }
-
-long long grid_of(const Tiling &t, int C) { return (long long)t.tiles * C * t.nblk; }
-
-// ---------------------------------------------------------------------------
-// Plane-resident forward (small planes): LDS layout and plane stacking
-// ---------------------------------------------------------------------------
-
-constexpr int kFusedMaxSide = 64;
-constexpr int kFusedTargetBlocks = 768;  // ~3 workgroups per compute unit
-
-// Layout of one plane block; fills everything but PB / NB / nblk / VE.  The weight
-// table comes first, then the plane blocks, then a tail so that the synthesis
-// reads of rows past the plane (values that are discarded) stay in the allocation.
-bool fused_layout(const wtconv_desc &d, FusedArgs &a) {
-    const int K = d.k, KK = K * K, KKP = (KK + 3) & ~3;
-    if (d.h > kFusedMaxSide || d.w > kFusedMaxSide) return false;
-    a.H = d.h;
-    a.W = d.w;
-    a.L = d.levels;
-    a.hl[0] = d.h;
-    a.wl_[0] = d.w;
-    for (int l = 1; l <= d.levels; ++l) {
-        a.hl[l] = (a.hl[l - 1] + 1) / 2;
-        a.wl_[l] = (a.wl_[l - 1] + 1) / 2;
-    }
-    for (int l = 0; l <= d.levels; ++l) a.sp[l] = cdiv(a.hl[l], kRH);
-    const int wtab_floats = (d.levels * 4 * KKP + 3) & ~3;
-    a.wtab = 0;
-    int off = wtab_floats;
-    // regions hold the grid plus its halo; the extra rows that the last 8-row strip
-    // reads (only for outputs past the grid, which are discarded) fall in the next
-    // region or in the tail of the allocation
-    a.xoff = off;
-    a.xs = d.w + K - 1;
-    off += (d.h + K - 1) * a.xs;
-    int items = 0;
-    for (int l = 0; l < d.levels; ++l) {
-        off = (off + 3) & ~3;
-        a.yb[l] = off;
-        a.sy[l] = a.wl_[l + 1] + K - 1;
-        a.bs[l] = (a.hl[l + 1] + K - 1) * a.sy[l];
-        off += 4 * a.bs[l];
-        items += 4 * a.sp[l + 1] * a.wl_[l + 1];
-        a.items_end[l] = items;
-    }
-    a.conv_items = items;
-    off = (off + 3) & ~3;
-    a.plane_floats = off - wtab_floats;
-    return true;
-}
-
-int fused_tail_floats(const FusedArgs &a) {
-    // Reads for discarded outputs run past a region by at most 8 rows (the last
-    // 8-row strip) or 4 block rows (synthesis); past every region but the last they
-    // land in the next region, past the last one in this tail.
-    const int last = a.L > 0 ? a.sy[a.L - 1] : a.xs;
-    return (kRH + 4) * last + 64;
-}
-
-int fused_prefetch_capacity(int dtype, int VE) {
-    // prefetch words per thread (8 for 16-bit activations, 16 for f32), 256 threads
-    const int es = dtype != WTCONV_F32 ? 2 : 4;
-    const int words = dtype != WTCONV_F32 ? 8 : 16;
-    const int words_per_vec = (VE * es + 3) / 4;
-    return (words / words_per_vec) * kThreads * VE;
-}
-
-// Choose PB (planes per pass) and NB (planes per workgroup).  False when the plane
-// is too large for the plane-resident kernel.
-bool plan_fused(const wtconv_desc &d, int VE, FusedArgs &a) {
-    if (d.n <= 0 || d.c <= 0 || d.h <= 0 || d.w <= 0) return false;
-    FusedArgs base{};
-    if (!fused_layout(d, base)) return false;
-    const int wtab_floats = base.xoff;
-    const int tail = fused_tail_floats(base);
-    const long long HW = (long long)d.h * d.w;
-    const int fin = base.sp[0] * d.w;
-    int haar = 0;
-    for (int l = 1; l <= d.levels; ++l) haar += base.hl[l] * base.wl_[l];
-    double best = 1e30;
-    int best_pb = 0;
-    for (int pb = 1; pb <= std::min(d.n, 64); ++pb) {
-        const long long lds = (long long)wtab_floats + (long long)pb * base.plane_floats + tail;
-        if (lds * 4 > (long long)kLdsBudget) break;
-        if ((long long)pb * base.conv_items > (long long)kFusedMaxItems * kThreads) break;
-        if ((long long)pb * fin > (long long)kFusedMaxFinal * kThreads) break;
-        if (pb * HW > fused_prefetch_capacity(d.dtype, VE)) break;
-        if ((long long)pb * d.c * HW >= (1LL << 30)) break;  // 32-bit offsets from a plane base
-        // estimated wave-instructions per pass: a conv or final item is 8 K^2 FMAs
-        // (+ synthesis for the final ones), Haar / combine ~15 per position, ~300 fixed
-        const double per_item = 8.0 * d.k * d.k;
-        const double cost = cdiv((long long)pb * base.conv_items, kThreads) * per_item +
-                            cdiv((long long)pb * fin, kThreads) * (per_item + 10.0 * d.levels + 20.0) +
-                            2.0 * cdiv((long long)pb * haar, kThreads) * 15.0 + 300.0;
-        if (cost / pb < best - 1e-9) {
-            best = cost / pb;
-            best_pb = pb;
-        }
-    }
-    if (best_pb == 0) return false;
-    a = base;
-    a.PB = best_pb;
-    a.lds_floats = wtab_floats + best_pb * base.plane_floats + tail;
-    a.VE = VE;
-    // planes per workgroup: a multiple of PB, about kFusedTargetBlocks workgroups
-    const long long passes = cdiv(d.n, a.PB);
-    const long long want_per_chan = std::max<long long>(1, cdiv(kFusedTargetBlocks, d.c));
-    const long long passes_per_wg = std::max<long long>(1, cdiv(passes, want_per_chan));
-    a.NB = (int)(passes_per_wg * a.PB);
-    a.nblk = cdiv(d.n, a.NB);
-    a.n = d.n;
-    a.C = d.c;
-    a.m_hw = magic_of((int)HW);
-    a.m_w = magic_of(d.w);
-    a.m_conv = magic_of(std::max(1, a.conv_items));
-    a.m_fin = magic_of(fin);
-    for (int l = 0; l < d.levels; ++l) {
-        a.m_per[l] = magic_of(a.hl[l + 1] * a.wl_[l + 1]);
-        a.m_wl[l] = magic_of(a.wl_[l + 1]);
-    }
-    return true;
-}
-
-
-
 // ---------------------------------------------------------------------------
 // Plane-resident forward on the polyphase grid: layout, stacking, bank-aware strides
 // ---------------------------------------------------------------------------
 
 constexpr int kPlaneLdsBudget = 40960;  // four workgroups per compute unit
 
-struct PlaneCfg {
-    int CW = 1, RH = 8;
-};
 
 // Bank cost of 16-byte cell reads by items (strip s, plane p, column j), item t =
 // (s PB + p) W1 + j on lane t, cell s RH sy + p Pw1 + j: gfx950 serves a 16-byte
@@ -472,7 +291,7 @@ bool plane_layout(const wtconv_desc &d, const PlaneCfg &cfg, int pb, PlaneArgs &
 // shape is outside the kernel's range.
 bool plan_plane(const wtconv_desc &d, PlaneArgs &a, PlaneCfg &cfg) {
     if (d.levels < 0 || d.n <= 0 || d.c <= 0 || d.h <= 0 || d.w <= 0) return false;
-    if (d.h > kFusedMaxSide || d.w > kFusedMaxSide) return false;
+    if (d.h > kPlaneMaxSide || d.w > kPlaneMaxSide) return false;
     const int H1 = (d.h + 1) / 2;
     cfg.RH = H1 % 7 == 0 ? 7 : (H1 <= 4 ? 4 : 8);
     cfg.CW = d.w % 8 == 0 ? 4 : (d.w % 4 == 0 ? 2 : 1);
@@ -555,7 +374,7 @@ int dw_blocks_per_channel(const wtconv_desc &d, int NG, int lds_floats) {
 
 bool plan_dwb(const wtconv_desc &d, PlaneDwbArgs &a, PlaneCfg &cfg) {
     if (d.n <= 0 || d.c <= 0 || d.h <= 0 || d.w <= 0) return false;
-    if (d.h > kFusedMaxSide || d.w > kFusedMaxSide) return false;
+    if (d.h > kPlaneMaxSide || d.w > kPlaneMaxSide) return false;
     const int H1 = (d.h + 1) / 2;
     cfg.RH = H1 % 7 == 0 ? 7 : (H1 <= 4 ? 4 : 8);
     cfg.CW = d.w % 8 == 0 ? 4 : (d.w % 4 == 0 ? 2 : 1);
@@ -699,7 +518,7 @@ int dwl_lane_items(const PlaneDwlArgs &a) {
 
 bool plan_dwl(const wtconv_desc &d, PlaneDwlArgs &a, PlaneCfg &cfg) {
     if (d.levels < 1 || d.n <= 0 || d.c <= 0 || d.h <= 0 || d.w <= 0) return false;
-    if (d.h > kFusedMaxSide || d.w > kFusedMaxSide) return false;
+    if (d.h > kPlaneMaxSide || d.w > kPlaneMaxSide) return false;
     cfg.RH = 4;  // item rows: one 16-byte read of dy per item
     cfg.CW = d.w % 8 == 0 ? 4 : (d.w % 4 == 0 ? 2 : 1);
     double best = 1e30;
@@ -737,129 +556,6 @@ bool plan_dwl(const wtconv_desc &d, PlaneDwlArgs &a, PlaneCfg &cfg) {
     return (long long)d.c * a.k < (1LL << 31);
 }
 
-// ---------------------------------------------------------------------------
-// Plane-resident weight gradient of the levels (small planes)
-// ---------------------------------------------------------------------------
-
-constexpr int kFusedDwTargetBlocks = 1024;
-
-// Layout and lane allocation from the shape alone (the prefetch capacity does not
-// depend on the vector width), so that the workspace size is shape-determined.
-bool plan_fused_dw(const wtconv_desc &d, FusedDwArgs &a) {
-    if (d.levels < 1 || d.n <= 0 || d.c <= 0 || d.h <= 0 || d.w <= 0) return false;
-    if (d.h > kFusedMaxSide || d.w > kFusedMaxSide) return false;
-    const int K = d.k, L = d.levels;
-    FusedDwArgs b{};
-    b.H = d.h;
-    b.W = d.w;
-    b.L = L;
-    b.hl[0] = d.h;
-    b.wl_[0] = d.w;
-    for (int l = 1; l <= L; ++l) {
-        b.hl[l] = (b.hl[l - 1] + 1) / 2;
-        b.wl_[l] = (b.wl_[l - 1] + 1) / 2;
-    }
-    for (int l = 0; l <= L; ++l) b.sp[l] = cdiv(b.hl[l], kRH);
-    // regions: x pyramid (halo R, rows trimmed to the grid), then dy pyramid (centre)
-    int off = 0;
-    for (int l = 0; l < L; ++l) {
-        off = (off + 3) & ~3;
-        b.yb[l] = off;
-        b.ys[l] = b.wl_[l + 1] + K - 1;
-        b.ybs[l] = (b.hl[l + 1] + K - 1) * b.ys[l];
-        off += 4 * b.ybs[l];
-    }
-    for (int l = 0; l < L; ++l) {
-        off = (off + 3) & ~3;
-        b.gb[l] = off;
-        b.gbs[l] = b.hl[l + 1] * b.wl_[l + 1];
-        off += 4 * b.gbs[l];
-    }
-    b.plane_floats = (off + 3) & ~3;
-    // reads for discarded rows run up to 8 (+4) rows past the last region
-    const int tail = (kRH + 4) * std::max(b.wl_[L], b.ys[L - 1]) + 64;
-    b.blocks = b.hl[1] * b.wl_[1];
-    const int capacity = d.dtype != WTCONV_F32 ? 2048 : 1024;  // level-1 blocks prefetched per pass
-    long long per_pair[kMaxLevels];
-    for (int l = 0; l < L; ++l) per_pair[l] = (long long)b.sp[l + 1] * b.wl_[l + 1];
-    const int KK = K * K;
-    double best = 1e30;
-    int best_pb = 0, best_r = 0;
-    for (int pb = 1; pb <= std::min(d.n, 16); ++pb) {
-        const long long lds = std::max<long long>((long long)pb * b.plane_floats + tail, 256LL * 9);
-        if (lds * 4 > (long long)kLdsBudget) break;
-        if ((long long)pb * b.blocks > capacity) break;
-        if ((long long)pb * d.c * d.h * d.w >= (1LL << 30)) break;
-        int r = 1;
-        for (; r <= kDwMaxRounds; ++r) {
-            long long lanes = 0;
-            for (int l = 0; l < L; ++l) lanes += 4 * cdiv(pb * per_pair[l], r);
-            if (lanes <= kThreads) break;
-        }
-        if (r > kDwMaxRounds) continue;
-        // wave-instructions per pass: r rounds of 8 K^2 FMAs (+ ~40), Haar ~300, fixed ~300
-        const double cost = r * (8.0 * KK + 40.0) + 300.0 + 300.0;
-        if (cost / pb < best - 1e-9) {
-            best = cost / pb;
-            best_pb = pb;
-            best_r = r;
-        }
-    }
-    if (best_pb == 0) return false;
-    a = b;
-    a.PB = best_pb;
-    a.rounds = best_r;
-    int lane = 0;
-    for (int l = 0; l < L; ++l)
-        for (int bd = 0; bd < 4; ++bd) {
-            a.lane0[4 * l + bd] = lane;
-            a.lanes[4 * l + bd] = cdiv(best_pb * per_pair[l], best_r);
-            lane += a.lanes[4 * l + bd];
-        }
-    a.lds_floats = (int)std::max<long long>((long long)best_pb * b.plane_floats + tail, 256LL * 9);
-    const long long passes = cdiv(d.n, a.PB);
-    const long long want_per_chan = std::max<long long>(1, cdiv(kFusedDwTargetBlocks, d.c));
-    const long long passes_per_wg = std::max<long long>(1, cdiv(passes, want_per_chan));
-    a.NB = (int)(passes_per_wg * a.PB);
-    a.nblk = cdiv(d.n, a.NB);
-    a.n = d.n;
-    a.C = d.c;
-    a.m_w1 = magic_of(a.wl_[1]);
-    a.m_blocks = magic_of(a.blocks);
-    for (int l = 0; l < L; ++l) {
-        a.m_per[l] = magic_of(a.hl[l + 1] * a.wl_[l + 1]);
-        a.m_wl[l] = magic_of(a.wl_[l + 1]);
-    }
-    return true;
-}
-
-struct FwdPlan {
-    LevelDims ld;
-    size_t q_off[kMaxLevels], c_off[kMaxLevels];  // byte offsets into the workspace
-    Tiling lvl[kMaxLevels], syn;
-    size_t bytes;
-};
-
-struct DwPlan {
-    bool fused;          // levels by the plane-resident kernel (no carriers)
-    FusedDwArgs fa;
-    bool dwb;            // base by the plane-resident kernel
-    PlaneDwbArgs ba;
-    PlaneCfg bcfg;
-    bool dwl;            // levels by the band-major plane-resident kernel
-    PlaneDwlArgs la;
-    PlaneCfg lcfg;
-    LevelDims ld;
-    size_t xc_off[kMaxLevels], gc_off[kMaxLevels];
-    size_t part_off;                 // byte offset of the partials
-    long long region[kMaxLevels + 1];  // float offsets within the partials
-    int G[kMaxLevels + 1];
-    Tiling lvl[kMaxLevels], base;
-    size_t bytes;
-};
-
-size_t elem_size(int dtype) { return dtype != WTCONV_F32 ? 2 : 4; }
-
 FwdPlan build_forward_plan(const wtconv_desc &d) {
     FwdPlan p{};
     p.ld = level_dims(d);
@@ -884,10 +580,9 @@ DwPlan build_backward_weight_plan(const wtconv_desc &d) {
     DwPlan p{};
     p.ld = level_dims(d);
     p.dwl = plan_dwl(d, p.la, p.lcfg);
-    p.fused = !p.dwl && plan_fused_dw(d, p.fa);
     const size_t es = elem_size(d.dtype), planes = (size_t)d.n * d.c;
     size_t off = 0;
-    if (!p.fused && !p.dwl) {
+    if (!p.dwl) {
         for (int l = 1; l < d.levels; ++l) {
             p.xc_off[l - 1] = off;
             off = align_up(off + planes * p.ld.H[l] * p.ld.W[l] * es);
@@ -911,8 +606,6 @@ DwPlan build_backward_weight_plan(const wtconv_desc &d) {
         p.region[l] = floats;
         if (p.dwl)
             p.G[l] = p.la.k;
-        else if (p.fused)
-            p.G[l] = p.fa.nblk;
         else
             p.G[l] = (d.n > 0 && d.h > 0 && d.w > 0) ? p.lvl[l - 1].nblk * p.lvl[l - 1].tiles : 0;
         floats += (long long)d.c * p.G[l] * 4 * KK;
@@ -922,21 +615,8 @@ DwPlan build_backward_weight_plan(const wtconv_desc &d) {
 }
 
 // ---------------------------------------------------------------------------
-// Argument checks
+// Plans per descriptor, argument checks
 // ---------------------------------------------------------------------------
-
-bool empty(const wtconv_desc &d) { return d.n == 0 || d.c == 0 || d.h == 0 || d.w == 0; }
-
-// Plans depend on the descriptor only; they are built once per descriptor and
-// kept (a call's host cost is then a lookup, not the layout searches).
-struct PlanSet {
-    wtconv_desc d;
-    FwdPlan fp;
-    DwPlan dp;
-    bool plane;  // forward by the plane-resident kernel
-    PlaneArgs pa;
-    PlaneCfg pcfg;
-};
 
 bool same_desc(const wtconv_desc &a, const wtconv_desc &b) {
     return a.n == b.n && a.c == b.c && a.h == b.h && a.w == b.w && a.k == b.k && a.levels == b.levels &&
@@ -962,13 +642,14 @@ std::shared_ptr<const PlanSet> plans_for(const wtconv_desc &d) {
     return ps;
 }
 
-FwdPlan plan_forward(const wtconv_desc &d) { return plans_for(d)->fp; }
-DwPlan plan_backward_weight(const wtconv_desc &d) { return plans_for(d)->dp; }
 
 // Workspace of the forward-shaped passes: none when the plane-resident kernel runs
 // (a choice made from the descriptor alone), the per-level coefficients and
 // carriers otherwise.
-size_t forward_workspace_bytes(const wtconv_desc &d) { return plans_for(d)->plane ? 0 : plan_forward(d).bytes; }
+size_t forward_workspace_bytes(const wtconv_desc &d) {
+    const auto ps = plans_for(d);
+    return ps->plane ? 0 : ps->fp.bytes;
+}
 
 int check_desc(const wtconv_desc *d) {
     if (!d) return WTCONV_ERR_NULL;
@@ -981,8 +662,9 @@ int check_desc(const wtconv_desc *d) {
     if ((long long)d->h * d->w > (1LL << 31) - 1) return WTCONV_ERR_SHAPE;
     if (planes > (1LL << 31) - 1) return WTCONV_ERR_SHAPE;
     if (!empty(*d)) {
-        const FwdPlan fp = plan_forward(*d);
-        const DwPlan dp = plan_backward_weight(*d);
+        const auto ps = plans_for(*d);
+        const FwdPlan &fp = ps->fp;
+        const DwPlan &dp = ps->dp;
         auto too_big = [&](const Tiling &t) { return grid_of(t, d->c) > (1LL << 31) - 1; };
         if (too_big(fp.syn) || too_big(dp.base)) return WTCONV_ERR_SHAPE;
         if (!tiling_fits(Kind::Synth, d->k, fp.syn) || !tiling_fits(Kind::DwBase, d->k, dp.base))
@@ -994,349 +676,6 @@ int check_desc(const wtconv_desc *d) {
         }
     }
     return WTCONV_OK;
-}
-
-bool aligned(const void *p, size_t a) { return ((uintptr_t)p % a) == 0; }
-
-// ---------------------------------------------------------------------------
-// Launch sequences, templated on kernel size K and activation storage T
-// ---------------------------------------------------------------------------
-
-template <int K, typename T>
-int run_fused_forward(const wtconv_desc &d, FusedArgs a, const void *x, const float *w0, const float *b0,
-                      const float *s0, const float *wl, const float *sl, void *y, hipStream_t st, int rotate) {
-    const int bf = dtype_of<T>();  // dtype code, for the launch records
-    a.x = x;
-    a.y = y;
-    a.w0 = w0;
-    a.b0 = b0;
-    a.s0 = s0;
-    a.wl = wl;
-    a.sl = sl;
-    a.rotate = rotate;
-    const dim3 grid((unsigned)((long long)d.c * a.nblk)), block(kThreads);
-    const size_t shm = (size_t)a.lds_floats * sizeof(float);
-    switch (a.VE) {
-        case 8:
-            if constexpr (sizeof(T) == 2)
-                return launch("fused_fwd", K, bf, 0, fused_fwd_kernel<K, T, 8>, grid, block, shm, st, a);
-            return WTCONV_ERR_HIP;
-        case 4: return launch("fused_fwd", K, bf, 0, fused_fwd_kernel<K, T, 4>, grid, block, shm, st, a);
-        case 2: return launch("fused_fwd", K, bf, 0, fused_fwd_kernel<K, T, 2>, grid, block, shm, st, a);
-        default: return launch("fused_fwd", K, bf, 0, fused_fwd_kernel<K, T, 1>, grid, block, shm, st, a);
-    }
-}
-
-template <int K, typename T, int CW>
-const void *plane_kernel_rh(int RH, bool base) {
-#define WTC_PKR(RH_) base ? reinterpret_cast<const void *>(plane_fwd_kernel<K, T, CW, RH_, true>) \
-                          : reinterpret_cast<const void *>(plane_fwd_kernel<K, T, CW, RH_, false>)
-    switch (RH) {
-        case 7: return WTC_PKR(7);
-        case 4: return WTC_PKR(4);
-        default: return WTC_PKR(8);
-    }
-#undef WTC_PKR
-}
-
-template <int K, typename T>
-const void *plane_kernel(const PlaneCfg &cfg, bool base) {
-    switch (cfg.CW) {
-        case 4: return plane_kernel_rh<K, T, 4>(cfg.RH, base);
-        case 2: return plane_kernel_rh<K, T, 2>(cfg.RH, base);
-        default: return plane_kernel_rh<K, T, 1>(cfg.RH, base);
-    }
-}
-
-const void *plane_kernel_for(const wtconv_desc &d, const PlaneCfg &cfg) {
-    const bool base = d.levels == 0;
-#define WTC_PK(KV) \
-    (d.dtype == WTCONV_BF16 ? plane_kernel<KV, uint16_t>(cfg, base) \
-                            : d.dtype == WTCONV_F16 ? plane_kernel<KV, wtc_f16>(cfg, base) : plane_kernel<KV, float>(cfg, base))
-    switch (d.k) {
-        case 3: return WTC_PK(3);
-        case 5: return WTC_PK(5);
-        default: return WTC_PK(7);
-    }
-#undef WTC_PK
-}
-
-// Persistent grid: as many workgroups as can be resident at once on the current
-// device (they stride over the units), never more than the units.
-int plane_grid(const wtconv_desc &d, const PlaneArgs &a, const PlaneCfg &cfg) {
-    int dev = 0, cus = 0, per_cu = 0;
-    const size_t shm = (size_t)a.lds_floats * sizeof(float);
-    const void *kern = plane_kernel_for(d, cfg);
-    static std::mutex mu;
-    struct Entry {
-        int dev;
-        const void *kern;
-        size_t shm;
-        int slots;
-    };
-    static std::vector<Entry> seen;
-    if (hipGetDevice(&dev) == hipSuccess) {
-        std::lock_guard<std::mutex> lock(mu);
-        for (const Entry &e : seen)
-            if (e.dev == dev && e.kern == kern && e.shm == shm) return (int)std::min<long long>(a.U, e.slots);
-    }
-    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
-        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, kFwdThreads, shm) != hipSuccess ||
-        cus <= 0 || per_cu <= 0) {
-        (void)hipGetLastError();
-        cus = 256;
-        per_cu = std::max(1, std::min(4, (int)((160 * 1024) / std::max<size_t>(shm, 1))));
-    } else {
-        std::lock_guard<std::mutex> lock(mu);
-        seen.push_back(Entry{dev, kern, shm, cus * per_cu});
-    }
-    return (int)std::min<long long>(a.U, (long long)cus * per_cu);
-}
-
-template <int K, typename T>
-int run_plane_forward(const wtconv_desc &d, PlaneArgs a, const PlaneCfg &cfg, const void *x, const float *w0,
-                      const float *b0, const float *s0, const float *wl, const float *sl, void *y, hipStream_t st,
-                      int rotate) {
-    a.x = x;
-    a.y = y;
-    a.w0 = w0;
-    a.b0 = b0;
-    a.s0 = s0;
-    a.wl = wl;
-    a.sl = sl;
-    a.rotate = rotate;
-    a.vec = d.w % (2 * cfg.CW) == 0 && aligned(x, 2 * cfg.CW * sizeof(T)) ? 1 : 0;
-    a.pair_store = d.w % 2 == 0 && aligned(y, 2 * sizeof(T)) ? 1 : 0;
-    const dim3 grid((unsigned)plane_grid(d, a, cfg));
-    const size_t shm = (size_t)a.lds_floats * sizeof(float);
-    const int bf = dtype_of<T>();  // dtype code, for the launch records
-#define WTC_PLANE_LAUNCH(CW_, RH_)                                                                                \
-    (d.levels == 0                                                                                               \
-         ? launch("plane_fwd", K, bf, 0, plane_fwd_kernel<K, T, CW_, RH_, true>, grid, dim3(kFwdThreads), shm, st, a) \
-         : launch("plane_fwd", K, bf, 0, plane_fwd_kernel<K, T, CW_, RH_, false>, grid, dim3(kFwdThreads), shm, st, a))
-    switch (cfg.CW * 16 + cfg.RH) {
-        case 4 * 16 + 7: return WTC_PLANE_LAUNCH(4, 7);
-        case 4 * 16 + 4: return WTC_PLANE_LAUNCH(4, 4);
-        case 4 * 16 + 8: return WTC_PLANE_LAUNCH(4, 8);
-        case 2 * 16 + 7: return WTC_PLANE_LAUNCH(2, 7);
-        case 2 * 16 + 4: return WTC_PLANE_LAUNCH(2, 4);
-        case 2 * 16 + 8: return WTC_PLANE_LAUNCH(2, 8);
-        case 1 * 16 + 7: return WTC_PLANE_LAUNCH(1, 7);
-        case 1 * 16 + 4: return WTC_PLANE_LAUNCH(1, 4);
-        default: return WTC_PLANE_LAUNCH(1, 8);
-    }
-#undef WTC_PLANE_LAUNCH
-}
-
-template <int K, typename T>
-int run_plane_dwb(const wtconv_desc &d, PlaneDwbArgs a, const PlaneCfg &cfg, const void *x, const void *dy,
-                  float *partial, hipStream_t st) {
-    a.x = x;
-    a.dy = dy;
-    a.partial = partial;
-    a.vec = d.w % (2 * cfg.CW) == 0 && aligned(x, 2 * cfg.CW * sizeof(T)) && aligned(dy, 2 * cfg.CW * sizeof(T)) ? 1 : 0;
-    const dim3 grid((unsigned)((long long)d.c * a.k));
-    const size_t shm = (size_t)a.lds_floats * sizeof(float);
-    const int bf = dtype_of<T>();  // dtype code, for the launch records
-#define WTC_DWB_LAUNCH(CW_, RH_) \
-    launch("plane_dwb", K, bf, 0, plane_dwb_kernel<K, T, CW_, RH_>, grid, dim3(kDwbThreads), shm, st, a)
-    switch (cfg.CW * 16 + cfg.RH) {
-        case 4 * 16 + 7: return WTC_DWB_LAUNCH(4, 7);
-        case 4 * 16 + 4: return WTC_DWB_LAUNCH(4, 4);
-        case 4 * 16 + 8: return WTC_DWB_LAUNCH(4, 8);
-        case 2 * 16 + 7: return WTC_DWB_LAUNCH(2, 7);
-        case 2 * 16 + 4: return WTC_DWB_LAUNCH(2, 4);
-        case 2 * 16 + 8: return WTC_DWB_LAUNCH(2, 8);
-        case 1 * 16 + 7: return WTC_DWB_LAUNCH(1, 7);
-        case 1 * 16 + 4: return WTC_DWB_LAUNCH(1, 4);
-        default: return WTC_DWB_LAUNCH(1, 8);
-    }
-#undef WTC_DWB_LAUNCH
-}
-
-template <int K, typename T>
-int run_plane_dwl(const wtconv_desc &d, const DwPlan &p, const void *x, const void *dy, float *partial,
-                  hipStream_t st) {
-    PlaneDwlArgs a = p.la;
-    const PlaneCfg &cfg = p.lcfg;
-    a.x = x;
-    a.dy = dy;
-    a.partial = partial;
-    for (int l = 0; l < d.levels; ++l) a.off[l] = p.region[l + 1];
-    a.vec = d.w % (2 * cfg.CW) == 0 && aligned(x, 2 * cfg.CW * sizeof(T)) && aligned(dy, 2 * cfg.CW * sizeof(T)) ? 1 : 0;
-    const dim3 grid((unsigned)((long long)d.c * a.k));
-    const size_t shm = (size_t)a.lds_floats * sizeof(float);
-    const int bf = dtype_of<T>();  // dtype code, for the launch records
-#define WTC_DWL_LAUNCH(CW_, RH_) \
-    launch("plane_dwl", K, bf, 0, plane_dwl_kernel<K, T, CW_, RH_>, grid, dim3(kDwlThreads), shm, st, a)
-    switch (cfg.CW) {
-        case 4: return WTC_DWL_LAUNCH(4, 4);
-        case 2: return WTC_DWL_LAUNCH(2, 4);
-        default: return WTC_DWL_LAUNCH(1, 4);
-    }
-#undef WTC_DWL_LAUNCH
-}
-
-template <int K, typename T>
-int run_forward(const wtconv_desc &d, const void *x, const float *w0, const float *b0, const float *s0,
-                const float *wl, const float *sl, void *y, char *ws, hipStream_t st, int rotate) {
-    {
-        const auto ps = plans_for(d);
-        if (ps->plane) return run_plane_forward<K, T>(d, ps->pa, ps->pcfg, x, w0, b0, s0, wl, sl, y, st, rotate);
-    }
-    {
-        FusedArgs fa{};
-        if (plan_fused(d, vec_width(d.w, d.dtype, x), fa))
-            return run_fused_forward<K, T>(d, fa, x, w0, b0, s0, wl, sl, y, st, rotate);
-    }
-    const FwdPlan p = plan_forward(d);
-    const int bf = dtype_of<T>();  // dtype code, for the launch records
-
-    const int L = d.levels;
-    for (int l = 1; l <= L; ++l) {
-        LevelArgs a{};
-        a.in = l == 1 ? x : (const void *)(ws + p.c_off[l - 2]);
-        a.qout = ws + p.q_off[l - 1];
-        a.cout = l < L ? (void *)(ws + p.c_off[l - 1]) : nullptr;
-        a.wl = wl + (size_t)(l - 1) * d.c * 4 * K * K;
-        a.sl = sl + (size_t)(l - 1) * d.c * 4;
-        a.n = d.n;
-        a.C = d.c;
-        a.Hi = p.ld.H[l - 1];
-        a.Wi = p.ld.W[l - 1];
-        a.Ho = p.ld.H[l];
-        a.Wo = p.ld.W[l];
-        a.wscale = std::ldexp(1.0f, -(l + 1));
-        a.rotate = rotate;
-        a.pairs = (a.Wi % 2 == 0) && ((uintptr_t)a.in % (2 * sizeof(T)) == 0);
-        a.t = p.lvl[l - 1];
-        const size_t shm = lds_bytes(Kind::LevelFwd, K, a.t);
-        int rc = launch("level_fwd", K, bf, l, level_fwd_kernel<K, T>, dim3((unsigned)grid_of(a.t, d.c)),
-                        dim3(kThreads), shm, st, a);
-        if (rc) return rc;
-    }
-    SynthArgs s{};
-    s.x = x;
-    s.y = y;
-    s.w0 = w0;
-    s.b0 = b0;
-    s.s0 = s0;
-    for (int l = 1; l <= L; ++l) {
-        s.q[l - 1] = ws + p.q_off[l - 1];
-        s.wq[l - 1] = 2 * p.ld.W[l];
-        s.qplane[l - 1] = 4LL * p.ld.H[l] * p.ld.W[l];
-    }
-    s.n = d.n;
-    s.C = d.c;
-    s.H = d.h;
-    s.W = d.w;
-    s.L = L;
-    s.rotate = rotate;
-    s.t = p.syn;
-    s.t.VW = vec_width(d.w, d.dtype, x);
-    const size_t shm = lds_bytes(Kind::Synth, K, s.t);
-    return launch("synth", K, bf, 0, synth_kernel<K, T>, dim3((unsigned)grid_of(s.t, d.c)), dim3(kThreads), shm, st,
-                  s);
-}
-
-template <int K, typename T>
-int run_backward_weight(const wtconv_desc &d, const void *x, const void *dy, const float *w0, const float *b0,
-                        const float *s0, const float *wl, const float *sl, float *dw0, float *db0, float *ds0,
-                        float *dwl, float *dsl, char *ws, hipStream_t st) {
-    const DwPlan p = plan_backward_weight(d);
-    const int bf = dtype_of<T>();  // dtype code, for the launch records
-    const int L = d.levels;
-    float *partial = reinterpret_cast<float *>(ws + p.part_off);
-    if (!empty(d) && p.dwl && L > 0) {
-        int rc = run_plane_dwl<K, T>(d, p, x, dy, partial, st);
-        if (rc) return rc;
-    }
-    if (!empty(d) && p.fused && L > 0) {
-        FusedDwArgs a = p.fa;
-        a.x = x;
-        a.dy = dy;
-        a.partial = partial;
-        for (int l = 0; l < L; ++l) a.off[l] = p.region[l + 1];
-        const int ve = std::min(vec_width(d.w, d.dtype, x), vec_width(d.w, d.dtype, dy));
-        a.VE = ve >= 2 ? ve : 1;
-        const dim3 grid((unsigned)((long long)d.c * a.nblk)), block(kThreads);
-        const size_t shm = (size_t)a.lds_floats * sizeof(float);
-        int rc;
-        switch (a.VE) {
-            case 8:
-                if constexpr (sizeof(T) == 2) {
-                    rc = launch("fused_dw", K, bf, 0, fused_dw_kernel<K, T, 8>, grid, block, shm, st, a);
-                    break;
-                }
-                return WTCONV_ERR_HIP;
-            case 4: rc = launch("fused_dw", K, bf, 0, fused_dw_kernel<K, T, 4>, grid, block, shm, st, a); break;
-            case 2: rc = launch("fused_dw", K, bf, 0, fused_dw_kernel<K, T, 2>, grid, block, shm, st, a); break;
-            default: rc = launch("fused_dw", K, bf, 0, fused_dw_kernel<K, T, 1>, grid, block, shm, st, a); break;
-        }
-        if (rc) return rc;
-    }
-    if (!empty(d)) {
-        for (int l = 1; l <= L && !p.fused && !p.dwl; ++l) {
-            DwLevelArgs a{};
-            a.xin = l == 1 ? x : (const void *)(ws + p.xc_off[l - 2]);
-            a.gin = l == 1 ? dy : (const void *)(ws + p.gc_off[l - 2]);
-            a.xc = l < L ? (void *)(ws + p.xc_off[l - 1]) : nullptr;
-            a.gc = l < L ? (void *)(ws + p.gc_off[l - 1]) : nullptr;
-            a.partial = partial + p.region[l];
-            a.n = d.n;
-            a.C = d.c;
-            a.Hi = p.ld.H[l - 1];
-            a.Wi = p.ld.W[l - 1];
-            a.Ho = p.ld.H[l];
-            a.Wo = p.ld.W[l];
-            a.pairs = (a.Wi % 2 == 0) && ((uintptr_t)a.xin % (2 * sizeof(T)) == 0) &&
-                      ((uintptr_t)a.gin % (2 * sizeof(T)) == 0);
-            a.t = p.lvl[l - 1];
-            const size_t shm = lds_bytes(Kind::DwLevel, K, a.t);
-            int rc = launch("dw_level", K, bf, l, dw_level_kernel<K, T>, dim3((unsigned)grid_of(a.t, d.c)),
-                            dim3(kThreads), shm, st, a);
-            if (rc) return rc;
-        }
-        if (p.dwb) {
-            int rc = run_plane_dwb<K, T>(d, p.ba, p.bcfg, x, dy, partial + p.region[0], st);
-            if (rc) return rc;
-        }
-        DwBaseArgs b{};
-        b.x = x;
-        b.dy = dy;
-        b.partial = partial + p.region[0];
-        b.n = d.n;
-        b.C = d.c;
-        b.H = d.h;
-        b.W = d.w;
-        b.t = p.base;
-        b.t.VW = std::min(vec_width(d.w, d.dtype, x), vec_width(d.w, d.dtype, dy));
-        const size_t shm = lds_bytes(Kind::DwBase, K, b.t);
-        int rc = p.dwb ? 0
-                       : launch("dw_base", K, bf, 0, dw_base_kernel<K, T>, dim3((unsigned)grid_of(b.t, d.c)),
-                                dim3(kThreads), shm, st, b);
-        if (rc) return rc;
-    }
-    FinalizeArgs f{};
-    f.partial = partial;
-    for (int r = 0; r <= L; ++r) {
-        f.off[r] = p.region[r];
-        f.G[r] = p.G[r];
-    }
-    f.C = d.c;
-    f.L = L;
-    f.w0 = w0;
-    f.b0 = b0;
-    f.s0 = s0;
-    f.wl = wl;
-    f.sl = sl;
-    f.dw0 = dw0;
-    f.db0 = db0;
-    f.ds0 = ds0;
-    f.dwl = dwl;
-    f.dsl = dsl;
-    return launch("dw_finalize", K, bf, 0, dw_finalize_kernel<K>, dim3((unsigned)d.c, (unsigned)(L + 1)), dim3(128), 0,
-                  st, f);
 }
 
 #define WTC_DISPATCH(KVAL, DTYPE, FN, ...)                                   \
@@ -1353,6 +692,8 @@ int run_backward_weight(const wtconv_desc &d, const void *x, const void *dy, con
         }                                                                   \
     } while (0)
 
+int plane_grid_for(const PlanSet &ps) { WTC_DISPATCH(ps.d.k, ps.d.dtype, plane_grid, ps); }
+
 int fwd_common(const wtconv_desc *desc, const void *in, const float *w0, const float *b0, const float *s0,
                const float *wl, const float *sl, void *out, void *workspace, size_t workspace_bytes, void *stream,
                int rotate) {
@@ -1365,11 +706,12 @@ int fwd_common(const wtconv_desc *desc, const void *in, const float *w0, const f
     if (!aligned(in, es) || !aligned(out, es) || !aligned(w0, 4) || !aligned(s0, 4) || (b0 && !aligned(b0, 4)) ||
         (wl && !aligned(wl, 4)) || (sl && !aligned(sl, 4)))
         return WTCONV_ERR_ALIGN;
-    const size_t need = forward_workspace_bytes(d);
+    const auto ps = plans_for(d);
+    const size_t need = ps->plane ? 0 : ps->fp.bytes;
     if (need > 0 && (!workspace || workspace_bytes < need)) return WTCONV_ERR_WORKSPACE;
     if (workspace && !aligned(workspace, 16)) return WTCONV_ERR_ALIGN;
     hipStream_t st = static_cast<hipStream_t>(stream);
-    WTC_DISPATCH(d.k, d.dtype, run_forward, d, in, w0, b0, s0, wl, sl, out, static_cast<char *>(workspace), st,
+    WTC_DISPATCH(d.k, d.dtype, run_forward, *ps, in, w0, b0, s0, wl, sl, out, static_cast<char *>(workspace), st,
                  rotate);
 }
 
@@ -1380,9 +722,9 @@ using namespace wtc;
 
 extern "C" {
 
-int wtconv_version(void) { return WTCONV_VERSION; }
+WTCONV_API int wtconv_version(void) { return WTCONV_VERSION; }
 
-const char *wtconv_status_string(int status) {
+WTCONV_API const char *wtconv_status_string(int status) {
     switch (status) {
         case WTCONV_OK: return "ok";
         case WTCONV_ERR_SHAPE: return "invalid shape (negative extent or tensor too large)";
@@ -1398,7 +740,7 @@ const char *wtconv_status_string(int status) {
     }
 }
 
-int wtconv_workspace_size(const wtconv_desc *desc, int op, size_t *bytes) {
+WTCONV_API int wtconv_workspace_size(const wtconv_desc *desc, int op, size_t *bytes) {
     if (!bytes) return WTCONV_ERR_NULL;
     *bytes = 0;
     int rc = check_desc(desc);
@@ -1406,29 +748,29 @@ int wtconv_workspace_size(const wtconv_desc *desc, int op, size_t *bytes) {
     if (op != WTCONV_OP_FORWARD && op != WTCONV_OP_BACKWARD_INPUT && op != WTCONV_OP_BACKWARD_WEIGHT)
         return WTCONV_ERR_OP;
     if (op == WTCONV_OP_BACKWARD_WEIGHT) {
-        *bytes = plan_backward_weight(*desc).bytes;
+        *bytes = plans_for(*desc)->dp.bytes;
     } else {
         *bytes = empty(*desc) ? 0 : forward_workspace_bytes(*desc);
     }
     return WTCONV_OK;
 }
 
-int wtconv_forward(const wtconv_desc *desc, const void *x, const float *w0, const float *b0, const float *s0,
-                   const float *wl, const float *sl, void *y, void *workspace, size_t workspace_bytes,
-                   void *stream) {
+WTCONV_API int wtconv_forward(const wtconv_desc *desc, const void *x, const float *w0, const float *b0,
+                              const float *s0, const float *wl, const float *sl, void *y, void *workspace,
+                              size_t workspace_bytes, void *stream) {
     return fwd_common(desc, x, w0, b0, s0, wl, sl, y, workspace, workspace_bytes, stream, 0);
 }
 
-int wtconv_backward_input(const wtconv_desc *desc, const void *dy, const float *w0, const float *s0,
-                          const float *wl, const float *sl, void *dx, void *workspace, size_t workspace_bytes,
-                          void *stream) {
+WTCONV_API int wtconv_backward_input(const wtconv_desc *desc, const void *dy, const float *w0, const float *s0,
+                                     const float *wl, const float *sl, void *dx, void *workspace,
+                                     size_t workspace_bytes, void *stream) {
     return fwd_common(desc, dy, w0, nullptr, s0, wl, sl, dx, workspace, workspace_bytes, stream, 1);
 }
 
-int wtconv_backward_weight(const wtconv_desc *desc, const void *x, const void *dy, const float *w0,
-                           const float *b0, const float *s0, const float *wl, const float *sl, float *dw0,
-                           float *db0, float *ds0, float *dwl, float *dsl, void *workspace, size_t workspace_bytes,
-                           void *stream) {
+WTCONV_API int wtconv_backward_weight(const wtconv_desc *desc, const void *x, const void *dy, const float *w0,
+                                      const float *b0, const float *s0, const float *wl, const float *sl,
+                                      float *dw0, float *db0, float *ds0, float *dwl, float *dsl, void *workspace,
+                                      size_t workspace_bytes, void *stream) {
     int rc = check_desc(desc);
     if (rc) return rc;
     const wtconv_desc &d = *desc;
@@ -1441,15 +783,16 @@ int wtconv_backward_weight(const wtconv_desc *desc, const void *x, const void *d
         (wl && !aligned(wl, 4)) || (sl && !aligned(sl, 4)) || (dwl && !aligned(dwl, 4)) ||
         (dsl && !aligned(dsl, 4)))
         return WTCONV_ERR_ALIGN;
-    const DwPlan p = plan_backward_weight(d);
-    if (p.bytes > 0 && (!workspace || workspace_bytes < p.bytes)) return WTCONV_ERR_WORKSPACE;
+    const auto ps = plans_for(d);
+    if (ps->dp.bytes > 0 && (!workspace || workspace_bytes < ps->dp.bytes)) return WTCONV_ERR_WORKSPACE;
     if (workspace && !aligned(workspace, 16)) return WTCONV_ERR_ALIGN;
     hipStream_t st = static_cast<hipStream_t>(stream);
-    WTC_DISPATCH(d.k, d.dtype, run_backward_weight, d, x, dy, w0, b0, s0, wl, sl, dw0, db0, ds0, dwl, dsl,
+    WTC_DISPATCH(d.k, d.dtype, run_backward_weight, *ps, x, dy, w0, b0, s0, wl, sl, dw0, db0, ds0, dwl, dsl,
                  static_cast<char *>(workspace), st);
 }
 
-int wtconv_plan_launches(const wtconv_desc *desc, int op, wtconv_launch *out, int max_entries, int *n_entries) {
+WTCONV_API int wtconv_plan_launches(const wtconv_desc *desc, int op, wtconv_launch *out, int max_entries,
+                                    int *n_entries) {
     if (!n_entries) return WTCONV_ERR_NULL;
     *n_entries = 0;
     int rc = check_desc(desc);
@@ -1458,10 +801,10 @@ int wtconv_plan_launches(const wtconv_desc *desc, int op, wtconv_launch *out, in
         return WTCONV_ERR_OP;
     const wtconv_desc &d = *desc;
     const char *dt = dtype_name(d.dtype);
-    const size_t es = elem_size(d.dtype);
     std::vector<wtconv_launch> v;
-    auto add = [&](const char *fam, int level, long long wg, int thr, size_t lds) {
+    auto add = [&](const char *fam, int level, long long wg, int thr, size_t lds, int variant = 0) {
         wtconv_launch e{};
+        e.variant = variant;
         if (level > 0)
             snprintf(e.name, sizeof(e.name), "%s<%d,%s>#%d", fam, d.k, dt, level);
         else
@@ -1472,17 +815,14 @@ int wtconv_plan_launches(const wtconv_desc *desc, int op, wtconv_launch *out, in
         if (wg > 0) v.push_back(e);
     };
     const void *aligned_ptr = reinterpret_cast<const void *>(uintptr_t(256));
+    const auto ps = plans_for(d);
     if (op != WTCONV_OP_BACKWARD_WEIGHT) {
         if (!empty(d)) {
-            FusedArgs fa{};
-            const auto ps = plans_for(d);
             if (ps->plane) {
-                add("plane_fwd", 0, plane_grid(d, ps->pa, ps->pcfg), kFwdThreads,
-                    (size_t)ps->pa.lds_floats * sizeof(float));
-            } else if (plan_fused(d, vec_width(d.w, d.dtype, aligned_ptr), fa)) {
-                add("fused_fwd", 0, (long long)d.c * fa.nblk, kThreads, (size_t)fa.lds_floats * sizeof(float));
+                add("plane_fwd", 0, plane_grid_for(*ps), kFwdThreads, (size_t)ps->pa.lds_floats * sizeof(float),
+                    16 * ps->pcfg.CW + ps->pcfg.RH + (d.levels == 0 ? 256 : 0));
             } else {
-                const FwdPlan p = plan_forward(d);
+                const FwdPlan &p = ps->fp;
                 for (int l = 1; l <= d.levels; ++l)
                     add("level_fwd", l, grid_of(p.lvl[l - 1], d.c), kThreads, lds_bytes(Kind::LevelFwd, d.k, p.lvl[l - 1]));
                 Tiling t = p.syn;
@@ -1491,18 +831,18 @@ int wtconv_plan_launches(const wtconv_desc *desc, int op, wtconv_launch *out, in
             }
         }
     } else if (d.c > 0) {
-        const DwPlan p = plan_backward_weight(d);
+        const DwPlan &p = ps->dp;
         if (!empty(d)) {
             if (p.dwl && d.levels > 0) {
-                add("plane_dwl", 0, (long long)d.c * p.la.k, kDwlThreads, (size_t)p.la.lds_floats * sizeof(float));
-            } else if (p.fused && d.levels > 0) {
-                add("fused_dw", 0, (long long)d.c * p.fa.nblk, kThreads, (size_t)p.fa.lds_floats * sizeof(float));
+                add("plane_dwl", 0, (long long)d.c * p.la.k, kDwlThreads, (size_t)p.la.lds_floats * sizeof(float),
+                    16 * p.lcfg.CW + p.lcfg.RH);
             } else {
                 for (int l = 1; l <= d.levels; ++l)
                     add("dw_level", l, grid_of(p.lvl[l - 1], d.c), kThreads, lds_bytes(Kind::DwLevel, d.k, p.lvl[l - 1]));
             }
             if (p.dwb) {
-                add("plane_dwb", 0, (long long)d.c * p.ba.k, kDwbThreads, (size_t)p.ba.lds_floats * sizeof(float));
+                add("plane_dwb", 0, (long long)d.c * p.ba.k, kDwbThreads, (size_t)p.ba.lds_floats * sizeof(float),
+                    16 * p.bcfg.CW + p.bcfg.RH);
             } else {
                 Tiling t = p.base;
                 t.VW = vec_width(d.w, d.dtype, aligned_ptr);
@@ -1511,14 +851,12 @@ int wtconv_plan_launches(const wtconv_desc *desc, int op, wtconv_launch *out, in
         }
         add("dw_finalize", 0, (long long)d.c * (d.levels + 1), 128, 0);
     }
-    (void)es;
     const int n = (int)v.size();
     for (int i = 0; i < n && i < max_entries && out; ++i) out[i] = v[i];
     *n_entries = n;
     return WTCONV_OK;
 }
-
-int wtconv_profile_begin(void) {
+WTCONV_API int wtconv_profile_begin(void) {
     std::lock_guard<std::mutex> lock(g_prof_mu);
     for (auto &r : g_prof) {
         g_event_pool.push_back(r.start);
@@ -1529,7 +867,7 @@ int wtconv_profile_begin(void) {
     return WTCONV_OK;
 }
 
-int wtconv_profile_end(wtconv_kernel_time *out, int max_entries, int *n_entries) {
+WTCONV_API int wtconv_profile_end(wtconv_kernel_time *out, int max_entries, int *n_entries) {
     std::lock_guard<std::mutex> lock(g_prof_mu);
     g_prof_on = false;
     std::vector<wtconv_kernel_time> agg;

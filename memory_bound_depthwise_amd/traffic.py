@@ -1,32 +1,41 @@
-"""Algorithmic HBM bytes and FLOPs of every kernel launch of the layer.
+"""Algorithmic HBM bytes and FLOPs of the layer and of every kernel launch.
 
-"Algorithmic" means what each kernel must move and compute by its design, in the
+"Algorithmic" means what each pass must move and compute by its design, in the
 units the paper's I/O model uses ("Fast and Memory-Efficient Wavelet Convolutions
 via I/O-Aware Reformulation", §3.1 Eq. 2 and §4.4 Eq. 10: every tensor a stage
 reads or writes crosses HBM once), with exact element counts including the
 pad-to-even of odd planes.  Parameters, weight-gradient partials and halo
 re-reads are not counted (they are O(C k^2) or cache hits).
 
+Two byte counts are kept apart:
+* `model_bytes`: the per-level pass structure of the paper's fused layer, which
+  the layer's stated bandwidth figure is measured against.  Forward (and the input
+  gradient, the same pipeline on dy): one analysis + filter pass per level (reads
+  the carrier, writes the four filtered bands and, above the deepest level, the
+  next carrier) and one synthesis pass with the base conv fused in (reads x and
+  every level's bands, writes y).  Weight gradient: one pass per level reading the
+  carriers of x and dy (level 1: x and dy themselves, the base gradient fused into
+  it) and writing the next carriers.  For even sizes this is
+  Q_F = 2N + (13/3)N(1-4^-L) - N 4^-L elements per forward-shaped pass and
+  Q_BW = (10/3)N(1-4^-L) - 2N 4^-L for the weight gradient (2N when L = 0).
+* `kernel_cost`: the bytes of the kernels this library actually launches for a
+  shape (the plane-resident kernels move only x in and y out, or x and dy in).
+
+FLOPs are the convolution multiply-adds at 2 FLOP each: per direction (forward,
+input gradient, weight gradient) N k^2 for the base conv plus 4 B_l k^2 for level
+l; the Haar butterflies and the synthesis add a few N of additions, not counted.
+
 Per launch, with E = element size, P = n*C planes, H_l x W_l the level-l grid,
 B_l = P*H_l*W_l coefficient blocks of level l:
-  Plane-resident kernels (the whole pyramid of a plane stays in LDS):
-  fused_fwd,
-  plane_fwd    : read x (N), write y (N).  FLOPs: the per-level kernels' total,
-                 sum_l B_l*(8k^2 + 20) + N*(2k^2 + L).
-  fused_dw,
-  plane_dwl    : read x and dy (2N).  FLOPs: sum_l B_l*(8k^2 + 16).
-  Per-level kernels:
+  plane_fwd    : read x (N), write y (N).  FLOPs: 2 (N k^2 + sum_l 4 B_l k^2).
+  plane_dwl    : read x and dy (2N).  FLOPs: 2 sum_l 4 B_l k^2.
   level_fwd l  : reads the carrier P*H_{l-1}*W_{l-1}; writes Q(l) 4*B_l and,
-                 for l < L, the carrier B_l.
-                 FLOPs: 2*4*k^2 per coefficient block (the conv), 8 (analysis)
-                 and 12 (one-step synthesis) per block.
-  synth        : reads x (N) and every Q(l); writes y (N).
-                 FLOPs: 2*k^2 per pixel (base conv) + L adds.
+                 for l < L, the carrier B_l.  FLOPs: 2 * 4 B_l k^2.
+  synth        : reads x (N) and every Q(l); writes y (N).  FLOPs: 2 N k^2.
   dw_level l   : reads the x and dy carriers (2*P*H_{l-1}*W_{l-1}); writes both
-                 next carriers for l < L.  FLOPs: 2*4*k^2 + 16 per block.
-  Both paths:
+                 next carriers for l < L.  FLOPs: 2 * 4 B_l k^2.
   dw_base,
-  plane_dwb    : read x and dy (2N).  FLOPs: 2*k^2 + 1 per pixel.
+  plane_dwb    : read x and dy (2N).  FLOPs: 2 N k^2.
   dw_finalize  : parameter-sized, counted as 0.
 backward_input launches the same kernels as forward.  Which path a shape takes
 is the library's decision (wtconv_plan_launches); `launches` takes it as flags.
@@ -50,24 +59,25 @@ def kernel_cost(family, level, n, c, h, w, k, levels, elem_bytes):
     E = elem_bytes
     hs, ws = level_sizes(h, w, levels)
     blocks = [P * hs[l] * ws[l] for l in range(levels + 1)]
-    if family in ("fused_fwd", "plane_fwd"):
-        fl = sum(blocks[l] * (8 * k * k + 20) for l in range(1, levels + 1)) + N * (2 * k * k + levels)
-        return E * 2 * N, fl
-    if family in ("fused_dw", "plane_dwl"):
-        return E * 2 * N, sum(blocks[l] * (8 * k * k + 16) for l in range(1, levels + 1))
+    kk = k * k
+    lvl_flops = sum(2 * 4 * blocks[l] * kk for l in range(1, levels + 1))
+    if family == "plane_fwd":
+        return E * 2 * N, 2 * N * kk + lvl_flops
+    if family == "plane_dwl":
+        return E * 2 * N, lvl_flops
     if family == "level_fwd":
         l = level
         elems = blocks[l - 1] + 4 * blocks[l] + (blocks[l] if l < levels else 0)
-        return E * elems, blocks[l] * (8 * k * k + 20)
+        return E * elems, 2 * 4 * blocks[l] * kk
     if family == "synth":
         q = sum(4 * blocks[l] for l in range(1, levels + 1))
-        return E * (2 * N + q), N * (2 * k * k + levels)
+        return E * (2 * N + q), 2 * N * kk
     if family == "dw_level":
         l = level
         elems = 2 * blocks[l - 1] + (2 * blocks[l] if l < levels else 0)
-        return E * elems, blocks[l] * (8 * k * k + 16)
+        return E * elems, 2 * 4 * blocks[l] * kk
     if family in ("dw_base", "plane_dwb"):
-        return E * 2 * N, N * (2 * k * k + 1)
+        return E * 2 * N, 2 * N * kk
     if family == "dw_finalize":
         return 0, 0
     raise ValueError(f"unknown kernel family {family!r}")
@@ -79,29 +89,29 @@ def split_name(name):
     return base.partition("<")[0], int(lvl) if lvl else 0
 
 
-def launches(n, c, h, w, k, levels, elem_bytes, fused_fwd=False, fused_dw=False):
+def launches(n, c, h, w, k, levels, elem_bytes, plane_fwd=False, plane_dw=False):
     """List of (name, pass, bytes, flops) for one forward + input-gradient +
     weight-gradient step of one layer, in launch order; per-level kernels are
     named family#level, as the library's profiling records name them.  The flags
     select the plane-resident kernels for the forward-shaped passes and for the
-    levels' weight gradients."""
+    weight gradients."""
     def one(fam, l, pass_name):
         b, f = kernel_cost(fam, l, n, c, h, w, k, levels, elem_bytes)
         return (f"{fam}#{l}" if l else fam, pass_name, b, f)
 
     out = []
     for pass_name in ("forward", "backward_input"):
-        if fused_fwd:
-            out.append(one("fused_fwd", 0, pass_name))
+        if plane_fwd:
+            out.append(one("plane_fwd", 0, pass_name))
         else:
             out.extend(one("level_fwd", l, pass_name) for l in range(1, levels + 1))
             out.append(one("synth", 0, pass_name))
     if levels > 0:
-        if fused_dw:
-            out.append(one("fused_dw", 0, "backward_weight"))
+        if plane_dw:
+            out.append(one("plane_dwl", 0, "backward_weight"))
         else:
             out.extend(one("dw_level", l, "backward_weight") for l in range(1, levels + 1))
-    out.append(one("dw_base", 0, "backward_weight"))
+    out.append(one("plane_dwb" if plane_dw else "dw_base", 0, "backward_weight"))
     out.append(one("dw_finalize", 0, "backward_weight"))
     return out
 
@@ -116,6 +126,34 @@ def launches_from_plan(n, c, h, w, k, levels, elem_bytes, plan):
             b, f = kernel_cost(fam, l, n, c, h, w, k, levels, elem_bytes)
             out.append((name, pass_name, b, f))
     return out
+
+
+def model_bytes(n, c, h, w, levels, elem_bytes):
+    """Bytes of one forward + input-gradient + weight-gradient step of one layer
+    in the per-level pass structure of the paper's fused layer (module docstring),
+    exact for odd sizes: {"forward", "backward_input", "backward_weight", "step"}."""
+    P = n * c
+    N = P * h * w
+    hs, ws = level_sizes(h, w, levels)
+    blocks = [P * hs[l] * ws[l] for l in range(levels + 1)]
+    fwd = 0
+    for l in range(1, levels + 1):
+        fwd += blocks[l - 1] + 4 * blocks[l] + (blocks[l] if l < levels else 0)
+    fwd += 2 * N + sum(4 * blocks[l] for l in range(1, levels + 1))
+    if levels == 0:
+        bw = 2 * N
+    else:
+        bw = sum(2 * blocks[l - 1] + (2 * blocks[l] if l < levels else 0) for l in range(1, levels + 1))
+    out = {"forward": elem_bytes * fwd, "backward_input": elem_bytes * fwd, "backward_weight": elem_bytes * bw}
+    out["step"] = out["forward"] + out["backward_input"] + out["backward_weight"]
+    return out
+
+
+def conv_flops(n, c, h, w, k, levels):
+    """Convolution FLOPs of one direction (2 per multiply-add): N k^2 + sum_l 4 B_l k^2."""
+    P = n * c
+    hs, ws = level_sizes(h, w, levels)
+    return 2 * k * k * (P * h * w + sum(4 * P * hs[l] * ws[l] for l in range(1, levels + 1)))
 
 
 def step_totals(n, c, h, w, k, levels, elem_bytes, **flags):

@@ -35,7 +35,8 @@ class KernelTime(ctypes.Structure):
 
 class Launch(ctypes.Structure):
     _fields_ = [("name", ctypes.c_char * 64), ("workgroups", ctypes.c_int64),
-                ("threads", ctypes.c_int32), ("lds_bytes", ctypes.c_int32)]
+                ("threads", ctypes.c_int32), ("lds_bytes", ctypes.c_int32),
+                ("variant", ctypes.c_int32), ("reserved", ctypes.c_int32)]
 
 
 class WTConvError(RuntimeError):
@@ -90,7 +91,7 @@ def wtconv_plan_launches(desc: Desc, op: int):
     _check(library().wtconv_plan_launches(ctypes.byref(desc), int(op), arr, 32, ctypes.byref(n)),
            "wtconv_plan_launches")
     return [{"name": arr[i].name.decode(), "workgroups": arr[i].workgroups, "threads": arr[i].threads,
-             "lds_bytes": arr[i].lds_bytes} for i in range(min(n.value, 32))]
+             "lds_bytes": arr[i].lds_bytes, "variant": arr[i].variant} for i in range(min(n.value, 32))]
 
 
 def wtconv_workspace_size(desc: Desc, op: int) -> int:

@@ -126,8 +126,13 @@ def forward(x: np.ndarray, params: dict, levels: int, k: int, return_coeffs: boo
     return y, coeffs
 
 
-def backward(x: np.ndarray, dy: np.ndarray, params: dict, levels: int, k: int) -> dict:
-    """Reverse mode of forward.  Returns dx, dw0, db0, ds0, dwl, dsl (float64)."""
+GRADIENTS = ("dx", "dw0", "db0", "ds0", "dwl", "dsl")
+
+
+def backward(x: np.ndarray, dy: np.ndarray, params: dict, levels: int, k: int, outputs=GRADIENTS) -> dict:
+    """Reverse mode of forward.  Returns dx, dw0, db0, ds0, dwl, dsl (float64);
+    `outputs` names the ones to compute (the others are passed to the C code as
+    NULL, which skips them, and come back as None)."""
     n, C, H, W = x.shape
     L = levels
     xa, xp = _in(x)
@@ -143,9 +148,11 @@ def backward(x: np.ndarray, dy: np.ndarray, params: dict, levels: int, k: int) -
     ds0, ds0p = _out((C,))
     dwl, dwlp = _out((max(L, 1), C, 4, k, k))
     dsl, dslp = _out((max(L, 1), C, 4))
-    rc = _load().wo_backward(n, C, H, W, k, L, xp, gp, w0p, b0p, s0p, wlp, slp,
-                             dxp, dw0p, db0p, ds0p, dwlp, dslp)
+    want = set(outputs)
+    ptrs = {"dx": dxp, "dw0": dw0p, "db0": db0p, "ds0": ds0p, "dwl": dwlp, "dsl": dslp}
+    args = [ptrs[name] if name in want else None for name in GRADIENTS]
+    rc = _load().wo_backward(n, C, H, W, k, L, xp, gp, w0p, b0p, s0p, wlp, slp, *args)
     if rc != 0:
         raise RuntimeError(f"oracle backward failed: {rc}")
-    return {"dx": dx, "dw0": dw0, "db0": db0, "ds0": ds0,
-            "dwl": dwl[:L], "dsl": dsl[:L]}
+    res = {"dx": dx, "dw0": dw0, "db0": db0, "ds0": ds0, "dwl": dwl[:L], "dsl": dsl[:L]}
+    return {name: (res[name] if name in want else None) for name in GRADIENTS}

@@ -1,17 +1,23 @@
 """GPU parity: the HIP library (through its C ABI) against the CPU oracle.
 
-Small shapes are compared element by element on every output; they span several
-tiles, ragged tails, odd sizes (pad-to-even), 1x1 planes, levels 0..5 and k in
-{3, 5, 7}.  The full workload shapes run exactly as the benchmark launches them,
-and are compared on sampled (n, c) planes (forward, input gradient: a plane of the
-output depends only on the same plane of the input) and sampled channels (weight
-gradients: a channel's gradient depends only on that channel of x and dy).
+Every output element is compared, on small shapes and at the full workload sizes
+(run exactly as the benchmark launches them).  The small shapes span several
+tiles, ragged tails, odd sizes (pad-to-even), 1x1 planes, levels 0..5, k in
+{3, 5, 7}, every compiled variant of the plane-resident kernels and both kernel
+families (plane-resident and per-level); tests/test_plan_coverage.py checks that
+list against what the library can launch.
+
+Each comparison reports the normwise error (the stated bar) and the elementwise
+error, and holds every element to the bound the arithmetic of its path allows
+(tests/wtc_harness.py).  With WTC_PARITY_LOG set, the achieved errors are
+appended to that file as JSON lines.
 """
 import numpy as np
 import pytest
 
+from gpu_cases import SMALL, full_cases, small_cases, variant_shapes
 from synthetic import Case, baseline_cases
-from wtc_harness import TOL, compare, gpu_all, oracle_all, rel_err, tol, to_np, torch_act, torch_params
+from wtc_harness import TOL, compare, gpu_all, oracle_all, record, to_np, torch_act, torch_params
 
 pytestmark = pytest.mark.gpu
 
@@ -27,48 +33,23 @@ def _log(msg):
     print(msg, flush=True)
 
 
-SMALL = [
-    # (n, c, h, w, k, L)
-    (2, 3, 16, 16, 5, 2),
-    (2, 3, 37, 45, 5, 3),     # odd sizes, ragged strips
-    (1, 2, 130, 70, 5, 4),    # several tiles per row / column
-    (3, 4, 7, 7, 5, 1),       # 7x7 padded to 8x8
-    (2, 3, 1, 1, 5, 3),       # 1x1 planes at every level
-    (1, 2, 5, 3, 5, 5),
-    (2, 3, 20, 20, 5, 0),     # base path only
-    (2, 2, 33, 17, 3, 3),
-    (2, 2, 29, 31, 7, 2),
-    (5, 6, 9, 14, 5, 4),      # several planes stacked per workgroup
-    (1, 1, 256, 9, 5, 5),     # tall and narrow
-    (1, 1, 9, 200, 5, 5),     # short and wide
-    (1, 2, 9, 255, 7, 2),     # odd width: scalar loads, a staged row wider than a workgroup
-]
+def _fmt(errs):
+    return {k: f"norm {v['norm']:.2e} elem {v['elem']:.2e} bound {v['bound']:.2f}" for k, v in errs.items()}
 
 
-@pytest.mark.parametrize("dtype", ["f32", "bf16", "f16"])
-@pytest.mark.parametrize("shape", SMALL, ids=[f"{s[0]}x{s[1]}x{s[2]}x{s[3]}-k{s[4]}-L{s[5]}" for s in SMALL])
-def test_small_shapes_elementwise(shape, dtype):
+_SMALL = small_cases()
+
+
+@pytest.mark.parametrize("case", _SMALL, ids=[f"{c.n}x{c.c}x{c.h}x{c.w}-k{c.k}-L{c.levels}-{c.dtype}" for c in _SMALL])
+def test_small_shapes_elementwise(case):
     _cuda()
-    n, c, h, w, k, L = shape
-    case = Case(n, c, h, w, k, L, dtype, seed=7, w_std=0.1, b_std=0.05, name="small")
     _log(f"case {case}")
     x, dy, p = case.x(), case.dy(), case.params()
     got = gpu_all(case, x, dy, p)
     want = oracle_all(case, x, dy, p)
     errs = compare(case, got, want)
-    _log(f"  errs {errs}")
-
-
-def test_tiny_config_fp32():
-    """x[1,8,16,16] fp32, kernels N(0, 0.1), zero bias, L=2, seed 0."""
-    _cuda()
-    case = baseline_cases()["tiny"]
-    x, dy, p = case.x(), case.dy(), case.params()
-    got = gpu_all(case, x, dy, p)
-    want = oracle_all(case, x, dy, p)
-    errs = compare(case, got, want)
-    assert errs["y"] <= TOL[("f32", "fwd")]
-    _log(f"tiny errs {errs}")
+    record(case, errs)
+    _log(f"  errs {_fmt(errs)}")
 
 
 def test_no_bias_pointer():
@@ -81,53 +62,22 @@ def test_no_bias_pointer():
     assert got["db0"] is None
 
 
-def _sampled_check(case, planes, channels):
-    """Full-size GPU run in the benchmark's launch configuration; oracle on samples."""
-    import oracle
-    torch = _cuda()
+_FULL = full_cases()
+
+
+@pytest.mark.parametrize("case", _FULL, ids=[c.name for c in _FULL])
+def test_full_size(case):
+    """The full workload shapes, every element of every output against the oracle."""
+    _cuda()
     _log(f"full-size case {case}")
     x, dy, p = case.x(), case.dy(), case.params()
     got = gpu_all(case, x, dy, p)
-    q = {kk: v.astype(np.float64) for kk, v in p.items()}
-    L, k = case.levels, case.k
-    # forward / input gradient on sampled planes
-    for (nn, cc) in planes:
-        qc = {"w0": q["w0"][[cc]], "b0": q["b0"][[cc]], "s0": q["s0"][[cc]],
-              "wl": q["wl"][:, [cc]], "sl": q["sl"][:, [cc]]}
-        xs = x[nn:nn + 1, cc:cc + 1].astype(np.float64)
-        gs = dy[nn:nn + 1, cc:cc + 1].astype(np.float64)
-        y = oracle.forward(xs, qc, L, k)
-        e = rel_err(got["y"][nn:nn + 1, cc:cc + 1], y)
-        assert e <= tol(case, "fwd"), (case, "y", nn, cc, e)
-        qr = dict(qc)
-        qr["b0"] = None
-        dx = oracle.backward(xs, gs, qr, L, k)["dx"]
-        e = rel_err(got["dx"][nn:nn + 1, cc:cc + 1], dx)
-        assert e <= tol(case, "grad"), (case, "dx", nn, cc, e)
-    # weight gradients on sampled channels (all n)
-    qc = {"w0": q["w0"][channels], "b0": q["b0"][channels], "s0": q["s0"][channels],
-          "wl": q["wl"][:, channels], "sl": q["sl"][:, channels]}
-    gw = oracle.backward(x[:, channels].astype(np.float64), dy[:, channels].astype(np.float64), qc, L, k)
-    for key, sl in [("dw0", np.s_[channels]), ("db0", np.s_[channels]), ("ds0", np.s_[channels]),
-                    ("dwl", np.s_[:, channels]), ("dsl", np.s_[:, channels])]:
-        if L == 0 and key in ("dwl", "dsl"):
-            continue
-        e = rel_err(got[key][sl], gw[key])
-        assert e <= tol(case, "grad"), (case, key, e)
-    _log(f"  ok {case}")
-    del torch
-
-
-FULL = ["stage1", "stage2", "stage3", "hires_L1", "hires_L2", "hires_L3", "hires_L4", "hires_L5",
-        "stack_1", "stack_2", "stack_3", "stack_4", "dw5", "dw7", "stage1_f16"]
-
-
-@pytest.mark.parametrize("name", FULL)
-def test_full_size_sampled(name):
-    case = baseline_cases()[name]
-    planes = [(0, 0), (case.n - 1, case.c - 1), (case.n // 2, case.c // 3)]
-    channels = sorted({0, case.c // 2, case.c - 1})
-    _sampled_check(case, planes, channels)
+    want = oracle_all(case, x, dy, p)
+    errs = compare(case, got, want)
+    record(case, errs)
+    if case.name == "tiny":
+        assert errs["y"]["norm"] <= TOL[("f32", "fwd")]
+    _log(f"  ok {case.name}: {_fmt(errs)}")
 
 
 def test_backward_weight_bitwise_deterministic():
@@ -158,6 +108,7 @@ def test_adjoint_on_gpu():
     lhs = float(np.sum(to_np(mv) * g))
     rhs = float(np.sum(v * to_np(mtg)))
     assert abs(lhs - rhs) <= 1e-5 * max(1.0, abs(lhs)), (lhs, rhs)
+    del torch
 
 
 def test_empty_inputs_on_gpu():
@@ -220,3 +171,9 @@ def test_f16_output_rounding_is_rne():
     want = (x.astype(np.float32) * s).astype(np.float32).astype(np.float16).view(np.uint16)
     assert not np.array_equal(want, x.astype(np.float16).view(np.uint16))  # the scale does round
     np.testing.assert_array_equal(got, want)
+
+
+def test_small_list_is_the_shared_one():
+    """The parametrised small cases are the ones the coverage test checks."""
+    assert len(_SMALL) == 3 * (len(SMALL) + len(variant_shapes()))
+    assert set(c.name for c in _FULL) <= set(baseline_cases())
