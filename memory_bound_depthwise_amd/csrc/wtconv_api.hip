@@ -30,6 +30,18 @@ namespace wtc {
 constexpr size_t kLdsBudget = 64 * 1024;   // bytes of LDS per workgroup of the per-level kernels
 constexpr int kDwTargetBlocks = 2048;      // workgroups wanted for the gradient kernels
 constexpr int kPlaneMaxSide = 64;          // largest plane side of the plane-resident kernels
+#ifndef WTC_FWD_PB_CAP
+#define WTC_FWD_PB_CAP 64
+#endif
+#ifndef WTC_DW_PB_CAP
+#define WTC_DW_PB_CAP 64
+#endif
+#ifndef WTC_DW_WG_PER_CU
+#define WTC_DW_WG_PER_CU 4
+#endif
+constexpr int kFwdPbCap = WTC_FWD_PB_CAP;  // planes side by side in one pass of the forward kernel
+constexpr int kDwPbCap = WTC_DW_PB_CAP;    // ... of the weight-gradient kernels
+constexpr int kDwWgPerCu = WTC_DW_WG_PER_CU;  // resident weight-gradient workgroups per CU aimed at
 
 // Reciprocal for udiv16 (exact n / d for n < 2^16, d < 2^15): ceil(2^31 / d).
 inline uint32_t magic31_of(int d) { return (uint32_t)(((1ULL << 31) + (uint64_t)d - 1) / (uint64_t)d); }
@@ -175,33 +187,34 @@ bool tiling_fits(Kind kind, int K, const Tiling &t) { return lds_bytes(kind, K, 
 constexpr int kPlaneLdsBudget = 40960;  // four workgroups per compute unit
 
 
-// Bank cost of 16-byte cell reads by items (strip s, plane p, column j), item t =
+// Bank cost of cell reads by items (strip s, plane p, column j), item t =
 // (s PB + p) W1 + j on lane t, cell s RH sy + p Pw1 + j: gfx950 serves a 16-byte
-// read 16 lanes at a time from 64 banks, conflict-free when the 16 cells are
-// distinct mod 16.  Cost: per group of 16 lanes the largest number of lanes sharing
-// a cell slot mod 16 (1 = conflict-free), summed.
-long long cell_bank_cost(int items, int pb, int W1, int pitch, int RH, int sy) {
+// read 16 lanes at a time from 64 banks (an 8-byte read 32 lanes at a time), so
+// the read is conflict-free when the cells of those lanes are distinct mod 16 (mod
+// 32).  Cost: per group of lanes served together the largest number of them
+// sharing a slot (1 = conflict-free), summed.
+long long cell_bank_cost(int items, int pb, int W1, int pitch, int RH, int sy, int group = 16) {
     long long cost = 0;
     const int per_strip = pb * W1;
-    for (int g = 0; g * 16 < items; ++g) {
-        int cnt[16] = {0};
+    for (int g = 0; g * group < items; ++g) {
+        int cnt[32] = {0};
         int worst = 0;
-        for (int t = g * 16; t < std::min(items, g * 16 + 16); ++t) {
+        for (int t = g * group; t < std::min(items, g * group + group); ++t) {
             const int s = t / per_strip, r = t % per_strip, p = r / W1, j = r % W1;
             const int cell = s * RH * sy + p * pitch + j;
-            worst = std::max(worst, ++cnt[cell & 15]);
+            worst = std::max(worst, ++cnt[cell & (group - 1)]);
         }
         cost += worst;
     }
     return cost;
 }
 
-// Smallest row stride in [lo, lo + 16) with the least bank cost.
-int best_stride(int items, int pb, int W1, int pitch, int RH, int lo) {
+// Smallest row stride in [lo, lo + group) with the least bank cost.
+int best_stride(int items, int pb, int W1, int pitch, int RH, int lo, int group = 16) {
     long long best = -1;
     int sy = lo;
-    for (int cand = lo; cand < lo + 16; ++cand) {
-        const long long cost = cell_bank_cost(items, pb, W1, pitch, RH, cand);
+    for (int cand = lo; cand < lo + group; ++cand) {
+        const long long cost = cell_bank_cost(items, pb, W1, pitch, RH, cand, group);
         if (best < 0 || cost < best) {
             best = cost;
             sy = cand;
@@ -246,7 +259,9 @@ bool plane_layout(const wtconv_desc &d, const PlaneCfg &cfg, int pb, PlaneArgs &
     const int W1s = pb == 1 ? a.W1 : pb * a.Pw1;
     a.commit_items = pb * a.H1 * a.Gw;
     a.final_items = a.S1 * pb * a.W1;
-    if (a.final_items >= 32768 || a.commit_items >= 32768) return false;
+    // one final item per lane (each keeps its filtered bands across the in-place
+    // rebuild of the cells); a single plane of at most 64 x 64 always fits
+    if (a.final_items > kFwdThreads || a.commit_items >= 32768) return false;
     if ((long long)pb * d.c * d.h * d.w >= (1LL << 31)) return false;  // 32-bit offsets from a plane base
     // level-1 arrays: the stride (cells) with the fewest bank conflicts in the final pass
     a.sy1 = best_stride(a.final_items, pb, a.W1, a.Pw1, RH, kPlaneCO + W1s + R);
@@ -277,6 +292,13 @@ bool plane_layout(const wtconv_desc &d, const PlaneCfg &cfg, int pb, PlaneArgs &
     a.zero_floats = (int)fl;
     a.tab = (int)fl;  // deep-level geometry table, filled once per workgroup
     fl += (kPlaneTabFields * std::max(L - 1, 0) + 3) & ~3;
+    // the final pass reads the deep patterns of every item row, also of rows past
+    // the plane (their outputs are discarded): keep those reads in the allocation
+    for (int l = 2; l <= L; ++l) {
+        const int li = l - 2;
+        const long long end = a.offq[li] + (long long)((a.S1 * RH - 1) >> li) * a.sq[li] + ((W1s - 1) >> li) + 1;
+        fl = std::max(fl, (end + 3) & ~3LL);
+    }
     a.lds_floats = (int)fl;
     if (fl * 4 > kPlaneLdsBudget) return false;
     a.m_gw = magic31_of(a.Gw);
@@ -298,7 +320,7 @@ bool plan_plane(const wtconv_desc &d, PlaneArgs &a, PlaneCfg &cfg) {
     const int K = d.k;
     double best = 1e30;
     int best_pb = 0;
-    for (int pb = 1; pb <= std::min(d.n, 64); ++pb) {
+    for (int pb = 1; pb <= std::min(d.n, kFwdPbCap); ++pb) {
         PlaneArgs t{};
         if (!plane_layout(d, cfg, pb, t)) {
             if (pb == 1) return false;
@@ -368,7 +390,7 @@ bool dwb_layout(const wtconv_desc &d, const PlaneCfg &cfg, int pb, PlaneDwbArgs 
 // at most four of two wavefronts each, x 256 compute units), at most one per image
 // group.
 int dw_blocks_per_channel(const wtconv_desc &d, int NG, int lds_floats) {
-    const int per_cu = std::max(1, std::min(4, (160 * 1024) / std::max(1, lds_floats * 4)));
+    const int per_cu = std::max(1, std::min(kDwWgPerCu, (160 * 1024) / std::max(1, lds_floats * 4)));
     return std::max(1, std::min(NG, 256 * per_cu / std::max(1, d.c)));
 }
 
@@ -380,7 +402,7 @@ bool plan_dwb(const wtconv_desc &d, PlaneDwbArgs &a, PlaneCfg &cfg) {
     cfg.CW = d.w % 8 == 0 ? 4 : (d.w % 4 == 0 ? 2 : 1);
     double best = 1e30;
     int best_pb = 0;
-    for (int pb = 1; pb <= std::min(d.n, 64); ++pb) {
+    for (int pb = 1; pb <= std::min(d.n, kDwPbCap); ++pb) {
         PlaneDwbArgs t{};
         if (!dwb_layout(d, cfg, pb, t)) {
             if (pb == 1) return false;
@@ -452,7 +474,9 @@ bool dwl_layout(const wtconv_desc &d, const PlaneCfg &cfg, int pb, PlaneDwlArgs 
         a.hl[li] = hs[l];
         a.wl[li] = pb == 1 ? ws[l] : (pb * a.Pw1) >> (l - 1);
         a.ns[li] = cdiv(hs[l], RHD);
-        const int items = a.ns[li] * a.wl[li];
+        a.wr[li] = ws[l];
+        a.pw[li] = pb == 1 ? ws[l] : a.Pw1 >> (l - 1);
+        const int items = a.ns[li] * pb * a.wr[li];
         if (items >= 32768 || 2LL * hs[l] * a.wl[li] >= 32768) return false;
         a.xs[li] = column_stride(std::max((a.ns[li] - 1) * RHD + 4 * WQ, a.ns[li] * RHD + 2 * R));
         a.xb[li] = a.xs[li] * (a.wl[li] + 2 * R);
@@ -466,6 +490,8 @@ bool dwl_layout(const wtconv_desc &d, const PlaneCfg &cfg, int pb, PlaneDwlArgs 
         a.go[li] = (int)fl;
         fl += 4LL * a.gb[li];
         a.m_wl[li] = magic31_of(a.wl[li]);
+        a.m_row[li] = magic31_of(pb * a.wr[li]);
+        a.m_wr[li] = magic31_of(a.wr[li]);
         a.m_hl[li] = magic31_of(a.hl[li]);
     }
     const int TC = KK <= 24 ? KK : (KK + 1) / 2;  // reduction chunk of the kernel
@@ -480,7 +506,7 @@ bool dwl_layout(const wtconv_desc &d, const PlaneCfg &cfg, int pb, PlaneDwlArgs 
     while (used + 4 <= kDwlThreads) {
         int worst = -1, wl_items = 0;
         for (int l = 0; l < L; ++l) {
-            const int items = a.ns[l] * a.wl[l], per = cdiv(items, M[l]);
+            const int items = a.ns[l] * a.PB * a.wr[l], per = cdiv(items, M[l]);
             if (M[l] < std::min(items, 255) && per > wl_items) {
                 wl_items = per;
                 worst = l;
@@ -511,7 +537,7 @@ int dwl_lane_items(const PlaneDwlArgs &a) {
     for (int t = 0; t < kDwlThreads; ++t) {
         const uint32_t in = a.lane[t];
         const int M = (in >> 16) & 255, l = (int)(in & 15) - 1;
-        if (M) worst = std::max(worst, cdiv(a.ns[l] * a.wl[l], M));
+        if (M) worst = std::max(worst, cdiv(a.ns[l] * a.PB * a.wr[l], M));
     }
     return worst;
 }
@@ -523,7 +549,7 @@ bool plan_dwl(const wtconv_desc &d, PlaneDwlArgs &a, PlaneCfg &cfg) {
     cfg.CW = d.w % 8 == 0 ? 4 : (d.w % 4 == 0 ? 2 : 1);
     double best = 1e30;
     int best_pb = 0;
-    for (int pb = 1; pb <= std::min(d.n, 64); ++pb) {
+    for (int pb = 1; pb <= std::min(d.n, kDwPbCap); ++pb) {
         PlaneDwlArgs t{};
         if (!dwl_layout(d, cfg, pb, t)) {
             if (pb == 1) return false;

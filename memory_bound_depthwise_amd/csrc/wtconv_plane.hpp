@@ -259,11 +259,14 @@ __device__ __forceinline__ void plane_fwd_body(const PlaneArgs &args) {
         t[7] = a0.hl[tid];
     }
 
-    // A unit is PB images of one channel: unit u = (channel u / NG, images
-    // [(u % NG) PB, ...)).  Workgroup w takes units w, w + G, w + 2G, ...
+    // A unit is PB images of one channel: unit u = (channel u % C, images
+    // [(u / C) PB, ...)).  Workgroup w takes units w, w + G, w + 2G, ...; workgroups
+    // running side by side take neighbouring channels of the same images, whose
+    // planes are adjacent in memory (small planes share cache lines).
     auto unit_of = [&](const auto &A, int u, int &c, int &n0) {
-        c = u / A.NG;
-        n0 = (u - c * A.NG) * A.PB;
+        const int g = u / A.C;
+        c = u - g * A.C;
+        n0 = g * A.PB;
     };
     // Patch (p, i, m) of commit item g: plane p, level-1 row i, cell group m.
     auto patch_of = [&](const auto &A, int g, int &p, int &i, int &m) {
@@ -427,78 +430,129 @@ __device__ __forceinline__ void plane_fwd_body(const PlaneArgs &args) {
         if (u + (int)gridDim.x < a.U) prefetch(a, u + gridDim.x);
         T *yb = static_cast<T *>(a.y) + ((size_t)n0 * a.C + c) * HW;
 
-        // 4. level 1 + base conv + deeper patterns, one store per pixel pair
+        // 4. level 1 + base conv + deeper patterns, one store per pixel pair.  Every
+        //    lane owns at most one item (the plan keeps final_items <= kFwdThreads).
+        //    4a filters the four level-1 bands of the item's window into registers;
+        //    once every item has read its window, 4b rewrites the item's own cells in
+        //    place as their pixels (the inverse butterfly, once per cell; 4x, the 1/4
+        //    is in the base weights); 4c runs the base conv on those pixels, adds the
+        //    deeper levels' patterns and the bias, forms the level-1 patterns and
+        //    stores.  Without levels the cells already hold the pixels: only 4c runs.
+        //    Lanes past the last item of a wavefront that has items repeat that item
+        //    (nothing of theirs is written), so that the branches stay uniform.
         {
-            const float bias = smem[a.wt + (4 * L + 1) * KK];
-            auto final_item = [&](int t) __attribute__((always_inline)) {
-                // opaque per item: the weight-table reads stay next to their use
-                const int sy1 = opaque(a.sy1), wt = opaque(a.wt);
-                const int s = udiv16(t, a.m_strip), r = t - s * (PB * a.W1);
-                const int p = udiv16(r, a.m_w1), j = r - p * a.W1;
-                const int col = p * a.Pw1 + j, row0 = s * RH;
-                float z[4][RH], P[2][2][RH];
+            const bool has = tid < a.final_items;
+            const int wave_has = __builtin_amdgcn_readfirstlane((tid & ~(kWave - 1)) < a.final_items ? 1 : 0);
+            const int t = min(tid, a.final_items - 1);
+            const int sy1 = opaque(a.sy1), wt = opaque(a.wt);
+            const int s = udiv16(t, a.m_strip), r = t - s * (PB * a.W1);
+            const int p = udiv16(r, a.m_w1), j = r - p * a.W1;
+            const int col = p * a.Pw1 + j, row0 = s * RH;
+            float z[4][RH];
+            if constexpr (!kBase) {
+                if (wave_has) {
+                    // window cell (t, v) is level-1 cell (row0 - R + t, col - R + v)
+                    const float4 *win = s4 + row0 * sy1 + col + kPlaneCO - R;
+                    const float4 *wt1 = s4 + (wt >> 2);
+                    {  // tap column 0 starts the sums (no cleared accumulators)
+                        float4 wb[K];
 #pragma unroll
-                for (int i = 0; i < RH; ++i)
+                        for (int u = 0; u < K; ++u) wb[u] = wt1[u];
+                        float4 cl[RH + K - 1];
 #pragma unroll
-                    for (int b = 0; b < 4; ++b) z[b][i] = 0.f;
-                // window cell (t, v) is level-1 cell (row0 - R + t, col - R + v)
-                const float4 *win = s4 + row0 * sy1 + col + kPlaneCO - R;
-                const float4 *wt1 = s4 + (wt >> 2);
-#pragma unroll 1
-                for (int v = 0; v < (kBase ? 0 : K); ++v) {  // rolled: see conv_bands
-                    float4 wb[K];
-#pragma unroll
-                    for (int u = 0; u < K; ++u) wb[u] = wt1[v * K + u];
-                    float4 cl[RH + K - 1];
-#pragma unroll
-                    for (int tt = 0; tt < RH + K - 1; ++tt) cl[tt] = win[tt * sy1 + v];
-#pragma unroll
-                    for (int u = 0; u < K; ++u)
+                        for (int tt = 0; tt < RH + K - 1; ++tt) cl[tt] = win[tt * sy1];
 #pragma unroll
                         for (int i = 0; i < RH; ++i) {
-                            z[0][i] = fmaf(wb[u].x, cl[i + u].x, z[0][i]);
-                            z[1][i] = fmaf(wb[u].y, cl[i + u].y, z[1][i]);
-                            z[2][i] = fmaf(wb[u].z, cl[i + u].z, z[2][i]);
-                            z[3][i] = fmaf(wb[u].w, cl[i + u].w, z[3][i]);
+                            z[0][i] = wb[0].x * cl[i].x;
+                            z[1][i] = wb[0].y * cl[i].y;
+                            z[2][i] = wb[0].z * cl[i].z;
+                            z[3][i] = wb[0].w * cl[i].w;
                         }
-                }
-                // deeper levels' patterns and the bias enter through the low-pass band
 #pragma unroll
-                for (int i = 0; i < RH; ++i) {
-                    float tv = bias;
-                    const int r1 = min(row0 + i, a.H1 - 1);
-                    for (int l = 2; l <= L; ++l)
-                        tv += smem[a.offq[l - 2] + (r1 >> (l - 2)) * a.sq[l - 2] + (col >> (l - 2))];
-                    z[0][i] += tv;
-                }
-                // level-1 synthesis: slot (ry, rx) = LL +- LH +- HL +- HH
+                        for (int u = 1; u < K; ++u)
 #pragma unroll
-                for (int i = 0; i < RH; ++i) {
-                    const float a0v = z[0][i] + z[1][i], a1v = z[0][i] - z[1][i];
-                    const float b0 = z[2][i] + z[3][i], b1 = z[2][i] - z[3][i];
-                    P[0][0][i] = a0v + b0;
-                    P[0][1][i] = a0v - b0;
-                    P[1][0][i] = a1v + b1;
-                    P[1][1][i] = a1v - b1;
+                            for (int i = 0; i < RH; ++i) {
+                                z[0][i] = fmaf(wb[u].x, cl[i + u].x, z[0][i]);
+                                z[1][i] = fmaf(wb[u].y, cl[i + u].y, z[1][i]);
+                                z[2][i] = fmaf(wb[u].z, cl[i + u].z, z[2][i]);
+                                z[3][i] = fmaf(wb[u].w, cl[i + u].w, z[3][i]);
+                            }
+                    }
+#pragma unroll 1
+                    for (int v = 1; v < K; ++v) {  // rolled: see conv_bands
+                        float4 wb[K];
+#pragma unroll
+                        for (int u = 0; u < K; ++u) wb[u] = wt1[v * K + u];
+                        float4 cl[RH + K - 1];
+#pragma unroll
+                        for (int tt = 0; tt < RH + K - 1; ++tt) cl[tt] = win[tt * sy1 + v];
+#pragma unroll
+                        for (int u = 0; u < K; ++u)
+#pragma unroll
+                            for (int i = 0; i < RH; ++i) {
+                                z[0][i] = fmaf(wb[u].x, cl[i + u].x, z[0][i]);
+                                z[1][i] = fmaf(wb[u].y, cl[i + u].y, z[1][i]);
+                                z[2][i] = fmaf(wb[u].z, cl[i + u].z, z[2][i]);
+                                z[3][i] = fmaf(wb[u].w, cl[i + u].w, z[3][i]);
+                            }
+                    }
+                }
+                __syncthreads();  // every window is read: the bands may be overwritten
+                if (has) {
+                    float4 *own = s4 + (row0 + R) * sy1 + col + kPlaneCO;
+#pragma unroll
+                    for (int i = 0; i < RH; ++i) {
+                        const float4 c4 = own[i * sy1];
+                        const float A = c4.x + c4.y, B = c4.x - c4.y, C = c4.z + c4.w, D = c4.z - c4.w;
+                        own[i * sy1] = make_float4(A + C, A - C, B + D, B - D);
+                    }
+                }
+                __syncthreads();  // every cell holds its pixels
+            }
+            const float bias = smem[a.wt + (4 * L + 1) * KK];
+            if (wave_has) {
+                float P[2][2][RH];
+                if constexpr (kBase) {
+#pragma unroll
+                    for (int i = 0; i < RH; ++i) {
+                        P[0][0][i] = P[0][1][i] = P[1][0][i] = P[1][1][i] = bias;
+                    }
+                } else {
+                    // deeper levels' patterns and the bias enter through the low-pass
+                    // band; rows past the plane read padding (their outputs are not stored)
+                    // (summed apart from z, so that the level loop carries only them)
+                    float dz[RH];
+#pragma unroll
+                    for (int i = 0; i < RH; ++i) dz[i] = bias;
+                    for (int l = 2; l <= L; ++l) {
+                        const int sh = l - 2, sq = a.sq[sh];
+                        const float *qc = smem + a.offq[sh] + (col >> sh);
+#pragma unroll
+                        for (int i = 0; i < RH; ++i) dz[i] += qc[__umul24((row0 + i) >> sh, sq)];
+                    }
+#pragma unroll
+                    for (int i = 0; i < RH; ++i) z[0][i] += dz[i];
+                    // level-1 synthesis: slot (ry, rx) = LL +- LH +- HL +- HH
+#pragma unroll
+                    for (int i = 0; i < RH; ++i) {
+                        const float a0v = z[0][i] + z[1][i], a1v = z[0][i] - z[1][i];
+                        const float b0 = z[2][i] + z[3][i], b1 = z[2][i] - z[3][i];
+                        P[0][0][i] = a0v + b0;
+                        P[0][1][i] = a0v - b0;
+                        P[1][0][i] = a1v + b1;
+                        P[1][1][i] = a1v - b1;
+                    }
                 }
                 // base conv onto the patterns: output (2i+ry, 2j+rx), tap (u, w) reads
                 // pixel (2i+ry+u-R, 2j+rx+w-R), i.e. component (py, px) of cell
-                // (i + di, j + dj); x is rebuilt from the cell's bands
+                // (i + di, j + dj)
                 const float4 *xwin = s4 + (row0 + R - RC) * sy1 + col + kPlaneCO;
                 const float *w0 = smem + wt + 4 * L * KK;
 #pragma unroll 1
                 for (int dj = -RC; dj <= RC; ++dj) {  // rolled: see conv_bands
-                    float4 xq[RH + 2 * RC];  // 4 x (x00, x01, x10, x11) by the inverse butterfly
+                    float4 xq[RH + 2 * RC];  // (x00, x01, x10, x11) of each cell
 #pragma unroll
-                    for (int tt = 0; tt < RH + 2 * RC; ++tt) {
-                        const float4 c4 = xwin[tt * sy1 + dj];
-                        if constexpr (kBase) {
-                            xq[tt] = c4;
-                        } else {
-                            const float A = c4.x + c4.y, B = c4.x - c4.y, C = c4.z + c4.w, D = c4.z - c4.w;
-                            xq[tt] = make_float4(A + C, A - C, B + D, B - D);
-                        }
-                    }
+                    for (int tt = 0; tt < RH + 2 * RC; ++tt) xq[tt] = xwin[tt * sy1 + dj];
 #pragma unroll
                     for (int px = 0; px < 2; ++px)
 #pragma unroll
@@ -526,16 +580,14 @@ __device__ __forceinline__ void plane_fwd_body(const PlaneArgs &args) {
                                     }
                         }
                 }
-                if (p < live) {
-                    T *yp = yb + (p * CHW + 2 * j);
+                if (has && p < live) {
+                    const int nr = H - 2 * row0;  // pixel rows of the item inside the plane
+                    T *dst = yb + (p * CHW + 2 * row0 * W + 2 * j);
 #pragma unroll
                     for (int i = 0; i < RH; ++i) {
-                        if (row0 + i >= a.H1) break;
 #pragma unroll
-                        for (int ry = 0; ry < 2; ++ry) {
-                            const int pr = 2 * (row0 + i) + ry;
-                            if (pr >= H) break;
-                            T *dst = yp + pr * W;
+                        for (int ry = 0; ry < 2; ++ry, dst += W) {
+                            if (2 * i + ry >= nr) break;
                             if (a.pair_store) {
                                 if constexpr (kHalf<T>)
                                     *reinterpret_cast<uint32_t *>(dst) = Act<T>::pack(P[ry][0][i], P[ry][1][i]);
@@ -548,8 +600,7 @@ __device__ __forceinline__ void plane_fwd_body(const PlaneArgs &args) {
                         }
                     }
                 }
-            };
-            for (int t = tid; t < a.final_items; t += NT) final_item(t);
+            }
         }
     }
 }

@@ -14,8 +14,10 @@
 // same for dy (no halo).  Small planes sit side by side, PB per pass, with zero
 // cells between them.
 //
-// Workgroup (c, r) of the k workgroups of channel c walks the image groups
-// [r NG / k, (r + 1) NG / k) of that channel, PB images per pass:
+// Workgroup r C + c, the r-th of the k workgroups of channel c, walks the image
+// groups [r NG / k, (r + 1) NG / k) of that channel, PB images per pass (workgroups
+// running side by side take neighbouring channels of the same images, whose planes
+// are adjacent in memory):
 //   1. commit the prefetched 2 x 2CW pixel patches of x and dy as cells; issue the
 //      loads of the next pass;
 //   2. one item is one cell column x RH cell rows (2 x 2RH pixels of dy): the lane
@@ -64,7 +66,8 @@ __global__ __launch_bounds__(kDwbThreads, 2) void plane_dwb_kernel(PlaneDwbArgs 
     constexpr int SLOTS = kPlaneMaxWords / (2 * IO::kWords) > 0 ? kPlaneMaxWords / (2 * IO::kWords) : 1;
     extern __shared__ float smem[];
     float4 *s4 = reinterpret_cast<float4 *>(smem);
-    const int c = blockIdx.x / a.k, r = blockIdx.x - c * a.k;
+    // neighbouring workgroups take neighbouring channels of the same images
+    const int r = blockIdx.x / a.C, c = blockIdx.x - r * a.C;
     const int g_begin = (int)((long long)r * a.NG / a.k), g_end = (int)((long long)(r + 1) * a.NG / a.k);
     const int tid = threadIdx.x, PB = a.PB;
     const int HW = a.H * a.W, CHW = a.C * HW;
@@ -243,10 +246,12 @@ struct PlaneDwlArgs {
     // of x: element (row r, column j) at xo + b xb + (j + R) xs + (r + R); of dy:
     // go + b gb + j gs + r.  Strides and offsets are multiples of 4 floats.
     int hl[kMaxLevels], wl[kMaxLevels];    // rows, width
+    int wr[kMaxLevels], pw[kMaxLevels];    // width of one plane, column pitch between planes
     int ns[kMaxLevels];                    // strips of RHD rows
     int xs[kMaxLevels], xb[kMaxLevels], xo[kMaxLevels];  // x: column stride, band size, offset (floats)
     int gs[kMaxLevels], gb[kMaxLevels], go[kMaxLevels];  // dy: the same
     uint32_t m_wl[kMaxLevels], m_hl[kMaxLevels];          // udiv16 reciprocals of wl, hl
+    uint32_t m_row[kMaxLevels], m_wr[kMaxLevels];         // ... of PB wr (items per strip), wr
     uint32_t lane[kDwlThreads];            // level (bits 0-3) | band (4-5) | index in group (8-15) | lanes in group (16-23)
     int groups;                            // (level, band) groups in use: 4 L
     int lane0[kMaxLevels], lanes[kMaxLevels];  // level l: first lane of band 0, lanes per band
@@ -263,7 +268,8 @@ __global__ __launch_bounds__(kDwlThreads, 3) void plane_dwl_kernel(PlaneDwlArgs 
     using IO = PatchIO<T, CW>;
     constexpr int SLOTS = kPlaneMaxWords / (2 * IO::kWords) > 0 ? kPlaneMaxWords / (2 * IO::kWords) : 1;
     extern __shared__ float smem[];
-    const int c = blockIdx.x / a.k, r = blockIdx.x - c * a.k;
+    // neighbouring workgroups take neighbouring channels of the same images
+    const int r = blockIdx.x / a.C, c = blockIdx.x - r * a.C;
     const int g_begin = (int)((long long)r * a.NG / a.k), g_end = (int)((long long)(r + 1) * a.NG / a.k);
     const int tid = threadIdx.x, PB = a.PB, L = a.L;
     const int HW = a.H * a.W, CHW = a.C * HW;
@@ -320,8 +326,10 @@ __global__ __launch_bounds__(kDwlThreads, 3) void plane_dwl_kernel(PlaneDwlArgs 
     // the lane's item geometry, fixed for the kernel (the level differs between
     // lanes of a wavefront, so it is looked up once, not per item)
     const int li0 = gM > 0 ? lv - 1 : 0;
-    const int it_w = a.wl[li0], it_end = gM > 0 ? a.ns[li0] * it_w : 0;
-    const uint32_t it_mw = a.m_wl[li0];
+    // items cover the planes' own columns (not the zero columns between planes)
+    const int it_wr = a.wr[li0], it_row = PB * it_wr, it_pw = a.pw[li0];
+    const int it_end = gM > 0 ? a.ns[li0] * it_row : 0;
+    const uint32_t it_mrow = a.m_row[li0], it_mwr = a.m_wr[li0];
     const int it_xs = a.xs[li0], it_gs = a.gs[li0];
     const int it_x = a.xo[li0] + band * a.xb[li0], it_g = a.go[li0] + band * a.gb[li0];
     float acc[KK];
@@ -393,7 +401,8 @@ __global__ __launch_bounds__(kDwlThreads, 3) void plane_dwl_kernel(PlaneDwlArgs 
         // this lane's items: column j x RHD rows of (level lv, band)
         if (gM > 0) {
             for (int it = gm; it < it_end; it += gM) {
-                const int s = udiv16(it, it_mw), j = it - s * it_w;
+                const int s = udiv16(it, it_mrow), rem = it - s * it_row;
+                const int p = udiv16(rem, it_mwr), j = p * it_pw + (rem - p * it_wr);
                 // dy rows s RHD .. + RHD of column j; x window rows s RHD - R ..,
                 // columns j - R .. j + R (storage column j + v, row s RHD + t)
                 const float4 *gcol = reinterpret_cast<const float4 *>(smem + it_g + j * it_gs + s * RHD);

@@ -26,6 +26,9 @@ SMALL = [
     (6, 4, 8, 8, 5, 2),       # item strips of 4 rows
     (2, 3, 56, 20, 5, 2),     # item strips of 7 rows, CW = 2
     (2, 2, 70, 66, 3, 2),     # k = 3 on the per-level kernels
+    (24, 2, 14, 14, 5, 1),    # many planes side by side in one pass (arrays whose size is not a multiple of 4)
+    (40, 2, 7, 7, 5, 1),      # the same for 7 x 7 planes
+    (12, 2, 28, 28, 5, 2),    # several 28 x 28 planes per pass, two levels
 ]
 DTYPES = ["f32", "bf16", "f16"]
 
