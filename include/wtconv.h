@@ -78,7 +78,9 @@ enum wtconv_status {
     WTCONV_ERR_WORKSPACE = -6, /* workspace NULL or smaller than wtconv_workspace_size */
     WTCONV_ERR_ALIGN = -7,     /* a pointer is not aligned to its element size */
     WTCONV_ERR_OP = -8,        /* unknown wtconv_op */
-    WTCONV_ERR_HIP = -9        /* a kernel launch failed */
+    WTCONV_ERR_HIP = -9,       /* a kernel launch failed */
+    WTCONV_ERR_SCRATCH = -10   /* wtconv_backward_weight_noalloc: the shape needs more workspace
+                                  than WTCONV_STATIC_SCRATCH_BYTES */
 };
 
 /* Shape of one layer call.  An empty tensor (any of n, c, h, w equal to 0) is
@@ -133,6 +135,30 @@ WTCONV_API int wtconv_backward_weight(const wtconv_desc *desc, const void *x, co
                            const float *b0, const float *s0, const float *wl, const float *sl,
                            float *dw0, float *db0, float *ds0, float *dwl, float *dsl,
                            void *workspace, size_t workspace_bytes, void *stream);
+
+/* Bytes of the library's static device scratch used by
+ * wtconv_backward_weight_noalloc (one array per device, held until the process
+ * ends). */
+#define WTCONV_STATIC_SCRATCH_BYTES (16u << 20)
+
+/* wtconv_backward_weight without a caller workspace, for callers that cannot
+ * allocate device memory (code under HIP graph capture, tight serving loops,
+ * harnesses that forbid allocation).  Same arguments (minus the workspace), kernels
+ * and results as wtconv_backward_weight; its workspace is a static array of
+ * WTCONV_STATIC_SCRATCH_BYTES per device inside the library (the device address is
+ * looked up once per device, on its first call there).  No allocation happens in
+ * the call.  A shape whose weight-gradient workspace (wtconv_workspace_size with
+ * WTCONV_OP_BACKWARD_WEIGHT) exceeds WTCONV_STATIC_SCRATCH_BYTES is refused with
+ * WTCONV_ERR_SCRATCH before anything is enqueued; every shape that the
+ * plane-resident kernels handle at ordinary channel counts fits.  All calls on one
+ * device share its array: calls that overlap in time on that device (different
+ * streams, or host threads without ordering) race and give wrong results; calls
+ * ordered on one stream are safe.  Nothing in the array needs clearing between
+ * calls (each call writes every value it reads). */
+WTCONV_API int wtconv_backward_weight_noalloc(const wtconv_desc *desc, const void *x, const void *dy,
+                                              const float *w0, const float *b0, const float *s0, const float *wl,
+                                              const float *sl, float *dw0, float *db0, float *ds0, float *dwl,
+                                              float *dsl, void *stream);
 
 /* Launch plan of an operation for this shape, assuming activation pointers aligned
  * to 16 bytes (as device allocations are): one entry per kernel launch the call

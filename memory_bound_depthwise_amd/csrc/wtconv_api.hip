@@ -744,6 +744,63 @@ int fwd_common(const wtconv_desc *desc, const void *in, const float *w0, const f
 }  // namespace
 }  // namespace wtc
 
+// The allocation-free entry point's workspace (see scratch_ptr below).
+static __device__ __align__(256) unsigned char scratch[WTCONV_STATIC_SCRATCH_BYTES];
+
+namespace wtc {
+namespace {
+
+// Checks shared by the weight-gradient entry points (everything but the workspace).
+int check_backward_weight(const wtconv_desc *desc, const void *x, const void *dy, const float *w0, const float *b0,
+                          const float *s0, const float *wl, const float *sl, const float *dw0, const float *db0,
+                          const float *ds0, const float *dwl, const float *dsl) {
+    int rc = check_desc(desc);
+    if (rc) return rc;
+    const wtconv_desc &d = *desc;
+    if (d.c == 0) return WTCONV_OK;
+    if (!w0 || !s0 || !dw0 || !ds0 || (d.levels > 0 && (!wl || !sl || !dwl || !dsl))) return WTCONV_ERR_NULL;
+    if (!empty(d) && (!x || !dy)) return WTCONV_ERR_NULL;
+    const size_t es = elem_size(d.dtype);
+    if ((x && !aligned(x, es)) || (dy && !aligned(dy, es)) || !aligned(w0, 4) || !aligned(s0, 4) ||
+        !aligned(dw0, 4) || !aligned(ds0, 4) || (b0 && !aligned(b0, 4)) || (db0 && !aligned(db0, 4)) ||
+        (wl && !aligned(wl, 4)) || (sl && !aligned(sl, 4)) || (dwl && !aligned(dwl, 4)) ||
+        (dsl && !aligned(dsl, 4)))
+        return WTCONV_ERR_ALIGN;
+    return WTCONV_OK;
+}
+
+// The allocation-free entry point's workspace: one array per device, held until
+// the process ends.  Host code never uses `scratch` itself (on the host it names a
+// stand-in, not device memory): its device address is taken once per device with
+// hipGetSymbolAddress and kept in scratch_ptr.
+constexpr size_t kScratchBytes = WTCONV_STATIC_SCRATCH_BYTES;
+
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void *g_scratch_ptr[kMaxDevices] = {};
+
+// Device address of the current device's scratch array (nullptr on failure).
+void *scratch_ptr() {
+    int dev = -1;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= kMaxDevices) {
+        (void)hipGetLastError();
+        return nullptr;
+    }
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (!g_scratch_ptr[dev]) {
+        void *p = nullptr;
+        if (hipGetSymbolAddress(&p, HIP_SYMBOL(scratch)) != hipSuccess || !p) {
+            (void)hipGetLastError();
+            return nullptr;
+        }
+        g_scratch_ptr[dev] = p;
+    }
+    return g_scratch_ptr[dev];
+}
+
+}  // namespace
+}  // namespace wtc
+
 using namespace wtc;
 
 extern "C" {
@@ -762,6 +819,7 @@ WTCONV_API const char *wtconv_status_string(int status) {
         case WTCONV_ERR_ALIGN: return "misaligned pointer";
         case WTCONV_ERR_OP: return "unknown operation";
         case WTCONV_ERR_HIP: return "HIP kernel launch failed";
+        case WTCONV_ERR_SCRATCH: return "shape needs more workspace than the library's static scratch holds";
         default: return "unknown status";
     }
 }
@@ -797,24 +855,30 @@ WTCONV_API int wtconv_backward_weight(const wtconv_desc *desc, const void *x, co
                                       const float *b0, const float *s0, const float *wl, const float *sl,
                                       float *dw0, float *db0, float *ds0, float *dwl, float *dsl, void *workspace,
                                       size_t workspace_bytes, void *stream) {
-    int rc = check_desc(desc);
-    if (rc) return rc;
+    int rc = check_backward_weight(desc, x, dy, w0, b0, s0, wl, sl, dw0, db0, ds0, dwl, dsl);
+    if (rc || desc->c == 0) return rc;
     const wtconv_desc &d = *desc;
-    if (d.c == 0) return WTCONV_OK;
-    if (!w0 || !s0 || !dw0 || !ds0 || (d.levels > 0 && (!wl || !sl || !dwl || !dsl))) return WTCONV_ERR_NULL;
-    if (!empty(d) && (!x || !dy)) return WTCONV_ERR_NULL;
-    const size_t es = elem_size(d.dtype);
-    if ((x && !aligned(x, es)) || (dy && !aligned(dy, es)) || !aligned(w0, 4) || !aligned(s0, 4) ||
-        !aligned(dw0, 4) || !aligned(ds0, 4) || (b0 && !aligned(b0, 4)) || (db0 && !aligned(db0, 4)) ||
-        (wl && !aligned(wl, 4)) || (sl && !aligned(sl, 4)) || (dwl && !aligned(dwl, 4)) ||
-        (dsl && !aligned(dsl, 4)))
-        return WTCONV_ERR_ALIGN;
     const auto ps = plans_for(d);
     if (ps->dp.bytes > 0 && (!workspace || workspace_bytes < ps->dp.bytes)) return WTCONV_ERR_WORKSPACE;
     if (workspace && !aligned(workspace, 16)) return WTCONV_ERR_ALIGN;
     hipStream_t st = static_cast<hipStream_t>(stream);
     WTC_DISPATCH(d.k, d.dtype, run_backward_weight, *ps, x, dy, w0, b0, s0, wl, sl, dw0, db0, ds0, dwl, dsl,
                  static_cast<char *>(workspace), st);
+}
+
+WTCONV_API int wtconv_backward_weight_noalloc(const wtconv_desc *desc, const void *x, const void *dy,
+                                              const float *w0, const float *b0, const float *s0, const float *wl,
+                                              const float *sl, float *dw0, float *db0, float *ds0, float *dwl,
+                                              float *dsl, void *stream) {
+    int rc = check_backward_weight(desc, x, dy, w0, b0, s0, wl, sl, dw0, db0, ds0, dwl, dsl);
+    if (rc || desc->c == 0) return rc;
+    const wtconv_desc &d = *desc;
+    const auto ps = plans_for(d);
+    if (ps->dp.bytes > kScratchBytes) return WTCONV_ERR_SCRATCH;
+    char *ws = static_cast<char *>(scratch_ptr());
+    if (!ws) return WTCONV_ERR_HIP;
+    hipStream_t st = static_cast<hipStream_t>(stream);
+    WTC_DISPATCH(d.k, d.dtype, run_backward_weight, *ps, x, dy, w0, b0, s0, wl, sl, dw0, db0, ds0, dwl, dsl, ws, st);
 }
 
 WTCONV_API int wtconv_plan_launches(const wtconv_desc *desc, int op, wtconv_launch *out, int max_entries,

@@ -18,7 +18,8 @@ MAX_LEVELS = 8
 
 EXPORTED = ["wtconv_workspace_size", "wtconv_forward", "wtconv_backward_input",
             "wtconv_backward_weight", "wtconv_status_string", "wtconv_version",
-            "wtconv_profile_begin", "wtconv_profile_end", "wtconv_plan_launches"]
+            "wtconv_profile_begin", "wtconv_profile_end", "wtconv_plan_launches",
+            "wtconv_backward_weight_noalloc"]
 
 
 class Desc(ctypes.Structure):
@@ -60,6 +61,7 @@ def library():
         lib.wtconv_backward_input.argtypes = [dp, vp, fp, fp, fp, fp, vp, vp, ctypes.c_size_t, vp]
         lib.wtconv_backward_weight.argtypes = [dp, vp, vp, fp, fp, fp, fp, fp, fp, fp, fp, fp, fp,
                                                vp, ctypes.c_size_t, vp]
+        lib.wtconv_backward_weight_noalloc.argtypes = [dp, vp, vp, fp, fp, fp, fp, fp, fp, fp, fp, fp, fp, vp]
         lib.wtconv_status_string.argtypes = [i32]
         lib.wtconv_status_string.restype = ctypes.c_char_p
         lib.wtconv_version.argtypes = []
@@ -230,6 +232,28 @@ def wtconv_backward_weight(x, dy, w0, b0, s0, wl, sl, levels: int, out=None, wor
         _ptr(ws), wsb, _stream(dev))
     _check(rc, "wtconv_backward_weight")
     return out
+
+
+def wtconv_backward_weight_noalloc(x, dy, w0, b0, s0, wl, sl, levels: int, out):
+    """wtconv_backward_weight through the allocation-free entry point (the library's
+    static device scratch instead of a workspace).  `out` holds the preallocated
+    float32 gradients (keys as wtconv_backward_weight returns); nothing is allocated."""
+    n, C, H, W = x.shape
+    k = w0.shape[-1]
+    _check_tensor(x, "x", x.device)
+    _check_tensor(dy, "dy", x.device, x.dtype, x.shape)
+    _param_checks(x.device, C, k, levels, w0, b0, s0, wl, sl)
+    desc = make_desc(n, C, H, W, k, levels, _dtype_code(x))
+    rc = library().wtconv_backward_weight_noalloc(
+        ctypes.byref(desc), _ptr(x), _ptr(dy), _ptr(w0), _ptr(b0), _ptr(s0),
+        _ptr(wl if levels else None), _ptr(sl if levels else None),
+        _ptr(out["dw0"]), _ptr(out["db0"]), _ptr(out["ds0"]),
+        _ptr(out["dwl"] if levels else None), _ptr(out["dsl"] if levels else None), _stream(x.device))
+    _check(rc, "wtconv_backward_weight_noalloc")
+    return out
+
+
+STATIC_SCRATCH_BYTES = 16 << 20  # WTCONV_STATIC_SCRATCH_BYTES
 
 
 def profile_begin():

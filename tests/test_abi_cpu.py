@@ -14,7 +14,8 @@ from memory_bound_depthwise_amd import wtconv as binding
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "wtconv.h")
 
-OK, E_SHAPE, E_KERNEL, E_LEVELS, E_DTYPE, E_NULL, E_WS, E_ALIGN, E_OP, E_HIP = 0, -1, -2, -3, -4, -5, -6, -7, -8, -9
+OK, E_SHAPE, E_KERNEL, E_LEVELS, E_DTYPE, E_NULL, E_WS, E_ALIGN, E_OP, E_HIP, E_SCRATCH = (
+    0, -1, -2, -3, -4, -5, -6, -7, -8, -9, -10)
 
 
 def _declared_functions():
@@ -40,7 +41,7 @@ def test_library_exports_every_declared_symbol():
 
 def test_status_strings():
     lib = wt.library()
-    for code in [OK, E_SHAPE, E_KERNEL, E_LEVELS, E_DTYPE, E_NULL, E_WS, E_ALIGN, E_OP, E_HIP]:
+    for code in [OK, E_SHAPE, E_KERNEL, E_LEVELS, E_DTYPE, E_NULL, E_WS, E_ALIGN, E_OP, E_HIP, E_SCRATCH]:
         s = lib.wtconv_status_string(code).decode()
         assert s and s != "unknown status"
     assert lib.wtconv_status_string(12345).decode() == "unknown status"
@@ -193,3 +194,28 @@ def test_launch_plan_query():
     n = ctypes.c_int(-1)
     assert wt.library().wtconv_plan_launches(ctypes.byref(d), 7, None, 0, ctypes.byref(n)) == E_OP
     assert wt.library().wtconv_plan_launches(ctypes.byref(d), 0, None, 0, None) == E_NULL
+
+
+@needs_no_gpu
+def test_noalloc_refuses_shapes_beyond_the_static_scratch():
+    """The allocation-free weight gradient checks its arguments like the workspace
+    variant and refuses a shape whose workspace exceeds the static scratch before
+    anything is enqueued (or the scratch address is looked up)."""
+    lib = wt.library()
+    f = lambda desc, **kw: lib.wtconv_backward_weight_noalloc(
+        ctypes.byref(desc), kw.get("x", P), kw.get("dy", P), P, P, P, P, P, P, P, P, P, P, None)
+    big = wt.make_desc(8, 128, 256, 256, 5, 3, wt.BF16)  # per-level kernels: carriers of x and dy
+    assert wt.wtconv_workspace_size(big, wt.OP_BACKWARD_WEIGHT) > wt.STATIC_SCRATCH_BYTES
+    assert f(big) == E_SCRATCH
+    small = wt.make_desc(2, 3, 16, 16, 5, 2, wt.BF16)
+    assert f(small, x=None) == E_NULL
+    assert f(small, dy=P_ODD) == E_ALIGN
+    d = wt.make_desc(2, 3, 16, 16, 5, 9, wt.BF16)
+    assert f(d) == E_LEVELS
+    # every workload of the layer study fits
+    from synthetic import baseline_cases
+    code = {"f32": wt.F32, "bf16": wt.BF16, "f16": wt.F16}
+    for c in baseline_cases().values():
+        if c.h <= 64 and c.w <= 64:
+            d = wt.make_desc(c.n, c.c, c.h, c.w, c.k, c.levels, code[c.dtype])
+            assert wt.wtconv_workspace_size(d, wt.OP_BACKWARD_WEIGHT) <= wt.STATIC_SCRATCH_BYTES, c
