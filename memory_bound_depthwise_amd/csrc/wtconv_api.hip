@@ -375,7 +375,7 @@ bool dwb_layout(const wtconv_desc &d, const PlaneCfg &cfg, int pb, PlaneDwbArgs 
     a.ax = (a.S1 * RH + 2 * RC) * a.sx;
     a.sd = best_stride(a.final_items, pb, a.W1, a.Pw1, RH, W1s);
     const long long floats = 4LL * (a.ax + (long long)a.S1 * RH * a.sd);
-    a.lds_floats = (int)std::max<long long>(floats, (long long)kDwbThreads * (KK + 2));
+    a.lds_floats = (int)std::max<long long>(floats, (long long)(kDwbThreads / kWave) * (KK + 1));
     a.lds_floats = (a.lds_floats + 3) & ~3;
     if ((long long)a.lds_floats * 4 > kDwbLdsBudget) return false;
     a.m_gw = magic31_of(a.Gw);

@@ -153,7 +153,8 @@ __device__ __forceinline__ void load_patch_clamped(PatchRegs<T, CW> &r, const T 
     PatchIO<T, CW>::load_row(r[1], src + (2 * i + 1 < H ? W : 0), vec, col0, W);
 }
 template <typename T, int CW>
-__device__ __forceinline__ void mask_patch(PatchRegs<T, CW> &r, int p, int i, int live, int H) {
+__device__ __forceinline__ void mask_patch(PatchRegs<T, CW> &r, int p, int i, int live, int H, bool full = false) {
+    if (full) return;  // wave-uniform: every plane of the pass is live and H is even
 #pragma unroll
     for (int w = 0; w < PatchIO<T, CW>::kWords; ++w) {
         if (p >= live) r[0][w] = 0;
@@ -339,6 +340,7 @@ __device__ __forceinline__ void plane_fwd_body(const PlaneArgs &args) {
         unit_of(a, u, c, n0);
         const int live = min(PB, a.n - n0);
         const int H = a.H, W = a.W, L = a.L;
+        const bool full = live == PB && !(H & 1);  // nothing of the pass's patches needs masking
         __syncthreads();  // the previous pass is done with every array
         // 1. commit: this unit's weight table and level-1 bands
         {
@@ -360,7 +362,7 @@ __device__ __forceinline__ void plane_fwd_body(const PlaneArgs &args) {
                 if (g >= a.commit_items) continue;
                 int p, i, m;
                 patch_of(a, g, p, i, m);
-                mask_patch<T, CW>(raw[k], p, i, live, H);
+                mask_patch<T, CW>(raw[k], p, i, live, H, full);
                 commit_patch<K, T, CW, kBase>(s4, sy1, pw1, raw[k], p, i, m);
             }
             const T *xb = static_cast<const T *>(a.x) + ((size_t)n0 * a.C + c) * HW;
@@ -369,7 +371,7 @@ __device__ __forceinline__ void plane_fwd_body(const PlaneArgs &args) {
                 load_patch(a, r, xb, live, g);
                 int p, i, m;
                 patch_of(a, g, p, i, m);
-                mask_patch<T, CW>(r, p, i, live, H);
+                mask_patch<T, CW>(r, p, i, live, H, full);
                 commit_patch<K, T, CW, kBase>(s4, sy1, pw1, r, p, i, m);
             }
         }
@@ -396,8 +398,10 @@ __device__ __forceinline__ void plane_fwd_body(const PlaneArgs &args) {
         //    are spread over all lanes
         if (L >= 2) {
             for (int it = tid; it < a.dend[L - 2]; it += NT) {
+                // the item's level from comparisons with the (wave-uniform) level ends,
+                // then its geometry from the LDS table in one round of independent reads
                 int li = 0;
-                while (it >= tab[li * kPlaneTabFields]) ++li;
+                for (int k = 0; k < L - 2; ++k) li += it >= a.dend[k] ? 1 : 0;
                 const int *tl = tab + li * kPlaneTabFields;
                 const int loc = it - (li ? tl[-kPlaneTabFields] : 0), Wls = tl[1];
                 const int s = udiv16(loc, (uint32_t)tl[2]), j = loc - s * Wls;

@@ -25,7 +25,8 @@
 //      x cells around them and adds every (pixel, tap) product to its 25 (k^2)
 //      tap accumulators, and sum dy to a bias accumulator.
 // At the end the lanes' accumulators are summed in a fixed order (bitwise
-// repeatable) into the workgroup's partial row [c][r][k^2 + 1].
+// repeatable): over each wavefront with DPP, then over the wavefronts, into the
+// workgroup's partial row [c][r][k^2 + 1].
 
 #pragma once
 
@@ -118,6 +119,7 @@ __global__ __launch_bounds__(kDwbThreads, 2) void plane_dwb_kernel(PlaneDwbArgs 
 
     for (int g = g_begin; g < g_end; ++g) {
         const int n0 = g * PB, live = min(PB, a.n - n0);
+        const bool full = live == PB && !(a.H & 1);  // nothing of the pass's patches needs masking
         __syncthreads();  // the previous pass is done with the cells
         {
             const int sx = opaque(a.sx), sd = opaque(a.sd), ax = opaque(a.ax);
@@ -127,8 +129,8 @@ __global__ __launch_bounds__(kDwbThreads, 2) void plane_dwb_kernel(PlaneDwbArgs 
                 if (e >= a.commit_items) continue;
                 int p, i, m;
                 patch_of(e, p, i, m);
-                mask_patch<T, CW>(xr[k], p, i, live, a.H);
-                mask_patch<T, CW>(dr[k], p, i, live, a.H);
+                mask_patch<T, CW>(xr[k], p, i, live, a.H, full);
+                mask_patch<T, CW>(dr[k], p, i, live, a.H, full);
                 store_patch(s4, sx, RC, kPlaneCO, xr[k], p, i, m);
                 store_patch(s4 + ax, sd, 0, 0, dr[k], p, i, m);
             }
@@ -137,10 +139,10 @@ __global__ __launch_bounds__(kDwbThreads, 2) void plane_dwb_kernel(PlaneDwbArgs 
                 int p, i, m;
                 patch_of(e, p, i, m);
                 load_patch(rw, xc + (size_t)n0 * CHW, live, e);
-                mask_patch<T, CW>(rw, p, i, live, a.H);
+                mask_patch<T, CW>(rw, p, i, live, a.H, full);
                 store_patch(s4, sx, RC, kPlaneCO, rw, p, i, m);
                 load_patch(rw, dc + (size_t)n0 * CHW, live, e);
-                mask_patch<T, CW>(rw, p, i, live, a.H);
+                mask_patch<T, CW>(rw, p, i, live, a.H, full);
                 store_patch(s4 + ax, sd, 0, 0, rw, p, i, m);
             }
         }
@@ -193,16 +195,21 @@ __global__ __launch_bounds__(kDwbThreads, 2) void plane_dwb_kernel(PlaneDwbArgs 
         }
     }
 
-    // fixed-order reduction of the lanes' accumulators through LDS
-    __syncthreads();
-    constexpr int SL = KK + 1;
+    // fixed-order reduction: every accumulator over its wavefront with DPP
+    // (wave_sum), then the wavefronts' sums in order through LDS
+    constexpr int SL = KK + 1, NW = NT / kWave;
+    const int wave = tid / kWave, lane = tid % kWave;
+    __syncthreads();  // the cells are no longer read: LDS holds the wave sums
 #pragma unroll
-    for (int t = 0; t < KK; ++t) smem[tid * (SL + 1) + t] = acc[t];
-    smem[tid * (SL + 1) + KK] = bsum;
+    for (int t = 0; t < SL; ++t) {
+        const float v = wave_sum(t < KK ? acc[t] : bsum);
+        if (lane == 0) smem[wave * SL + t] = v;
+    }
     __syncthreads();
     if (tid < SL) {
-        float sum = 0.f;
-        for (int l = 0; l < NT; ++l) sum += smem[l * (SL + 1) + tid];
+        float sum = smem[tid];
+#pragma unroll
+        for (int w = 1; w < NW; ++w) sum += smem[w * SL + tid];
         a.partial[((size_t)c * a.k + r) * SL + tid] = sum;
     }
 }
@@ -339,6 +346,7 @@ __global__ __launch_bounds__(kDwlThreads, 3) void plane_dwl_kernel(PlaneDwlArgs 
 
     for (int g = g_begin; g < g_end; ++g) {
         const int n0 = g * PB, live = min(PB, a.n - n0);
+        const bool full = live == PB && !(a.H & 1);  // nothing of the pass's patches needs masking
         __syncthreads();  // the previous pass is done with the bands
         {
             const int xs = opaque(a.xs[0]), xb = opaque(a.xb[0]), gs = opaque(a.gs[0]), gb = opaque(a.gb[0]);
@@ -351,8 +359,8 @@ __global__ __launch_bounds__(kDwlThreads, 3) void plane_dwl_kernel(PlaneDwlArgs 
                 if (e >= a.commit_items) continue;
                 int p, i, m;
                 patch_of(e, p, i, m);
-                mask_patch<T, CW>(xr[k], p, i, live, a.H);
-                mask_patch<T, CW>(dr[k], p, i, live, a.H);
+                mask_patch<T, CW>(xr[k], p, i, live, a.H, full);
+                mask_patch<T, CW>(dr[k], p, i, live, a.H, full);
                 store_bands(xbase, xs, xb, xr[k], i, p * pw1 + m * CW);
                 store_bands(gbase, gs, gb, dr[k], i, p * pw1 + m * CW);
             }
@@ -361,10 +369,10 @@ __global__ __launch_bounds__(kDwlThreads, 3) void plane_dwl_kernel(PlaneDwlArgs 
                 int p, i, m;
                 patch_of(e, p, i, m);
                 load_patch(rw, xc + (size_t)n0 * CHW, live, e);
-                mask_patch<T, CW>(rw, p, i, live, a.H);
+                mask_patch<T, CW>(rw, p, i, live, a.H, full);
                 store_bands(xbase, xs, xb, rw, i, p * pw1 + m * CW);
                 load_patch(rw, dc + (size_t)n0 * CHW, live, e);
-                mask_patch<T, CW>(rw, p, i, live, a.H);
+                mask_patch<T, CW>(rw, p, i, live, a.H, full);
                 store_bands(gbase, gs, gb, rw, i, p * pw1 + m * CW);
             }
         }
