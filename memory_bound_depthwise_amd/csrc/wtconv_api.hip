@@ -348,6 +348,161 @@ bool plan_plane(const wtconv_desc &d, PlaneArgs &a, PlaneCfg &cfg) {
 }
 
 // ---------------------------------------------------------------------------
+// Plane-resident forward kernel on the matrix cores (bfloat16 activations)
+// ---------------------------------------------------------------------------
+
+#ifndef WTC_MMA
+#define WTC_MMA 1  // 0: bfloat16 forward-shaped passes on the vector kernel (for comparisons)
+#endif
+constexpr int kMmaLdsBudget = 40960;
+
+// Layout for pb planes per pass; false when it does not fit.  The geometry
+// constants follow MmaGeom (wtconv_mma.hpp).
+bool mma_layout(const wtconv_desc &d, int CW, int pb, MmaArgs &a) {
+    const int K = d.k, KK = K * K, R = (K - 1) / 2, L = d.levels;
+    const int ROW0 = 2 * R, COL0 = 2 * R, RROWS = 8 + 4 * R;
+    const bool TAIL = K == 5;
+    a = MmaArgs{};
+    a.n = d.n;
+    a.C = d.c;
+    a.H = d.h;
+    a.W = d.w;
+    a.L = L;
+    a.PB = pb;
+    a.H1 = (d.h + 1) / 2;
+    a.W1 = (d.w + 1) / 2;
+    a.Gw = cdiv(a.W1, CW);
+    const int Lg = std::max(L, 1);
+    int hs[kMaxLevels + 1], ws[kMaxLevels + 1];
+    hs[0] = d.h;
+    ws[0] = d.w;
+    for (int l = 1; l <= Lg; ++l) {
+        hs[l] = (hs[l - 1] + 1) / 2;
+        ws[l] = (ws[l - 1] + 1) / 2;
+    }
+    // column pitch between side-by-side planes: at every level the gap is >= R
+    // cells; a multiple of 4 cells (a lane's four output cells share a plane) that
+    // holds every commit group
+    if (pb == 1) {
+        a.Pw1 = (std::max(a.W1, a.Gw * CW) + 3) & ~3;
+    } else {
+        int pwL = 1;
+        for (int l = 1; l <= Lg; ++l) pwL = std::max(pwL, cdiv(ws[l] + R, 1LL << (Lg - l)));
+        while (((long long)pwL << (Lg - 1)) % 4) ++pwL;
+        a.Pw1 = pwL << (Lg - 1);
+    }
+    if (a.Pw1 < a.Gw * CW) return false;
+    const int Wc = pb == 1 ? a.W1 : (pb - 1) * a.Pw1 + a.W1;  // cells of the side-by-side strip
+    const int TY = cdiv(a.H1, 4);
+    a.TX = cdiv(Wc, 16);
+    a.tiles = TY * a.TX;
+    a.commit_items = pb * a.H1 * a.Gw;
+    if (a.commit_items >= 32768 || a.tiles >= 32768) return false;
+    if ((long long)pb * d.c * d.h * d.w >= (1LL << 31)) return false;
+    // canvas: bfloat16 pixels, row y of the strip at canvas row ROW0 + y, column x at
+    // kMmaCL + x; the row stride (dwords) is 16 mod 32, so that the four lane
+    // groups of an A read (four consecutive rows) fall on four distinct bank ranges
+    const long long s_min = std::max<long long>(kMmaCL / 2 + (long long)pb * a.Pw1,
+                                                (kMmaCL - COL0) / 2 + 16LL * a.TX + 4 + (TAIL ? 1 : 0));
+    long long S = s_min;
+    while (S % 32 != 16) ++S;
+    a.S = (int)S;
+    long long rows = std::max<long long>(ROW0 + 2LL * a.H1, 8LL * (TY - 1) + RROWS);
+    if (L >= 2) rows = std::max<long long>(rows, ROW0 + 4LL * hs[2]);
+    long long cells = (rows * S + 3) / 4;  // float4 cells after the canvas
+    int deep = 0;
+    for (int l = 2; l <= L; ++l) {
+        const int li = l - 2;
+        a.hl[li] = hs[l];
+        a.wls[li] = pb == 1 ? ws[l] : (pb * a.Pw1) >> (l - 1);
+        a.sd[li] = cdiv(hs[l], kPlaneRHd);
+        a.syd[li] = kPlaneCO + a.wls[li] + R;
+        a.offd[li] = (int)cells;
+        cells += (long long)(a.sd[li] * kPlaneRHd + 2 * R) * a.syd[li];
+        deep += a.sd[li] * a.wls[li];
+        a.dend[li] = deep;
+        if ((long long)a.hl[li] * a.wls[li] >= 32768 || deep >= 32768) return false;
+    }
+    long long fl = 4 * cells;
+    for (int l = 2; l <= L; ++l) {
+        const int li = l - 2;
+        a.sq[li] = li == 0 ? (2 * a.wls[li] + 3) & ~3 : 2 * a.wls[li];  // level 2: float4 rows
+        a.offq[li] = (int)fl;
+        fl += ((2LL * hs[l] * a.sq[li]) + 3) & ~3LL;
+    }
+    if (L >= 2 && 2LL * hs[2] * (a.sq[0] / 4) >= 65536) return false;
+    a.wt = (int)fl;
+    fl += ((4LL * L + 1) * KK + 1 + 3) & ~3LL;
+    a.zero_floats = (int)fl;
+    a.tab = (int)fl;
+    fl += (kPlaneTabFields * std::max(L - 1, 0) + 3) & ~3;
+    // the tiles read Q_2 (bias and deeper patterns added) at every tile cell, also
+    // past the plane; Q_2 takes them over its own rows and columns
+    for (int l = 2; l <= L; ++l) {
+        const int li = l - 2;
+        const long long end = a.offq[li] + (long long)((4 * TY - 1) >> li) * a.sq[li] + ((16 * a.TX - 1) >> li) + 1;
+        fl = std::max(fl, (end + 3) & ~3LL);
+    }
+    a.lds_floats = (int)fl;
+    if (fl * 4 > kMmaLdsBudget) return false;
+    a.m_gw = magic31_of(a.Gw);
+    a.m_h1 = magic31_of(a.H1);
+    a.m_tx = magic31_of(a.TX);
+    a.m_pw1 = magic31_of(a.Pw1);
+    a.m_q4 = magic31_of(L >= 2 ? a.sq[0] / 4 : 1);
+    for (int l = 2; l <= L; ++l) a.m_wls[l - 2] = magic31_of(a.wls[l - 2]);
+    return true;
+}
+
+// bfloat16 planes 27..64 pixels wide and at most 64 high, levels >= 1, k = 3 or 5.
+// Chooses CW and PB; false when the shape is outside the kernel's range.
+bool plan_mma(const wtconv_desc &d, MmaArgs &a, int &CW) {
+    if (!WTC_MMA || d.dtype != WTCONV_BF16) return false;
+    if (d.levels < 1 || d.n <= 0 || d.c <= 0 || d.h <= 0 || d.w <= 0) return false;
+    if (d.h > kPlaneMaxSide || d.w > kPlaneMaxSide || d.k > 5) return false;
+    // a tile is 16 cell columns: narrower planes (stacked side by side, more gap
+    // columns per tile, short rows of raw loads) run faster on the vector kernel,
+    // and so do planes without levels (measured: the base conv alone is too little
+    // work per pass to keep the latency of the products hidden)
+    if ((d.w + 1) / 2 < 14) return false;
+    CW = d.w % 8 == 0 ? 4 : (d.w % 4 == 0 ? 2 : 1);
+    const int K = d.k;
+    const int nfrag = K == 5 ? 5 : 3;  // B fragments (hi and lo each)
+    // Workgroups per compute unit as the registers allow (~167 VGPRs: 3 waves per
+    // SIMD); the LDS of a layout may allow fewer.  The kernel is latency-bound, so
+    // the choice weighs the resident passes as well as the work per pass.
+    const int wg_regs = 6;
+    double best = -1.0;
+    int best_pb = 0;
+    for (int pb = 1; pb <= std::min(d.n, kFwdPbCap); ++pb) {
+        MmaArgs t{};
+        if (!mma_layout(d, CW, pb, t)) {
+            if (pb == 1) return false;
+            break;
+        }
+        const int wg = std::max(1, std::min(wg_regs, (int)((160 * 1024) / ((long long)t.lds_floats * 4))));
+        // wave-instructions per pass: a tile ~8 per fragment (two 16-cycle products)
+        // plus ~40 others; deep items as in the vector kernel; commit ~20 per item;
+        // ~300 fixed
+        const double tiles = cdiv(t.tiles, kMmaThreads / kWave) * 2.0 * (8.0 * nfrag + 40.0);
+        const int deep_items = d.levels >= 2 ? t.dend[d.levels - 2] : 0;
+        const double deep = cdiv(deep_items, kMmaThreads) * 2.0 * (4.0 * kPlaneRHd * K * K + 60.0);
+        const double misc = cdiv(t.commit_items, kMmaThreads) * 2.0 * 20.0 + 300.0;
+        const double score = (double)pb * wg / (tiles + deep + misc);  // planes per unit time per CU
+        if (score > best * (1 + 1e-9)) {
+            best = score;
+            best_pb = pb;
+        }
+    }
+    if (!mma_layout(d, CW, best_pb, a)) return false;
+    a.NG = cdiv(d.n, a.PB);
+    const long long units = (long long)d.c * a.NG;
+    if (units >= (1LL << 31)) return false;
+    a.U = (int)units;
+    return true;
+}
+
+// ---------------------------------------------------------------------------
 // Plane-resident base weight gradient (polyphase cells of x and dy)
 // ---------------------------------------------------------------------------
 
@@ -662,6 +817,7 @@ std::shared_ptr<const PlanSet> plans_for(const wtconv_desc &d) {
     ps->fp = build_forward_plan(d);
     ps->dp = build_backward_weight_plan(d);
     ps->plane = plan_plane(d, ps->pa, ps->pcfg);
+    ps->mma = plan_mma(d, ps->ma, ps->mcw);
     std::lock_guard<std::mutex> lock(mu);
     if (cache.size() >= 64) cache.erase(cache.begin());
     cache.push_back(ps);
@@ -674,7 +830,7 @@ std::shared_ptr<const PlanSet> plans_for(const wtconv_desc &d) {
 // carriers otherwise.
 size_t forward_workspace_bytes(const wtconv_desc &d) {
     const auto ps = plans_for(d);
-    return ps->plane ? 0 : ps->fp.bytes;
+    return ps->plane || ps->mma ? 0 : ps->fp.bytes;
 }
 
 int check_desc(const wtconv_desc *d) {
@@ -719,6 +875,7 @@ int check_desc(const wtconv_desc *d) {
     } while (0)
 
 int plane_grid_for(const PlanSet &ps) { WTC_DISPATCH(ps.d.k, ps.d.dtype, plane_grid, ps); }
+int mma_grid_for(const PlanSet &ps) { WTC_DISPATCH(ps.d.k, ps.d.dtype, mma_grid, ps); }
 
 int fwd_common(const wtconv_desc *desc, const void *in, const float *w0, const float *b0, const float *s0,
                const float *wl, const float *sl, void *out, void *workspace, size_t workspace_bytes, void *stream,
@@ -733,7 +890,7 @@ int fwd_common(const wtconv_desc *desc, const void *in, const float *w0, const f
         (wl && !aligned(wl, 4)) || (sl && !aligned(sl, 4)))
         return WTCONV_ERR_ALIGN;
     const auto ps = plans_for(d);
-    const size_t need = ps->plane ? 0 : ps->fp.bytes;
+    const size_t need = ps->plane || ps->mma ? 0 : ps->fp.bytes;
     if (need > 0 && (!workspace || workspace_bytes < need)) return WTCONV_ERR_WORKSPACE;
     if (workspace && !aligned(workspace, 16)) return WTCONV_ERR_ALIGN;
     hipStream_t st = static_cast<hipStream_t>(stream);
@@ -908,7 +1065,10 @@ WTCONV_API int wtconv_plan_launches(const wtconv_desc *desc, int op, wtconv_laun
     const auto ps = plans_for(d);
     if (op != WTCONV_OP_BACKWARD_WEIGHT) {
         if (!empty(d)) {
-            if (ps->plane) {
+            if (ps->mma) {
+                add("mma_fwd", 0, mma_grid_for(*ps), kMmaThreads, (size_t)ps->ma.lds_floats * sizeof(float),
+                    ps->mcw);
+            } else if (ps->plane) {
                 add("plane_fwd", 0, plane_grid_for(*ps), kFwdThreads, (size_t)ps->pa.lds_floats * sizeof(float),
                     16 * ps->pcfg.CW + ps->pcfg.RH + (d.levels == 0 ? 256 : 0));
             } else {

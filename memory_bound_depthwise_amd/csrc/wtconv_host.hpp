@@ -4,7 +4,8 @@
 // Paper: "Fast and Memory-Efficient Wavelet Convolutions via I/O-Aware
 // Reformulation".  A call runs one of two kernel families:
 //   * plane-resident kernels (planes whose whole Haar pyramid fits in LDS): one
-//     launch per forward-shaped pass, two gradient launches and the finalize;
+//     launch per forward-shaped pass (on the matrix cores for bfloat16), two
+//     gradient launches and the finalize;
 //   * per-level kernels (larger planes): one analysis + filter launch per level
 //     and one closed-form synthesis launch per forward-shaped pass (§4.1-4.4), one
 //     gradient launch per level, the base gradient and the finalize.
@@ -24,6 +25,7 @@
 #include "wtconv_kernels.hpp"
 #include "wtconv_plane.hpp"
 #include "wtconv_plane_dw.hpp"
+#include "wtconv_mma.hpp"
 
 namespace wtc {
 
@@ -114,6 +116,9 @@ struct PlanSet {
     bool plane;  // forward-shaped passes by the plane-resident kernel
     PlaneArgs pa;
     PlaneCfg pcfg;
+    bool mma = false;  // ... by the plane-resident kernel on the matrix cores (bfloat16)
+    MmaArgs ma{};
+    int mcw = 1;       // its commit width (cells per item)
 };
 
 // ---- Profiling hooks (wtconv_api.hip) ------------------------------------
@@ -134,5 +139,8 @@ int run_backward_weight(const PlanSet &ps, const void *x, const void *dy, const 
 // resident at once on the current device, at most one per unit.
 template <int K, typename T>
 int plane_grid(const PlanSet &ps);
+// ... of the matrix-core forward kernel (one contiguous range of units each).
+template <int K, typename T>
+int mma_grid(const PlanSet &ps);
 
 }  // namespace wtc

@@ -226,6 +226,70 @@ __device__ __forceinline__ void conv_bands(const float4 *win, int stride, const 
     }
 }
 
+// Haar analysis of levels l0..L of a plane-resident pass (unscaled butterflies of
+// the low-pass band of the level above; level 1 is the first grid's .x band).
+template <int K, typename Args>
+__device__ __forceinline__ void haar_levels(const Args &a, float4 *s4, int l0, int tid, int NT) {
+    constexpr int R = (K - 1) / 2;
+    for (int l = l0; l <= a.L; ++l) {
+        const int li = l - 2, Wls = a.wls[li];
+        const float4 *src = s4 + (l == 2 ? 0 : a.offd[li - 1]);
+        const int ss = l == 2 ? a.sy1 : a.syd[li - 1];
+        float4 *dst = s4 + a.offd[li];
+        const int ds = a.syd[li];
+        for (int q = tid; q < a.hl[li] * Wls; q += NT) {
+            const int i = udiv16(q, a.m_wls[li]), j = q - i * Wls;
+            const float4 *sp = src + (2 * i + R) * ss + 2 * j + kPlaneCO;
+            const float x00 = sp[0].x, x01 = sp[1].x, x10 = sp[ss].x, x11 = sp[ss + 1].x;
+            const float s0 = x00 + x01, s1 = x10 + x11, d0 = x00 - x01, d1 = x10 - x11;
+            dst[(i + R) * ds + j + kPlaneCO] = make_float4(s0 + s1, s0 - s1, d0 + d1, d0 - d1);
+        }
+        __syncthreads();
+    }
+}
+
+// Deep levels l >= 2 of a plane-resident pass: the filtered bands of each level
+// (weights folded with s(l) 4^-l: the scale of Eq. 8, the 2^-l of S_l and the 2^-l
+// synthesis weight of Eq. 7) give the four sign patterns of each block (Eq. 12/13),
+// written to Q_l.  One item is one column x kPlaneRHd rows of all four bands of one
+// level; items of all levels are spread over all lanes.
+template <int K, typename Args>
+__device__ __forceinline__ void deep_patterns(const Args &a, float4 *s4, float *smem, const int *tab, int tid,
+                                              int NT) {
+    constexpr int R = (K - 1) / 2, KK = K * K;
+    const int L = a.L;
+    if (L < 2) return;
+    for (int it = tid; it < a.dend[L - 2]; it += NT) {
+        // the item's level from comparisons with the (wave-uniform) level ends,
+        // then its geometry from the LDS table in one round of independent reads
+        int li = 0;
+        for (int k = 0; k < L - 2; ++k) li += it >= a.dend[k] ? 1 : 0;
+        const int *tl = tab + li * kPlaneTabFields;
+        const int loc = it - (li ? tl[-kPlaneTabFields] : 0), Wls = tl[1];
+        const int s = udiv16(loc, (uint32_t)tl[2]), j = loc - s * Wls;
+        const int syd = tl[3];
+        float z[4][kPlaneRHd];
+#pragma unroll
+        for (int b = 0; b < 4; ++b)
+#pragma unroll
+            for (int i = 0; i < kPlaneRHd; ++i) z[b][i] = 0.f;
+        conv_bands<K, kPlaneRHd>(s4 + tl[4] + (s * kPlaneRHd) * syd + j + kPlaneCO - R, syd,
+                                 s4 + (opaque(a.wt) >> 2) + (li + 1) * KK, z);
+        const int sq = tl[5], hl = tl[7];
+        float *q = smem + tl[6] + 2 * j;
+#pragma unroll
+        for (int i = 0; i < kPlaneRHd; ++i) {
+            const int row = s * kPlaneRHd + i;
+            if (row >= hl) break;
+            const float a0v = z[0][i] + z[1][i], a1v = z[0][i] - z[1][i];
+            const float b0 = z[2][i] + z[3][i], b1 = z[2][i] - z[3][i];
+            *reinterpret_cast<float2 *>(q + (2 * row) * sq) = make_float2(a0v + b0, a0v - b0);
+            *reinterpret_cast<float2 *>(q + (2 * row + 1) * sq) = make_float2(a1v + b1, a1v - b1);
+        }
+    }
+    __syncthreads();
+}
+
 // kBase: levels = 0 (a plain depthwise conv); cells hold the four pixels of each
 // 2 x 2 block as loaded, and there is no level to filter.
 template <int K, typename T, int CW, int RH, bool kBase>
@@ -378,55 +442,9 @@ __device__ __forceinline__ void plane_fwd_body(const PlaneArgs &args) {
         __syncthreads();
 
         // 2. Haar analysis of levels 2..L (unscaled butterflies of the low-pass band)
-        for (int l = 2; l <= L; ++l) {
-            const int li = l - 2, Wls = a.wls[li];
-            const float4 *src = s4 + (l == 2 ? 0 : a.offd[li - 1]);
-            const int ss = l == 2 ? a.sy1 : a.syd[li - 1];
-            float4 *dst = s4 + a.offd[li];
-            const int ds = a.syd[li];
-            for (int q = tid; q < a.hl[li] * Wls; q += NT) {
-                const int i = udiv16(q, a.m_wls[li]), j = q - i * Wls;
-                const float4 *sp = src + (2 * i + R) * ss + 2 * j + kPlaneCO;
-                const float x00 = sp[0].x, x01 = sp[1].x, x10 = sp[ss].x, x11 = sp[ss + 1].x;
-                const float s0 = x00 + x01, s1 = x10 + x11, d0 = x00 - x01, d1 = x10 - x11;
-                dst[(i + R) * ds + j + kPlaneCO] = make_float4(s0 + s1, s0 - s1, d0 + d1, d0 - d1);
-            }
-            __syncthreads();
-        }
-
-        // 3. deep levels: filtered bands -> sign patterns Q_l; items of all levels
-        //    are spread over all lanes
-        if (L >= 2) {
-            for (int it = tid; it < a.dend[L - 2]; it += NT) {
-                // the item's level from comparisons with the (wave-uniform) level ends,
-                // then its geometry from the LDS table in one round of independent reads
-                int li = 0;
-                for (int k = 0; k < L - 2; ++k) li += it >= a.dend[k] ? 1 : 0;
-                const int *tl = tab + li * kPlaneTabFields;
-                const int loc = it - (li ? tl[-kPlaneTabFields] : 0), Wls = tl[1];
-                const int s = udiv16(loc, (uint32_t)tl[2]), j = loc - s * Wls;
-                const int syd = tl[3];
-                float z[4][kPlaneRHd];
-#pragma unroll
-                for (int b = 0; b < 4; ++b)
-#pragma unroll
-                    for (int i = 0; i < kPlaneRHd; ++i) z[b][i] = 0.f;
-                conv_bands<K, kPlaneRHd>(s4 + tl[4] + (s * kPlaneRHd) * syd + j + kPlaneCO - R, syd,
-                                         s4 + (opaque(a.wt) >> 2) + (li + 1) * KK, z);
-                const int sq = tl[5], hl = tl[7];
-                float *q = smem + tl[6] + 2 * j;
-#pragma unroll
-                for (int i = 0; i < kPlaneRHd; ++i) {
-                    const int row = s * kPlaneRHd + i;
-                    if (row >= hl) break;
-                    const float a0v = z[0][i] + z[1][i], a1v = z[0][i] - z[1][i];
-                    const float b0 = z[2][i] + z[3][i], b1 = z[2][i] - z[3][i];
-                    *reinterpret_cast<float2 *>(q + (2 * row) * sq) = make_float2(a0v + b0, a0v - b0);
-                    *reinterpret_cast<float2 *>(q + (2 * row + 1) * sq) = make_float2(a1v + b1, a1v - b1);
-                }
-            }
-            __syncthreads();
-        }
+        haar_levels<K>(a, s4, 2, tid, NT);
+        // 3. deep levels: filtered bands -> sign patterns Q_l
+        deep_patterns<K>(a, s4, smem, tab, tid, NT);
 
         // The next unit's loads are issued only now, while no phase of this pass
         // waits for vector memory any more: a wait for anything loaded after them

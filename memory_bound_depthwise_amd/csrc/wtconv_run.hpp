@@ -180,9 +180,81 @@ int run_plane_dwl(const PlanSet &ps, const void *x, const void *dy, float *parti
 #undef WTC_DWL_LAUNCH
 }
 
+// Resident workgroups of a kernel on the current device (cached per device, kernel
+// and LDS size); a conservative estimate when the occupancy query fails.
+inline long long resident_slots(const void *kern, int threads, size_t shm) {
+    static std::mutex mu;
+    struct Entry {
+        int dev;
+        const void *kern;
+        size_t shm;
+        long long slots;
+    };
+    static std::vector<Entry> seen;
+    int dev = 0, cus = 0, per_cu = 0;
+    if (hipGetDevice(&dev) == hipSuccess) {
+        std::lock_guard<std::mutex> lock(mu);
+        for (const Entry &e : seen)
+            if (e.dev == dev && e.kern == kern && e.shm == shm) return e.slots;
+    }
+    if (hipGetDevice(&dev) != hipSuccess || hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess ||
+        hipOccupancyMaxActiveBlocksPerMultiprocessor(&per_cu, kern, threads, shm) != hipSuccess || cus <= 0 || per_cu <= 0) {
+        (void)hipGetLastError();
+        return 256LL * std::max(1, std::min(4, (int)((160 * 1024) / std::max<size_t>(shm, 1))));
+    }
+    std::lock_guard<std::mutex> lock(mu);
+    seen.push_back(Entry{dev, kern, shm, (long long)cus * per_cu});
+    return (long long)cus * per_cu;
+}
+
+template <int K, typename T>
+int mma_grid(const PlanSet &ps) {
+    if constexpr (K > 5) {
+        return 0;  // not planned: the matrix-core kernel takes K = 3 or 5
+    } else {
+        const MmaArgs &a = ps.ma;
+        const size_t shm = (size_t)a.lds_floats * sizeof(float);
+        const void *kern = ps.mcw == 4   ? reinterpret_cast<const void *>(mma_fwd_kernel<K, 4>)
+                           : ps.mcw == 2 ? reinterpret_cast<const void *>(mma_fwd_kernel<K, 2>)
+                                         : reinterpret_cast<const void *>(mma_fwd_kernel<K, 1>);
+        return (int)std::min<long long>(a.U, resident_slots(kern, kMmaThreads, shm));
+    }
+}
+
+template <int K, typename T>
+int run_mma_forward(const PlanSet &ps, const void *x, const float *w0, const float *b0, const float *s0,
+                    const float *wl, const float *sl, void *y, hipStream_t st, int rotate) {
+    if constexpr (!std::is_same<T, uint16_t>::value || K > 5) {
+        return WTCONV_ERR_DTYPE;  // not planned: bfloat16 with K = 3 or 5 only
+    } else {
+        const wtconv_desc &d = ps.d;
+        const int CW = ps.mcw;
+        MmaArgs a = ps.ma;
+        a.x = x;
+        a.y = y;
+        a.w0 = w0;
+        a.b0 = b0;
+        a.s0 = s0;
+        a.wl = wl;
+        a.sl = sl;
+        a.rotate = rotate;
+        a.vec = d.w % (2 * CW) == 0 && aligned(x, 2 * CW * sizeof(T)) ? 1 : 0;
+        a.store_mode = d.w % 4 == 0 && aligned(y, 4 * sizeof(T)) ? 2 : (d.w % 2 == 0 && aligned(y, 2 * sizeof(T)) ? 1 : 0);
+        const dim3 grid((unsigned)mma_grid<K, T>(ps));
+        const size_t shm = (size_t)a.lds_floats * sizeof(float);
+        const int bf = dtype_of<T>();
+        switch (CW) {
+            case 4: return launch("mma_fwd", K, bf, 0, mma_fwd_kernel<K, 4>, grid, dim3(kMmaThreads), shm, st, a);
+            case 2: return launch("mma_fwd", K, bf, 0, mma_fwd_kernel<K, 2>, grid, dim3(kMmaThreads), shm, st, a);
+            default: return launch("mma_fwd", K, bf, 0, mma_fwd_kernel<K, 1>, grid, dim3(kMmaThreads), shm, st, a);
+        }
+    }
+}
+
 template <int K, typename T>
 int run_forward(const PlanSet &ps, const void *x, const float *w0, const float *b0, const float *s0,
                 const float *wl, const float *sl, void *y, char *ws, hipStream_t st, int rotate) {
+    if (ps.mma) return run_mma_forward<K, T>(ps, x, w0, b0, s0, wl, sl, y, st, rotate);
     if (ps.plane) return run_plane_forward<K, T>(ps, x, w0, b0, s0, wl, sl, y, st, rotate);
     const wtconv_desc &d = ps.d;
     const FwdPlan &p = ps.fp;

@@ -61,7 +61,7 @@ def kernel_cost(family, level, n, c, h, w, k, levels, elem_bytes):
     blocks = [P * hs[l] * ws[l] for l in range(levels + 1)]
     kk = k * k
     lvl_flops = sum(2 * 4 * blocks[l] * kk for l in range(1, levels + 1))
-    if family == "plane_fwd":
+    if family in ("plane_fwd", "mma_fwd"):
         return E * 2 * N, 2 * N * kk + lvl_flops
     if family == "plane_dwl":
         return E * 2 * N, lvl_flops

@@ -35,7 +35,7 @@ DTYPES = ["f32", "bf16", "f16"]
 
 def variant_shapes():
     """One shape per compiled variant of the plane-resident kernels, for every k and
-    for levels = 0 and >= 1.  The library picks the variant from the plane alone:
+    for levels = 0 and >= 1 (the matrix-core kernel's at the end).  The library picks the variant from the plane alone:
     cell rows per item RH = 7 when ceil(h/2) is a multiple of 7, 4 when ceil(h/2) <= 4,
     8 otherwise; cells per staging item CW = 4 when w % 8 == 0, 2 when w % 4 == 0,
     1 otherwise.  Heights alternate between even and odd (pad-to-even), and three
@@ -51,6 +51,15 @@ def variant_shapes():
                     h = he if i % 2 == 0 else ho
                     out.append((3, 2, h, w, k, L))
                     i += 1
+    # bfloat16 planes 27..64 wide with levels run the matrix-core kernel, k = 3 or 5:
+    # one shape per commit width CW (w % 8 == 0, w % 4 == 0, odd w), levels 1..3,
+    # even and odd heights, three images per channel
+    mma = {4: 32, 2: 28, 1: 29}
+    for k in (3, 5):
+        for cw, w in mma.items():
+            h = (30, 33, 40)[i % 3]
+            out.append((3, 2, h, w, k, 1 + i % 3))
+            i += 1
     return out
 
 

@@ -174,10 +174,14 @@ def test_backward_weight_argument_errors():
 def test_launch_plan_query():
     # host-only query: the kernels each operation enqueues for a shape
     plan = lambda d, op: [e["name"] for e in wt.wtconv_plan_launches(d, op)]
-    d = wt.make_desc(64, 96, 56, 56, 5, 3, wt.BF16)       # plane-resident path
-    assert plan(d, wt.OP_FORWARD) == ["plane_fwd<5,bf16>"]
-    assert plan(d, wt.OP_BACKWARD_INPUT) == ["plane_fwd<5,bf16>"]
+    d = wt.make_desc(64, 96, 56, 56, 5, 3, wt.BF16)       # plane-resident path, bfloat16 on the matrix cores
+    assert plan(d, wt.OP_FORWARD) == ["mma_fwd<5,bf16>"]
+    assert plan(d, wt.OP_BACKWARD_INPUT) == ["mma_fwd<5,bf16>"]
     assert plan(d, wt.OP_BACKWARD_WEIGHT) == ["plane_dwl<5,bf16>", "plane_dwb<5,bf16>", "dw_finalize<5,bf16>"]
+    d = wt.make_desc(64, 96, 56, 56, 5, 3, wt.F16)        # ... on the vector units for the other dtypes
+    assert plan(d, wt.OP_FORWARD) == ["plane_fwd<5,f16>"]
+    d = wt.make_desc(64, 384, 14, 14, 5, 1, wt.BF16)      # ... and for narrow planes
+    assert plan(d, wt.OP_FORWARD) == ["plane_fwd<5,bf16>"]
     d = wt.make_desc(64, 96, 56, 56, 7, 0, wt.BF16)       # levels = 0: the same kernel, base only
     assert plan(d, wt.OP_FORWARD) == ["plane_fwd<7,bf16>"]
     assert plan(d, wt.OP_BACKWARD_WEIGHT) == ["plane_dwb<7,bf16>", "dw_finalize<7,bf16>"]

@@ -56,12 +56,14 @@ def plan_names(case):
 
 def path_of(case):
     """(forward path, weight-gradient path): 'plane' when the plane-resident
-    kernels run (every intermediate stays on chip in float32), 'level' when the
+    kernels run (every intermediate stays on chip in float32; the matrix-core
+    forward kernel multiplies the bfloat16 pixels by weights split into two
+    bfloat16 halves, ~16 significant bits, with float32 accumulation), 'level' when the
     per-level kernels run (coefficients and carriers pass through the workspace in
     the activation dtype)."""
     import memory_bound_depthwise_amd as wt
     names = plan_names(case)
-    fwd = "plane" if any(n.startswith("plane_fwd") for n in names[wt.OP_FORWARD]) else "level"
+    fwd = "plane" if any(n.startswith(("plane_fwd", "mma_fwd")) for n in names[wt.OP_FORWARD]) else "level"
     dw = names[wt.OP_BACKWARD_WEIGHT]
     if case.levels == 0:
         dwp = "plane" if any(n.startswith("plane_dwb") for n in dw) else "level"
