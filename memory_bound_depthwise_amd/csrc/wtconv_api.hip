@@ -592,7 +592,7 @@ int column_stride(int lo) {
     return s;
 }
 
-bool dwl_layout(const wtconv_desc &d, const PlaneCfg &cfg, int pb, PlaneDwlArgs &a) {
+bool dwl_layout(const wtconv_desc &d, const PlaneCfg &cfg, int pb, PlaneDwlArgs &a, int lfirst) {
     const int K = d.k, KK = K * K, R = (K - 1) / 2, L = d.levels, RHD = cfg.RH, CW = cfg.CW;
     a = PlaneDwlArgs{};
     a.n = d.n;
@@ -653,14 +653,15 @@ bool dwl_layout(const wtconv_desc &d, const PlaneCfg &cfg, int pb, PlaneDwlArgs 
     fl = std::max<long long>(fl, (long long)kDwlThreads * (TC + 1));
     a.lds_floats = (int)((fl + 3) & ~3LL);
     if ((long long)a.lds_floats * 4 > kDwlLdsBudget) return false;
-    // lanes per (level, band): greedy, to minimise the largest item count of a lane
+    // lanes per (level, band) of levels lfirst + 1 .. L: greedy, to minimise the
+    // largest item count of a lane
     int M[kMaxLevels];
-    for (int l = 0; l < L; ++l) M[l] = 1;
-    if (4 * L > kDwlThreads) return false;
-    int used = 4 * L;
+    for (int l = 0; l < L; ++l) M[l] = l < lfirst ? 0 : 1;
+    if (4 * (L - lfirst) > kDwlThreads) return false;
+    int used = 4 * (L - lfirst);
     while (used + 4 <= kDwlThreads) {
         int worst = -1, wl_items = 0;
-        for (int l = 0; l < L; ++l) {
+        for (int l = lfirst; l < L; ++l) {
             const int items = a.ns[l] * a.PB * a.wr[l], per = cdiv(items, M[l]);
             if (M[l] < std::min(items, 255) && per > wl_items) {
                 wl_items = per;
@@ -672,7 +673,7 @@ bool dwl_layout(const wtconv_desc &d, const PlaneCfg &cfg, int pb, PlaneDwlArgs 
         used += 4;
     }
     int t = 0;
-    for (int l = 0; l < L; ++l) {
+    for (int l = lfirst; l < L; ++l) {
         a.lane0[l] = t;
         a.lanes[l] = M[l];
         for (int b = 0; b < 4; ++b)
@@ -680,7 +681,8 @@ bool dwl_layout(const wtconv_desc &d, const PlaneCfg &cfg, int pb, PlaneDwlArgs 
                 a.lane[t] = (uint32_t)(l + 1) | ((uint32_t)b << 4) | ((uint32_t)m << 8) | ((uint32_t)M[l] << 16);
     }
     for (; t < kDwlThreads; ++t) a.lane[t] = 0;
-    a.groups = 4 * L;
+    a.groups = 4 * (L - lfirst);
+    a.lfirst = lfirst;
     a.m_gw = magic31_of(a.Gw);
     a.m_h1 = magic31_of(a.H1);
     return true;
@@ -697,8 +699,9 @@ int dwl_lane_items(const PlaneDwlArgs &a) {
     return worst;
 }
 
-bool plan_dwl(const wtconv_desc &d, PlaneDwlArgs &a, PlaneCfg &cfg) {
-    if (d.levels < 1 || d.n <= 0 || d.c <= 0 || d.h <= 0 || d.w <= 0) return false;
+// lfirst = 1: levels 2..L only (level 1 runs in the correlation kernel)
+bool plan_dwl(const wtconv_desc &d, PlaneDwlArgs &a, PlaneCfg &cfg, int lfirst) {
+    if (d.levels < 1 + lfirst || d.n <= 0 || d.c <= 0 || d.h <= 0 || d.w <= 0) return false;
     if (d.h > kPlaneMaxSide || d.w > kPlaneMaxSide) return false;
     cfg.RH = 4;  // item rows: one 16-byte read of dy per item
     cfg.CW = d.w % 8 == 0 ? 4 : (d.w % 4 == 0 ? 2 : 1);
@@ -706,7 +709,7 @@ bool plan_dwl(const wtconv_desc &d, PlaneDwlArgs &a, PlaneCfg &cfg) {
     int best_pb = 0;
     for (int pb = 1; pb <= std::min(d.n, kDwPbCap); ++pb) {
         PlaneDwlArgs t{};
-        if (!dwl_layout(d, cfg, pb, t)) {
+        if (!dwl_layout(d, cfg, pb, t, lfirst)) {
             if (pb == 1) return false;
             break;
         }
@@ -719,7 +722,7 @@ bool plan_dwl(const wtconv_desc &d, PlaneDwlArgs &a, PlaneCfg &cfg) {
             best_pb = pb;
         }
     }
-    if (!dwl_layout(d, cfg, best_pb, a)) return false;
+    if (!dwl_layout(d, cfg, best_pb, a, lfirst)) return false;
     a.NG = cdiv(d.n, a.PB);
     // Among the workgroup counts per channel that are all resident at once, the one
     // with the least work on the busiest compute unit: workgroups per CU times image
@@ -734,6 +737,104 @@ bool plan_dwl(const wtconv_desc &d, PlaneDwlArgs &a, PlaneCfg &cfg) {
             a.k = k;
         }
     }
+    return (long long)d.c * a.k < (1LL << 31);
+}
+
+// ---------------------------------------------------------------------------
+// Base and level-1 weight gradients on the matrix cores (bfloat16)
+// ---------------------------------------------------------------------------
+
+constexpr int kDwcLdsBudget = 40960;
+
+// Layout for pb planes per pass; false when it does not fit.  The offset range
+// follows DwcGeom (wtconv_dwc.hpp).
+bool dwc_layout(const wtconv_desc &d, int CW, int pb, PlaneDwcArgs &a, bool lev) {
+    const int K = d.k, R = (K - 1) / 2;
+    const int T0 = lev ? -R : -((R + 1) / 2), T1 = lev ? R : (R + 1) / 2;
+    const int NF = (T1 - T0 + 4) / 4, TYMAX = T0 + 4 * NF - 1;
+    a = PlaneDwcArgs{};
+    a.n = d.n;
+    a.C = d.c;
+    a.H = d.h;
+    a.W = d.w;
+    a.PB = pb;
+    a.H1 = (d.h + 1) / 2;
+    a.W1 = (d.w + 1) / 2;
+    a.Gw = cdiv(a.W1, CW);
+    // cell pitch between side-by-side planes: a gap of at least R zero cells, every
+    // commit group inside, even (patches are written as bfloat16 pairs)
+    a.Pw1 = (std::max(pb == 1 ? a.W1 : a.W1 + R, a.Gw * CW) + 1) & ~1;
+    const int Wc = (pb - 1) * a.Pw1 + a.W1;
+    a.nch = cdiv(Wc, 32);
+    a.commit_items = pb * a.H1 * a.Gw;
+    a.items = a.H1 * a.nch;
+    if (a.commit_items >= 32768 || a.items >= 32768) return false;
+    if ((long long)pb * d.c * d.h * d.w >= (1LL << 31)) return false;
+    // dy planes: DT zero rows above row 0, -T0 below; the row stride is 16 mod 64
+    // dwords and the plane size 4 mod 64, so that the 16 A rows of a lane group
+    // (4 components x 4 row shifts) fall on distinct banks
+    a.DT = std::max(TYMAX, 0);
+    const long long rows_d = a.H1 + a.DT + std::max(-T0, 0);
+    long long Sd = std::max<long long>(16LL * a.nch, cdiv((long long)pb * a.Pw1, 2));
+    while (Sd % 64 != 16) ++Sd;
+    long long pd = rows_d * Sd;
+    while (pd % 64 != 4) ++pd;
+    // x planes: XL zero cells left of column 0; a lane reads five dwords from the
+    // pair holding its first cell
+    a.XL = (-T0 + 1) & ~1;
+    long long Sx = std::max<long long>((a.XL + 32LL * a.nch + T0 + 4 * NF - 5) / 2 + 5, cdiv(a.XL + (long long)pb * a.Pw1, 2));
+    long long px = a.H1 * Sx;
+    while (px % 64 != 8) ++px;
+    a.Sd = (int)Sd;
+    a.pd = (int)pd;
+    a.Sx = (int)Sx;
+    a.px = (int)px;
+    a.xo = (int)(4 * pd);
+    const long long planes = 4 * pd + 4 * px;
+    const long long NC = (long long)NF * NF * 256;
+    const long long red = (kDwcThreads / kWave + 1) * NC + kDwcThreads / kWave;
+    const long long fl = std::max(planes, red);
+    a.lds_floats = (int)((fl + 3) & ~3LL);
+    if ((long long)a.lds_floats * 4 > kDwcLdsBudget) return false;
+    a.m_gw = magic31_of(a.Gw);
+    a.m_h1 = magic31_of(a.H1);
+    a.m_nch = magic31_of(a.nch);
+    return true;
+}
+
+// bfloat16 planes of at most 64 x 64.  Chooses CW, PB and the workgroups per channel.
+// lev: level 1 as well as the base (levels >= 1).
+bool plan_dwc(const wtconv_desc &d, PlaneDwcArgs &a, int &CW, bool lev) {
+    if (!WTC_MMA || d.dtype != WTCONV_BF16) return false;
+    if (d.n <= 0 || d.c <= 0 || d.h <= 0 || d.w <= 0) return false;
+    if (d.h > kPlaneMaxSide || d.w > kPlaneMaxSide) return false;
+    CW = d.w % 8 == 0 ? 4 : (d.w % 4 == 0 ? 2 : 1);
+    const int R = (d.k - 1) / 2;
+    const int NF = ((lev ? 2 * R : 2 * ((R + 1) / 2)) + 4) / 4;
+    double best = -1.0;
+    int best_pb = 0;
+    for (int pb = 1; pb <= std::min(d.n, kDwPbCap); ++pb) {
+        PlaneDwcArgs t{};
+        if (!dwc_layout(d, CW, pb, t, lev)) {
+            if (pb == 1) return false;
+            break;
+        }
+        // wave-instructions per pass: an item ~8 per product (16 cycles) plus ~10
+        // per operand read and ~20 others; commit ~40 per item; ~300 fixed.  Eight
+        // workgroups per compute unit as the registers allow, fewer as the LDS does.
+        const int wg = std::max(1, std::min(8, (int)((160 * 1024) / ((long long)t.lds_floats * 4))));
+        const double cost = cdiv(t.items, kDwcThreads / kWave) * 2.0 * (8.0 * NF * NF + 20.0 * NF + 20.0) +
+                            cdiv(t.commit_items, kDwcThreads) * 2.0 * 40.0 + 300.0;
+        const double score = (double)pb * wg / cost;
+        if (score > best * (1 + 1e-9)) {
+            best = score;
+            best_pb = pb;
+        }
+    }
+    if (!dwc_layout(d, CW, best_pb, a, lev)) return false;
+    a.NG = cdiv(d.n, a.PB);
+    const int wg = std::max(1, std::min(8, (int)((160 * 1024) / ((long long)a.lds_floats * 4))));
+    a.k = std::max(1, std::min(a.NG, 256 * wg / d.c));
     return (long long)d.c * a.k < (1LL << 31);
 }
 
@@ -760,10 +861,19 @@ FwdPlan build_forward_plan(const wtconv_desc &d) {
 DwPlan build_backward_weight_plan(const wtconv_desc &d) {
     DwPlan p{};
     p.ld = level_dims(d);
-    p.dwl = plan_dwl(d, p.la, p.lcfg);
+    // bfloat16: base and level 1 by the correlation kernel, levels 2..L by the level
+    // kernel; when the level kernel does not fit, the correlation kernel takes the
+    // base alone and the per-level kernels all levels
+    p.dwc = plan_dwc(d, p.ca, p.ccw, d.levels >= 1);
+    p.dwc_lev = p.dwc && d.levels >= 1;
+    if (p.dwc_lev && d.levels >= 2 && !plan_dwl(d, p.la, p.lcfg, 1)) {
+        p.dwc = plan_dwc(d, p.ca, p.ccw, false);
+        p.dwc_lev = false;
+    }
+    p.dwl = p.dwc_lev ? d.levels >= 2 : plan_dwl(d, p.la, p.lcfg, 0);
     const size_t es = elem_size(d.dtype), planes = (size_t)d.n * d.c;
     size_t off = 0;
-    if (!p.dwl) {
+    if (!p.dwl && !p.dwc_lev) {
         for (int l = 1; l < d.levels; ++l) {
             p.xc_off[l - 1] = off;
             off = align_up(off + planes * p.ld.H[l] * p.ld.W[l] * es);
@@ -774,10 +884,12 @@ DwPlan build_backward_weight_plan(const wtconv_desc &d) {
     p.part_off = off;
     const int KK = d.k * d.k;
     p.base = pick_tiling(Kind::DwBase, d.k, d.n, d.c, d.h, d.w, max_vec_width(d.dtype));
-    p.dwb = plan_dwb(d, p.ba, p.bcfg);
+    p.dwb = !p.dwc && plan_dwb(d, p.ba, p.bcfg);
     long long floats = 0;
     p.region[0] = 0;
-    if (p.dwb)
+    if (p.dwc)
+        p.G[0] = p.ca.k;
+    else if (p.dwb)
         p.G[0] = p.ba.k;
     else
         p.G[0] = (d.n > 0 && d.h > 0 && d.w > 0) ? p.base.nblk * p.base.tiles : 0;
@@ -785,7 +897,9 @@ DwPlan build_backward_weight_plan(const wtconv_desc &d) {
     for (int l = 1; l <= d.levels; ++l) {
         p.lvl[l - 1] = pick_tiling(Kind::DwLevel, d.k, d.n, d.c, p.ld.H[l], p.ld.W[l], 1);
         p.region[l] = floats;
-        if (p.dwl)
+        if (p.dwc_lev && l == 1)
+            p.G[l] = p.ca.k;
+        else if (p.dwl)
             p.G[l] = p.la.k;
         else
             p.G[l] = (d.n > 0 && d.h > 0 && d.w > 0) ? p.lvl[l - 1].nblk * p.lvl[l - 1].tiles : 0;
@@ -1082,7 +1196,14 @@ WTCONV_API int wtconv_plan_launches(const wtconv_desc *desc, int op, wtconv_laun
         }
     } else if (d.c > 0) {
         const DwPlan &p = ps->dp;
-        if (!empty(d)) {
+        if (p.dwc)
+            add("plane_dwc", 0, (long long)d.c * p.ca.k, kDwcThreads, (size_t)p.ca.lds_floats * sizeof(float),
+                p.ccw + (p.dwc_lev ? 16 : 0));
+        if (p.dwc_lev) {
+            if (d.levels >= 2)
+                add("plane_dwd", 0, (long long)d.c * p.la.k, kDwlThreads, (size_t)p.la.lds_floats * sizeof(float),
+                    16 * p.lcfg.CW + p.lcfg.RH);
+        } else if (!empty(d)) {
             if (p.dwl && d.levels > 0) {
                 add("plane_dwl", 0, (long long)d.c * p.la.k, kDwlThreads, (size_t)p.la.lds_floats * sizeof(float),
                     16 * p.lcfg.CW + p.lcfg.RH);
@@ -1090,7 +1211,9 @@ WTCONV_API int wtconv_plan_launches(const wtconv_desc *desc, int op, wtconv_laun
                 for (int l = 1; l <= d.levels; ++l)
                     add("dw_level", l, grid_of(p.lvl[l - 1], d.c), kThreads, lds_bytes(Kind::DwLevel, d.k, p.lvl[l - 1]));
             }
-            if (p.dwb) {
+            if (p.dwc) {
+                // the base ran in the correlation kernel
+            } else if (p.dwb) {
                 add("plane_dwb", 0, (long long)d.c * p.ba.k, kDwbThreads, (size_t)p.ba.lds_floats * sizeof(float),
                     16 * p.bcfg.CW + p.bcfg.RH);
             } else {

@@ -26,6 +26,7 @@
 #include "wtconv_plane.hpp"
 #include "wtconv_plane_dw.hpp"
 #include "wtconv_mma.hpp"
+#include "wtconv_dwc.hpp"
 
 namespace wtc {
 
@@ -93,6 +94,10 @@ struct FwdPlan {
 };
 
 struct DwPlan {
+    bool dwc;            // base by the matrix-core correlation kernel (bfloat16) ...
+    bool dwc_lev;        // ... and level 1 too; the level kernel then takes levels 2..L only
+    PlaneDwcArgs ca;
+    int ccw;             // its commit width
     bool dwb;            // base by the plane-resident kernel
     PlaneDwbArgs ba;
     PlaneCfg bcfg;

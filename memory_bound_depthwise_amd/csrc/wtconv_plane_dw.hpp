@@ -260,7 +260,8 @@ struct PlaneDwlArgs {
     uint32_t m_wl[kMaxLevels], m_hl[kMaxLevels];          // udiv16 reciprocals of wl, hl
     uint32_t m_row[kMaxLevels], m_wr[kMaxLevels];         // ... of PB wr (items per strip), wr
     uint32_t lane[kDwlThreads];            // level (bits 0-3) | band (4-5) | index in group (8-15) | lanes in group (16-23)
-    int groups;                            // (level, band) groups in use: 4 L
+    int groups;                            // (level, band) groups in use: 4 (L - lfirst)
+    int lfirst;                            // first level with items, 0-based (1: level 1 runs elsewhere)
     int lane0[kMaxLevels], lanes[kMaxLevels];  // level l: first lane of band 0, lanes per band
     int lds_floats;
     uint32_t m_gw, m_h1;                   // udiv16 reciprocals of Gw, H1
@@ -459,7 +460,7 @@ __global__ __launch_bounds__(kDwlThreads, 3) void plane_dwl_kernel(PlaneDwlArgs 
         const int nt = min(TC, KK - t0);
         for (int q = tid; q < a.groups * nt; q += NT) {
             const int grp = q / nt, tap = q - grp * nt;
-            const int l = grp >> 2, b = grp & 3;  // 0-based level
+            const int l = (grp >> 2) + a.lfirst, b = grp & 3;  // 0-based level
             const int l0 = a.lane0[l] + b * a.lanes[l];
             float sum = 0.f;
             for (int t = l0; t < l0 + a.lanes[l]; ++t) sum += smem[t * (TC + 1) + tap];

@@ -157,6 +157,41 @@ int run_plane_dwb(const PlanSet &ps, const void *x, const void *dy, float *parti
 }
 
 template <int K, typename T>
+int run_plane_dwc(const PlanSet &ps, const void *x, const void *dy, float *partial, hipStream_t st) {
+    if constexpr (!std::is_same<T, uint16_t>::value) {
+        return WTCONV_ERR_DTYPE;  // not planned: bfloat16 only
+    } else {
+        const wtconv_desc &d = ps.d;
+        const DwPlan &p = ps.dp;
+        PlaneDwcArgs a = p.ca;
+        const int CW = p.ccw;
+        a.x = x;
+        a.dy = dy;
+        a.pbase = partial + p.region[0];
+        a.plev = p.dwc_lev ? partial + p.region[1] : nullptr;
+        a.vec = d.w % (2 * CW) == 0 && aligned(x, 2 * CW * sizeof(T)) && aligned(dy, 2 * CW * sizeof(T)) ? 1 : 0;
+        const dim3 grid((unsigned)((long long)d.c * a.k));
+        const size_t shm = (size_t)a.lds_floats * sizeof(float);
+        const int bf = dtype_of<T>();
+#define WTC_DWC_LAUNCH(CW_, LEV_) \
+    launch("plane_dwc", K, bf, 0, plane_dwc_kernel<K, CW_, LEV_>, grid, dim3(kDwcThreads), shm, st, a)
+        if (p.dwc_lev) {
+            switch (CW) {
+                case 4: return WTC_DWC_LAUNCH(4, true);
+                case 2: return WTC_DWC_LAUNCH(2, true);
+                default: return WTC_DWC_LAUNCH(1, true);
+            }
+        }
+        switch (CW) {
+            case 4: return WTC_DWC_LAUNCH(4, false);
+            case 2: return WTC_DWC_LAUNCH(2, false);
+            default: return WTC_DWC_LAUNCH(1, false);
+        }
+#undef WTC_DWC_LAUNCH
+    }
+}
+
+template <int K, typename T>
 int run_plane_dwl(const PlanSet &ps, const void *x, const void *dy, float *partial, hipStream_t st) {
     const wtconv_desc &d = ps.d;
     const DwPlan &p = ps.dp;
@@ -170,8 +205,10 @@ int run_plane_dwl(const PlanSet &ps, const void *x, const void *dy, float *parti
     const dim3 grid((unsigned)((long long)d.c * a.k));
     const size_t shm = (size_t)a.lds_floats * sizeof(float);
     const int bf = dtype_of<T>();  // dtype code, for the launch records
+    // with the correlation kernel taking level 1, this launch covers levels 2..L
+    const char *fam = a.lfirst ? "plane_dwd" : "plane_dwl";
 #define WTC_DWL_LAUNCH(CW_, RH_) \
-    launch("plane_dwl", K, bf, 0, plane_dwl_kernel<K, T, CW_, RH_>, grid, dim3(kDwlThreads), shm, st, a)
+    launch(fam, K, bf, 0, plane_dwl_kernel<K, T, CW_, RH_>, grid, dim3(kDwlThreads), shm, st, a)
     switch (cfg.CW) {
         case 4: return WTC_DWL_LAUNCH(4, 4);
         case 2: return WTC_DWL_LAUNCH(2, 4);
@@ -315,7 +352,16 @@ int run_backward_weight(const PlanSet &ps, const void *x, const void *dy, const 
     const int bf = dtype_of<T>();  // dtype code, for the launch records
     const int L = d.levels;
     float *partial = reinterpret_cast<float *>(ws + p.part_off);
-    if (!empty(d)) {
+    if (!empty(d) && p.dwc) {
+        int rc = run_plane_dwc<K, T>(ps, x, dy, partial, st);
+        if (rc) return rc;
+    }
+    if (!empty(d) && p.dwc_lev) {
+        if (L >= 2) {
+            int rc = run_plane_dwl<K, T>(ps, x, dy, partial, st);
+            if (rc) return rc;
+        }
+    } else if (!empty(d)) {
         if (p.dwl && L > 0) {
             int rc = run_plane_dwl<K, T>(ps, x, dy, partial, st);
             if (rc) return rc;
@@ -341,7 +387,9 @@ int run_backward_weight(const PlanSet &ps, const void *x, const void *dy, const 
                             dim3(kThreads), shm, st, a);
             if (rc) return rc;
         }
-        if (p.dwb) {
+        if (p.dwc) {
+            // the base ran in the correlation kernel
+        } else if (p.dwb) {
             int rc = run_plane_dwb<K, T>(ps, x, dy, partial + p.region[0], st);
             if (rc) return rc;
         } else {

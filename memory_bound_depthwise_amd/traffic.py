@@ -65,6 +65,10 @@ def kernel_cost(family, level, n, c, h, w, k, levels, elem_bytes):
         return E * 2 * N, 2 * N * kk + lvl_flops
     if family == "plane_dwl":
         return E * 2 * N, lvl_flops
+    if family == "plane_dwc":  # base and level 1
+        return E * 2 * N, 2 * N * kk + (2 * 4 * blocks[1] * kk if levels >= 1 else 0)
+    if family == "plane_dwd":  # levels 2..L
+        return E * 2 * N, sum(2 * 4 * blocks[l] * kk for l in range(2, levels + 1))
     if family == "level_fwd":
         l = level
         elems = blocks[l - 1] + 4 * blocks[l] + (blocks[l] if l < levels else 0)

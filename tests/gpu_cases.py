@@ -60,6 +60,10 @@ def variant_shapes():
             h = (30, 33, 40)[i % 3]
             out.append((3, 2, h, w, k, 1 + i % 3))
             i += 1
+    # bfloat16 weight gradients of levels 2..L beside the correlation kernel, for the
+    # kernel sizes the rows above leave out at CW = 4
+    for k in (3, 7):
+        out.append((3, 2, 17, 24, k, 2))
     return out
 
 

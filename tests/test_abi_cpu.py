@@ -177,14 +177,16 @@ def test_launch_plan_query():
     d = wt.make_desc(64, 96, 56, 56, 5, 3, wt.BF16)       # plane-resident path, bfloat16 on the matrix cores
     assert plan(d, wt.OP_FORWARD) == ["mma_fwd<5,bf16>"]
     assert plan(d, wt.OP_BACKWARD_INPUT) == ["mma_fwd<5,bf16>"]
-    assert plan(d, wt.OP_BACKWARD_WEIGHT) == ["plane_dwl<5,bf16>", "plane_dwb<5,bf16>", "dw_finalize<5,bf16>"]
+    # weight gradients: base and level 1 by the correlation kernel, levels 2..L by the level kernel
+    assert plan(d, wt.OP_BACKWARD_WEIGHT) == ["plane_dwc<5,bf16>", "plane_dwd<5,bf16>", "dw_finalize<5,bf16>"]
     d = wt.make_desc(64, 96, 56, 56, 5, 3, wt.F16)        # ... on the vector units for the other dtypes
     assert plan(d, wt.OP_FORWARD) == ["plane_fwd<5,f16>"]
+    assert plan(d, wt.OP_BACKWARD_WEIGHT) == ["plane_dwl<5,f16>", "plane_dwb<5,f16>", "dw_finalize<5,f16>"]
     d = wt.make_desc(64, 384, 14, 14, 5, 1, wt.BF16)      # ... and for narrow planes
     assert plan(d, wt.OP_FORWARD) == ["plane_fwd<5,bf16>"]
     d = wt.make_desc(64, 96, 56, 56, 7, 0, wt.BF16)       # levels = 0: the same kernel, base only
     assert plan(d, wt.OP_FORWARD) == ["plane_fwd<7,bf16>"]
-    assert plan(d, wt.OP_BACKWARD_WEIGHT) == ["plane_dwb<7,bf16>", "dw_finalize<7,bf16>"]
+    assert plan(d, wt.OP_BACKWARD_WEIGHT) == ["plane_dwc<7,bf16>", "dw_finalize<7,bf16>"]
     d = wt.make_desc(2, 4, 256, 256, 3, 2, wt.F32)         # per-level path (plane past 64x64)
     assert plan(d, wt.OP_FORWARD) == ["level_fwd<3,f32>#1", "level_fwd<3,f32>#2", "synth<3,f32>"]
     assert plan(d, wt.OP_BACKWARD_WEIGHT) == ["dw_level<3,f32>#1", "dw_level<3,f32>#2", "dw_base<3,f32>",

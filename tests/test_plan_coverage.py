@@ -47,26 +47,17 @@ def _sweep():
                     yield n, 4, h, w, k, L
 
 
-# families compiled for one activation dtype only
-ONLY = {"mma_fwd": ("bf16",)}
-
-
 def test_every_reachable_kernel_has_a_gpu_case(covered):
+    # bfloat16 plans differ from float32 plans (the matrix-core kernels are
+    # bfloat16 only, and a shape outside their range falls back to the vector
+    # kernels); IEEE half plans are those of float32
     reach = {}
-    # bfloat16 and float32 plans differ (the matrix-core forward kernel is bfloat16
-    # only); IEEE half plans are those of float32
     for n, c, h, w, k, L in _sweep():
-        for dt in ("bf16", "f32"):
-            for key in _plan_keys(n, c, h, w, k, L, dt):
-                reach.setdefault(key, (n, c, h, w, k, L, dt))
-    # otherwise the dtype only changes the storage type: a variant reached in one
-    # dtype is reached in every dtype
-    missing = []
-    for (name, variant), example in sorted(reach.items()):
-        fam, rest = name.split("<")
-        k = rest.split(",")[0]
-        for dt in ONLY.get(fam, tuple(DT)):
-            key = (f"{fam}<{k},{dt}>", variant)
-            if key not in covered:
-                missing.append((key, example))
+        for dt, as_dts in (("bf16", ("bf16",)), ("f32", ("f32", "f16"))):
+            for name, variant in _plan_keys(n, c, h, w, k, L, dt):
+                fam, rest = name.split("<")
+                kk = rest.split(",")[0]
+                for adt in as_dts:
+                    reach.setdefault((f"{fam}<{kk},{adt}>", variant), (n, c, h, w, k, L, dt))
+    missing = [(key, example) for key, example in sorted(reach.items()) if key not in covered]
     assert not missing, "kernels without a GPU parity case: " + "; ".join(f"{k} e.g. {e}" for k, e in missing[:20])
