@@ -268,7 +268,7 @@ struct PlaneDwlArgs {
 };
 
 template <int K, typename T, int CW, int RHD>
-__global__ __launch_bounds__(kDwlThreads, 3) void plane_dwl_kernel(PlaneDwlArgs a) {
+__device__ __forceinline__ void plane_dwl_body(const PlaneDwlArgs &a) {
     constexpr int R = (K - 1) / 2, KK = K * K;
     constexpr int NT = kDwlThreads;
     constexpr int WQ = (RHD + 2 * R + 3) / 4;  // 16-byte reads per window column
@@ -467,6 +467,17 @@ __global__ __launch_bounds__(kDwlThreads, 3) void plane_dwl_kernel(PlaneDwlArgs 
             a.partial[a.off[l] + ((size_t)c * a.k + r) * 4 * KK + b * KK + t0 + tap] = ldexpf(sum, -2 * (l + 1));
         }
     }
+}
+
+template <int K, typename T, int CW, int RHD>
+__global__ __launch_bounds__(kDwlThreads, 3) void plane_dwl_kernel(PlaneDwlArgs a) {
+    plane_dwl_body<K, T, CW, RHD>(a);
+}
+// The same kernel when the correlation kernel takes level 1 (a.lfirst = 1): only
+// levels 2..L have items; a symbol of its own, so that traces tell the two apart.
+template <int K, typename T, int CW, int RHD>
+__global__ __launch_bounds__(kDwlThreads, 3) void plane_dwd_kernel(PlaneDwlArgs a) {
+    plane_dwl_body<K, T, CW, RHD>(a);
 }
 
 }  // namespace wtc

@@ -206,9 +206,9 @@ int run_plane_dwl(const PlanSet &ps, const void *x, const void *dy, float *parti
     const size_t shm = (size_t)a.lds_floats * sizeof(float);
     const int bf = dtype_of<T>();  // dtype code, for the launch records
     // with the correlation kernel taking level 1, this launch covers levels 2..L
-    const char *fam = a.lfirst ? "plane_dwd" : "plane_dwl";
-#define WTC_DWL_LAUNCH(CW_, RH_) \
-    launch(fam, K, bf, 0, plane_dwl_kernel<K, T, CW_, RH_>, grid, dim3(kDwlThreads), shm, st, a)
+#define WTC_DWL_LAUNCH(CW_, RH_)                                                                                 \
+    (a.lfirst ? launch("plane_dwd", K, bf, 0, plane_dwd_kernel<K, T, CW_, RH_>, grid, dim3(kDwlThreads), shm, st, a) \
+              : launch("plane_dwl", K, bf, 0, plane_dwl_kernel<K, T, CW_, RH_>, grid, dim3(kDwlThreads), shm, st, a))
     switch (cfg.CW) {
         case 4: return WTC_DWL_LAUNCH(4, 4);
         case 2: return WTC_DWL_LAUNCH(2, 4);

@@ -71,7 +71,7 @@ def counters(fetch_db, write_db, copy_fetch_db, copy_write_db, copy_bytes):
 
 
 def _family(short: str) -> str:
-    """'wtc::fused_fwd_kernel<5, unsigned short, 8>' -> 'fused_fwd'."""
+    """'wtc::plane_fwd_kernel<5, unsigned short, 4, 7, false>' -> 'plane_fwd'."""
     return short.split("<")[0].split("::")[-1].removesuffix("_kernel")
 
 
@@ -91,6 +91,7 @@ def traffic(workload, fetch_db, write_db, copy_fetch_db, copy_write_db, copy_byt
     for r in rec["kernels"]:
         rows[(_family(r["kernel"]), r["grid"])].append(r)
     out = {}
+    got = collections.defaultdict(dict)
     allc = baseline_cases()
     for name in bench.WORKLOADS[workload]:
         c = allc[name]
@@ -114,11 +115,17 @@ def traffic(workload, fetch_db, write_db, copy_fetch_db, copy_write_db, copy_byt
                 grids = {g for (f, g) in rows if f == fam}
                 if len(grids) == 1:
                     match = rows[(fam, grids.pop())]
-            if not match or match[0]["write_bytes"] is None:
+            if not match or any(r["write_bytes"] is None for r in match):
                 continue
-            r = match[0]
-            out[e["name"]] = {"fetch_bytes": r["fetch_bytes"], "write_bytes": r["write_bytes"],
-                              "bytes": r["fetch_bytes"] + r["write_bytes"]}
+            for r in match:  # every compiled variant the launch matched (one per layer shape)
+                got[e["name"]][r["kernel"]] = r
+    # a name's record is the mean over its launches' rows (the layers of a stack that
+    # run the same kernel family, as bench.py averages their times)
+    for name, rs in got.items():
+        rs = list(rs.values())
+        fb = round(sum(r["fetch_bytes"] for r in rs) / len(rs))
+        wb = round(sum(r["write_bytes"] for r in rs) / len(rs))
+        out[name] = {"fetch_bytes": fb, "write_bytes": wb, "bytes": fb + wb, "variants": len(rs)}
     return {"workload": workload, "source_digest": bench.source_digest(),
             "fetch_scale": rec["fetch_scale"], "write_scale": rec["write_scale"], "kernels": out}
 
