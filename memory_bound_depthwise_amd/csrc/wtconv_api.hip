@@ -397,6 +397,8 @@ bool mma_layout(const wtconv_desc &d, int CW, int pb, MmaArgs &a) {
     a.TX = cdiv(Wc, 16);
     a.tiles = TY * a.TX;
     a.commit_items = pb * a.H1 * a.Gw;
+    a.H2 = (a.H1 + 1) / 2;
+    a.pair_items = pb * a.H2 * a.Gw;
     if (a.commit_items >= 32768 || a.tiles >= 32768) return false;
     if ((long long)pb * d.c * d.h * d.w >= (1LL << 31)) return false;
     // canvas: bfloat16 pixels, row y of the strip at canvas row ROW0 + y, column x at
@@ -430,14 +432,12 @@ bool mma_layout(const wtconv_desc &d, int CW, int pb, MmaArgs &a) {
         a.offq[li] = (int)fl;
         fl += ((2LL * hs[l] * a.sq[li]) + 3) & ~3LL;
     }
-    if (L >= 2 && 2LL * hs[2] * (a.sq[0] / 4) >= 65536) return false;
     a.wt = (int)fl;
     fl += ((4LL * L + 1) * KK + 1 + 3) & ~3LL;
     a.zero_floats = (int)fl;
     a.tab = (int)fl;
     fl += (kPlaneTabFields * std::max(L - 1, 0) + 3) & ~3;
-    // the tiles read Q_2 (bias and deeper patterns added) at every tile cell, also
-    // past the plane; Q_2 takes them over its own rows and columns
+    // the tiles read the deep patterns of every tile cell, also past the plane
     for (int l = 2; l <= L; ++l) {
         const int li = l - 2;
         const long long end = a.offq[li] + (long long)((4 * TY - 1) >> li) * a.sq[li] + ((16 * a.TX - 1) >> li) + 1;
@@ -449,7 +449,7 @@ bool mma_layout(const wtconv_desc &d, int CW, int pb, MmaArgs &a) {
     a.m_h1 = magic31_of(a.H1);
     a.m_tx = magic31_of(a.TX);
     a.m_pw1 = magic31_of(a.Pw1);
-    a.m_q4 = magic31_of(L >= 2 ? a.sq[0] / 4 : 1);
+    a.m_h2 = magic31_of(a.H2);
     for (int l = 2; l <= L; ++l) a.m_wls[l - 2] = magic31_of(a.wls[l - 2]);
     return true;
 }

@@ -91,6 +91,7 @@ struct MmaArgs {
     int H1, W1;      // level-1 grid of one plane
     int Gw;          // commit column groups of CW cells per level-1 row
     int commit_items;
+    int H2, pair_items;  // level-2 rows ceil(H1 / 2); commit items of two stacked patches (PB H2 Gw)
     int S;           // canvas row stride (dwords)
     int TX, tiles;   // product tiles per tile row, in all
     int sy1;         // (unused: level 2 is analysed from the canvas)
@@ -104,7 +105,7 @@ struct MmaArgs {
     int zero_floats;  // floats cleared at the start (canvas, bands, patterns, weights)
     int tab;          // deep-level geometry table
     int lds_floats;
-    uint32_t m_gw, m_h1, m_tx, m_pw1, m_q4;  // udiv16 reciprocals of Gw, H1, TX, Pw1, sq[0] / 4
+    uint32_t m_gw, m_h1, m_tx, m_pw1, m_h2;  // udiv16 reciprocals of Gw, H1, TX, Pw1, H2
     uint32_t m_wls[kMaxLevels];
 };
 
@@ -188,6 +189,27 @@ __device__ __forceinline__ void mma_fwd_body(const MmaArgs &args) {
         return lb < 4 * A.L ? A.wt + ((lb >> 2) * KK + tap) * 4 + (lb & 3) : A.wt + 4 * A.L * KK + (lb - 4 * A.L) * KK + tap;
     };
 
+    // With CW >= 2 and levels >= 2, a commit item is two patches stacked, pixel rows
+    // 4a .. 4a + 3 of 2CW columns: the lane that commits them also forms the level-2
+    // bands of their CW / 2 level-2 cells (no separate analysis pass).
+    constexpr bool kPair = CW >= 2;
+    static_assert(!kPair || SLOTS % 2 == 0, "pairs of patches in the prefetch registers");
+    const bool fold = kPair && a0.L >= 2;
+    auto pair_of = [&](const auto &A, int d, int &p, int &a, int &m) {
+        const int q = udiv16(d, A.m_gw);
+        m = d - q * A.Gw;
+        p = udiv16(q, A.m_h2);
+        a = q - p * A.H2;
+    };
+    // the two patches of pair item d (the second past the plane when H1 is odd: its
+    // loads repeat the first's rows, and it is cleared at the commit)
+    auto load_pair = [&](const auto &A, uint32_t (&r0)[2][IO::kWords], uint32_t (&r1)[2][IO::kWords], const T *xb,
+                         int live, int d) {
+        int p, a, m;
+        pair_of(A, min(d, A.pair_items - 1), p, a, m);
+        load_patch_clamped<T, CW>(r0, xb, p, 2 * a, m, live, CHW, A.H, A.W, A.vec);
+        load_patch_clamped<T, CW>(r1, xb, p, min(2 * a + 1, A.H1 - 1), m, live, CHW, A.H, A.W, A.vec);
+    };
     uint32_t raw[SLOTS][2][IO::kWords];
     float wf0[WSLOTS], wf1[WSLOTS];
     auto prefetch = [&](const auto &A, int u) {
@@ -195,8 +217,13 @@ __device__ __forceinline__ void mma_fwd_body(const MmaArgs &args) {
         unit_of(A, u, c, n0);
         const int live = min(A.PB, A.n - n0);
         const T *xb = static_cast<const T *>(A.x) + ((size_t)n0 * A.C + c) * HW;
+        if (kPair && A.L >= 2) {
 #pragma unroll
-        for (int k = 0; k < SLOTS; ++k) load_patch(A, raw[k], xb, live, tid + k * NT);
+            for (int k = 0; k < SLOTS / 2; ++k) load_pair(A, raw[2 * k], raw[2 * k + 1], xb, live, tid + k * NT);
+        } else {
+#pragma unroll
+            for (int k = 0; k < SLOTS; ++k) load_patch(A, raw[k], xb, live, tid + k * NT);
+        }
 #pragma unroll
         for (int k = 0; k < WSLOTS; ++k) weight_factors(A, c, min(tid + k * NT, (4 * A.L + 1) * KK), wf0[k], wf1[k]);
     };
@@ -245,23 +272,67 @@ __device__ __forceinline__ void mma_fwd_body(const MmaArgs &args) {
                     }
                 }
             };
-#pragma unroll
-            for (int k = 0; k < SLOTS; ++k) {
-                const int g = tid + k * NT;
-                if (g >= a.commit_items) continue;
-                int p, i, m;
-                patch_of(a, g, p, i, m);
-                mask_patch<T, CW>(raw[k], p, i, live, H, full);
-                put(raw[k], p, i, m);
-            }
             const T *xb = static_cast<const T *>(a.x) + ((size_t)n0 * a.C + c) * HW;
-            for (int g = tid + SLOTS * NT; g < a.commit_items; g += NT) {
-                uint32_t r[2][IO::kWords];
-                load_patch(a, r, xb, live, g);
-                int p, i, m;
-                patch_of(a, g, p, i, m);
-                mask_patch<T, CW>(r, p, i, live, H, full);
-                put(r, p, i, m);
+            if (fold) {
+                // level-2 cell e of a pair: the butterflies of the low-pass sums of its
+                // four level-1 cells (pixel rows 4a .. 4a + 3, columns 4e .. 4e + 3)
+                const int ds = opaque(a.syd[0]);
+                float4 *l2 = s4 + opaque(a.offd[0]);
+                auto put_pair = [&](uint32_t (&r0)[2][IO::kWords], uint32_t (&r1)[2][IO::kWords], int d) {
+                    int p, aa, m;
+                    pair_of(a, d, p, aa, m);
+                    mask_patch<T, CW>(r0, p, 2 * aa, live, H, full);
+                    mask_patch<T, CW>(r1, p, 2 * aa + 1, live, H, full);
+                    if (2 * aa + 1 >= a.H1) {
+#pragma unroll
+                        for (int w = 0; w < IO::kWords; ++w) r1[0][w] = r1[1][w] = 0u;
+                    }
+                    put(r0, p, 2 * aa, m);
+                    if (2 * aa + 1 < a.H1) put(r1, p, 2 * aa + 1, m);
+                    float4 *dst = l2 + (aa + R) * ds + kPlaneCO + ((p * pw1 + CW * m) >> 1);
+#pragma unroll
+                    for (int e = 0; e < CW / 2; ++e) {
+                        float cs[2][2];
+#pragma unroll
+                        for (int cc = 0; cc < 2; ++cc) {
+                            const uint32_t t0 = r0[0][2 * e + cc], t1 = r0[1][2 * e + cc];
+                            const uint32_t t2 = r1[0][2 * e + cc], t3 = r1[1][2 * e + cc];
+                            cs[0][cc] = (Act<T>::lo(t0) + Act<T>::hi(t0)) + (Act<T>::lo(t1) + Act<T>::hi(t1));
+                            cs[1][cc] = (Act<T>::lo(t2) + Act<T>::hi(t2)) + (Act<T>::lo(t3) + Act<T>::hi(t3));
+                        }
+                        const float s0 = cs[0][0] + cs[0][1], s1 = cs[1][0] + cs[1][1];
+                        const float d0 = cs[0][0] - cs[0][1], d1 = cs[1][0] - cs[1][1];
+                        dst[e] = make_float4(s0 + s1, s0 - s1, d0 + d1, d0 - d1);
+                    }
+                };
+#pragma unroll
+                for (int k = 0; k < SLOTS / 2; ++k) {
+                    const int d = tid + k * NT;
+                    if (d < a.pair_items) put_pair(raw[2 * k], raw[2 * k + 1], d);
+                }
+                for (int d = tid + (SLOTS / 2) * NT; d < a.pair_items; d += NT) {  // beyond the registers
+                    uint32_t r0[2][IO::kWords], r1[2][IO::kWords];
+                    load_pair(a, r0, r1, xb, live, d);
+                    put_pair(r0, r1, d);
+                }
+            } else {
+#pragma unroll
+                for (int k = 0; k < SLOTS; ++k) {
+                    const int g = tid + k * NT;
+                    if (g >= a.commit_items) continue;
+                    int p, i, m;
+                    patch_of(a, g, p, i, m);
+                    mask_patch<T, CW>(raw[k], p, i, live, H, full);
+                    put(raw[k], p, i, m);
+                }
+                for (int g = tid + SLOTS * NT; g < a.commit_items; g += NT) {
+                    uint32_t r[2][IO::kWords];
+                    load_patch(a, r, xb, live, g);
+                    int p, i, m;
+                    patch_of(a, g, p, i, m);
+                    mask_patch<T, CW>(r, p, i, live, H, full);
+                    put(r, p, i, m);
+                }
             }
         }
         __syncthreads();
@@ -272,64 +343,34 @@ __device__ __forceinline__ void mma_fwd_body(const MmaArgs &args) {
 
         {
             // 2. level 2 from the pixels (a level-2 cell is a 4 x 4 pixel block: the
-            //    butterflies of the low-pass sums of its four level-1 cells), then
-            //    levels 3..L from the low-pass band above; 3. the deep patterns
+            //    butterflies of the low-pass sums of its four level-1 cells; formed at
+            //    the commit for CW >= 2), then levels 3..L from the low-pass band
+            //    above; 3. the deep patterns
             if (L >= 2) {
-                const int Wls = a.wls[0], ds = a.syd[0];
-                float4 *dst = s4 + a.offd[0];
-                for (int q = tid; q < a.hl[0] * Wls; q += NT) {
-                    const int i = udiv16(q, a.m_wls[0]), j = q - i * Wls;
-                    const uint32_t *sp = cv + (G::ROW0 + 4 * i) * S + kMmaCL / 2 + 2 * j;
-                    float cs[4][2];  // low-pass sums of the 2 x 2 level-1 cells, by (row, column)
+                if (!fold) {
+                    const int Wls = a.wls[0], ds = a.syd[0];
+                    float4 *dst = s4 + a.offd[0];
+                    for (int q = tid; q < a.hl[0] * Wls; q += NT) {
+                        const int i = udiv16(q, a.m_wls[0]), j = q - i * Wls;
+                        const uint32_t *sp = cv + (G::ROW0 + 4 * i) * S + kMmaCL / 2 + 2 * j;
+                        float cs[2][2];  // low-pass sums of the 2 x 2 level-1 cells, by (row, column)
 #pragma unroll
-                    for (int h = 0; h < 2; ++h) {
-                        const uint2 t0 = *reinterpret_cast<const uint2 *>(sp + (2 * h) * S);
-                        const uint2 t1 = *reinterpret_cast<const uint2 *>(sp + (2 * h + 1) * S);
-                        cs[h][0] = (Act<T>::lo(t0.x) + Act<T>::hi(t0.x)) + (Act<T>::lo(t1.x) + Act<T>::hi(t1.x));
-                        cs[h][1] = (Act<T>::lo(t0.y) + Act<T>::hi(t0.y)) + (Act<T>::lo(t1.y) + Act<T>::hi(t1.y));
+                        for (int h = 0; h < 2; ++h) {
+                            const uint2 t0 = *reinterpret_cast<const uint2 *>(sp + (2 * h) * S);
+                            const uint2 t1 = *reinterpret_cast<const uint2 *>(sp + (2 * h + 1) * S);
+                            cs[h][0] = (Act<T>::lo(t0.x) + Act<T>::hi(t0.x)) + (Act<T>::lo(t1.x) + Act<T>::hi(t1.x));
+                            cs[h][1] = (Act<T>::lo(t0.y) + Act<T>::hi(t0.y)) + (Act<T>::lo(t1.y) + Act<T>::hi(t1.y));
+                        }
+                        const float x00 = cs[0][0], x01 = cs[0][1], x10 = cs[1][0], x11 = cs[1][1];
+                        const float s0 = x00 + x01, s1 = x10 + x11, d0 = x00 - x01, d1 = x10 - x11;
+                        dst[(i + R) * ds + j + kPlaneCO] = make_float4(s0 + s1, s0 - s1, d0 + d1, d0 - d1);
                     }
-                    const float x00 = cs[0][0], x01 = cs[0][1], x10 = cs[1][0], x11 = cs[1][1];
-                    const float s0 = x00 + x01, s1 = x10 + x11, d0 = x00 - x01, d1 = x10 - x11;
-                    dst[(i + R) * ds + j + kPlaneCO] = make_float4(s0 + s1, s0 - s1, d0 + d1, d0 - d1);
+                    __syncthreads();
                 }
-                __syncthreads();
                 haar_levels<K>(a, s4, 3, tid, NT);
                 deep_patterns<K>(a, s4, smem, tab, tid, NT);
-                // Q_2 (level-1 resolution) takes the bias and the patterns of levels
-                // 3..L, so that a tile reads one float4 per lane; four cells per item
-                {
-                    const float bias = smem[a.wt + (4 * L + 1) * KK];
-                    int qo[kMaxLevels - 1], qs[kMaxLevels - 1];
-#pragma unroll
-                    for (int k = 0; k < kMaxLevels - 1; ++k) {
-                        qo[k] = opaque(a.offq[k]);
-                        qs[k] = opaque(a.sq[k]);
-                    }
-                    const int q4 = qs[0] >> 2;
-                    for (int it = tid; it < 2 * a.hl[0] * q4; it += NT) {
-                        const int r = udiv16(it, a.m_q4), c = 4 * (it - r * q4);
-                        float4 *d = reinterpret_cast<float4 *>(smem + qo[0] + r * qs[0] + c);
-                        float4 v = *d;
-                        v.x += bias;
-                        v.y += bias;
-                        v.z += bias;
-                        v.w += bias;
-#pragma unroll
-                        for (int k = 1; k < kMaxLevels - 1; ++k) {
-                            if (k >= L - 1) break;
-                            const float *qr = smem + qo[k] + __umul24(r >> k, qs[k]);
-                            v.x += qr[c >> k];
-                            v.y += qr[(c + 1) >> k];
-                            v.z += qr[(c + 2) >> k];
-                            v.w += qr[(c + 3) >> k];
-                        }
-                        *d = v;
-                    }
-                }
-                __syncthreads();
             }
         }
-
 
         // B fragments, when the channel changes (wave-uniform)
         if (c != cur_c) {
@@ -394,7 +435,14 @@ __device__ __forceinline__ void mma_fwd_body(const MmaArgs &args) {
         const float bias = smem[a.wt + (4 * L + 1) * KK];
         const int rp = mm >> 2, ry = mm & 1, rx = (mm >> 1) & 1;
         const int smode = opaque(a.store_mode), pw1 = opaque(a.Pw1), W1 = opaque(a.W1);
-        const int q2off = opaque(a.offq[0]), q2s = opaque(a.sq[0]);
+        // deep patterns of levels 2..L at level-1 resolution: Q_l of cell (row, col)
+        // at (row >> (l - 2), col >> (l - 2)); the offsets and strides held uniform
+        int qo[kMaxLevels - 1], qs[kMaxLevels - 1];
+#pragma unroll
+        for (int k = 0; k < kMaxLevels - 1; ++k) {
+            qo[k] = opaque(a.offq[k]);
+            qs[k] = opaque(a.sq[k]);
+        }
         // Two tiles per iteration (t and t + NT / kWave; the second may repeat the
         // first, then it stores nothing): their products and LDS reads are
         // independent, which hides the latency of each.
@@ -427,7 +475,27 @@ __device__ __forceinline__ void mma_fwd_body(const MmaArgs &args) {
             const int ty = udiv16(t, a.m_tx), tx = t - ty * a.TX;
             const int crow = 4 * ty + rp, cs0 = 16 * tx + 4 * g4;
             float4 dz = make_float4(bias, bias, bias, bias);
-            if (L >= 2) dz = *reinterpret_cast<const float4 *>(smem + q2off + __umul24(crow, q2s) + cs0);
+            if (L >= 2) {
+                // levels 2 and 3 (and 4) read unconditionally, a level past L from the
+                // level-2 array with its value discarded, so that the reads overlap
+                const float4 q2 = *reinterpret_cast<const float4 *>(smem + qo[0] + __umul24(crow, qs[0]) + cs0);
+                const bool l3 = L >= 3, l4 = L >= 4;
+                const float2 q3 = *reinterpret_cast<const float2 *>(
+                    smem + (l3 ? qo[1] + __umul24(crow >> 1, qs[1]) + (cs0 >> 1) : qo[0]));
+                const float q4 = smem[l4 ? qo[2] + __umul24(crow >> 2, qs[2]) + (cs0 >> 2) : qo[0]];
+                const float v3x = l3 ? q3.x : 0.f, v3y = l3 ? q3.y : 0.f, v4 = l4 ? q4 : 0.f;
+                dz.x += q2.x + (v3x + v4);
+                dz.y += q2.y + (v3x + v4);
+                dz.z += q2.z + (v3y + v4);
+                dz.w += q2.w + (v3y + v4);
+                for (int k = 3; k < L - 1; ++k) {  // levels 5..L: one value for the four cells
+                    const float v = smem[qo[k] + __umul24(crow >> k, qs[k]) + (cs0 >> k)];
+                    dz.x += v;
+                    dz.y += v;
+                    dz.z += v;
+                    dz.w += v;
+                }
+            }
             float y[4] = {(dh[0] + dl[0]) + dz.x, (dh[1] + dl[1]) + dz.y, (dh[2] + dl[2]) + dz.z, (dh[3] + dl[3]) + dz.w};
             // pair the two pixel columns (lane ^ 2 holds the other rx): rx = 0 keeps
             // cells cs0, cs0 + 1, rx = 1 cells cs0 + 2, cs0 + 3, four pixels in a row
