@@ -14,7 +14,11 @@ stack at batch 128 (forward of layers 1..4, then the backward of layers 4..1).
   only their inputs and outputs) are reported next to it.
 * `ms_per_step`: one forward + backward of the workload's layers; the per-step
   event times also give `ms_per_step_median`, and each pass is timed on its own
-  (`per_pass_ms`).
+  (`per_pass_ms`).  Launches are eager: the host enqueues the step's kernels
+  faster than they run, so the gaps between them are a few microseconds.  With
+  `--graph` the step is captured once per buffer set as a HIP graph
+  (torch.cuda.graph around the same library calls) and the replays are timed;
+  `eager_ms_per_step` then reports eager launches next to them.
 Inputs are resident in device memory before the timed region; `--rotate` buffer
 sets (default 3) are cycled so consecutive steps do not find their inputs in the
 256 MB last-level cache.
@@ -255,6 +259,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="stack", choices=sorted(WORKLOADS))
     ap.add_argument("--rotate", type=int, default=3)
+    ap.add_argument("--graph", action="store_true",
+                    help="time replays of the step captured as a HIP graph instead of eager launches")
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-budget", type=float, default=30.0, help="seconds for the oracle leg")
     ap.add_argument("--copy-probe", type=int, default=0, metavar="MIB",
@@ -310,11 +316,31 @@ def main():
         run_step(layers, i, wt)
     torch.cuda.synchronize()
 
+    # one HIP graph per rotating buffer set, each holding a whole step (every launch
+    # of the forward, input-gradient and weight-gradient passes of every layer)
+    graphs = []
+    if args.graph:
+        for r in range(args.rotate):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g):
+                run_step(layers, r, wt)
+            graphs.append(g)
+        for i in range(args.warmup):
+            graphs[i % len(graphs)].replay()
+        torch.cuda.synchronize()
+    step_fn = (lambda i: graphs[i % len(graphs)].replay()) if graphs else (lambda i: run_step(layers, i, wt))
+
     # timed region: exactly `steps` steps, synchronised on both sides
-    wall_ms, step_ms = timed(lambda i: run_step(layers, i, wt), args.steps, torch)
+    wall_ms, step_ms = timed(step_fn, args.steps, torch)
     gpu_ms = sum(step_ms)
     ms_per_step = max(wall_ms, gpu_ms) / args.steps
-    print(f"# timed {args.steps} steps: {ms_per_step:.4f} ms/step", file=sys.stderr, flush=True)
+    print(f"# timed {args.steps} steps ({'graph replay' if graphs else 'eager'}): "
+          f"{ms_per_step:.4f} ms/step", file=sys.stderr, flush=True)
+    eager_ms = None
+    if graphs:
+        # the same steps as eager launches, for comparison
+        ew, es_ms = timed(lambda i: run_step(layers, i, wt), args.steps, torch)
+        eager_ms = max(ew, sum(es_ms)) / args.steps
 
     # each pass on its own (forward of every layer, then input gradients, then weight gradients)
     per_pass = {}
@@ -400,10 +426,12 @@ def main():
         "dtype": cases[0].dtype,
         "data": "synthetic",
         "config": {"workload": args.workload, "shapes": describe(cases), "pass": "forward + dx + dW",
-                   "rotate_buffer_sets": args.rotate, "model_step_bytes": model["step"],
+                   "rotate_buffer_sets": args.rotate, "launch": "hip_graph" if graphs else "eager",
+                   "model_step_bytes": model["step"],
                    "moved_step_bytes": moved_bytes, "step_flops": step_flops},
         "hbm_frac": round(value / HBM_PEAK_GBS, 4),
         "ms_per_step_median": round(statistics.median(step_ms), 5),
+        "eager_ms_per_step": None if eager_ms is None else round(eager_ms, 5),
         "per_pass_ms": per_pass,
         "moved_bytes": {"gbs": round(moved_gbs, 1), "hbm_frac": round(moved_gbs / HBM_PEAK_GBS, 4),
                         "note": "bytes the launched kernels must move (plane-resident kernels: inputs and "

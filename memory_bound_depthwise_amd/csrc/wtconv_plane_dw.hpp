@@ -304,7 +304,9 @@ __device__ __forceinline__ void plane_dwl_body(const PlaneDwlArgs &a) {
         load_patch_clamped<T, CW>(rw, base, p, i, m, live, CHW, a.H, a.W, a.vec);
     };
     // level-1 bands of a patch's CW cells: element (row, col + q) of each band
-    // (column stride cs, band size bs)
+    // (column stride cs, band size bs); without level-1 items only the low-pass band,
+    // which the level-2 analysis reads
+    const bool lp_only = a.lfirst > 0;
     auto store_bands = [&](float *base, int cs, int bs, const uint32_t (&rw)[2][IO::kWords], int row, int col) {
 #pragma unroll
         for (int q = 0; q < CW; ++q) {
@@ -313,6 +315,7 @@ __device__ __forceinline__ void plane_dwl_body(const PlaneDwlArgs &a) {
             const float s0 = x00 + x01, s1 = x10 + x11, d0 = x00 - x01, d1 = x10 - x11;
             float *d = base + (col + q) * cs + row;
             d[0] = s0 + s1;
+            if (lp_only) continue;
             d[bs] = s0 - s1;
             d[2 * bs] = d0 + d1;
             d[3 * bs] = d0 - d1;
