@@ -34,10 +34,10 @@
 // bfloat16 x with hi and lo are exact in the fp32 accumulation), so the weights
 // carry ~16 significant bits.
 //
-// After the products, a lane holds pixel (ry, rx) of four consecutive cells of one
-// cell row; the deeper levels' patterns and the bias enter every pixel of a block
-// with a plus sign (they come in through the LL band).  One DPP exchange pairs the
-// two pixel columns, and y is stored four pixels per lane.
+// The product is taken transposed (B as the left operand), so that a lane receives
+// the four pixels of one cell; the deeper levels' patterns and the bias enter every
+// pixel of a cell with a plus sign (they come in through the LL band), so a lane adds
+// one value to its four pixels and stores them as two pixel pairs.
 //
 // Deeper levels (l >= 2) stay on the vector units, as in wtconv_plane.hpp: level 2
 // is analysed from the pixels (its cells are 4 x 4 pixel blocks), levels 3..L from
@@ -109,11 +109,6 @@ struct MmaArgs {
     uint32_t m_wls[kMaxLevels];
 };
 
-template <int CTRL>
-__device__ __forceinline__ float dpp_quad(float v) {
-    return __int_as_float(__builtin_amdgcn_update_dpp(0, __float_as_int(v), CTRL, 0xF, 0xF, false));
-}
-
 template <int K, int CW>
 __device__ __forceinline__ void mma_fwd_body(const MmaArgs &args) {
     using G = MmaGeom<K>;
@@ -127,7 +122,8 @@ __device__ __forceinline__ void mma_fwd_body(const MmaArgs &args) {
     float4 *s4 = reinterpret_cast<float4 *>(smem);
     uint32_t *cv = reinterpret_cast<uint32_t *>(smem);  // the canvas: bfloat16 pixel pairs
     const MmaArgs &a0 = args;
-    const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave;
+    const int tid = threadIdx.x, lane = tid & (kWave - 1);
+    const int wave = __builtin_amdgcn_readfirstlane(tid / kWave);
     const int HW = a0.H * a0.W, CHW = a0.C * HW;
 
     for (int i = tid * 4; i < a0.zero_floats; i += NT * 4)
@@ -430,110 +426,103 @@ __device__ __forceinline__ void mma_fwd_body(const MmaArgs &args) {
             }
         }
 
-        // 4. products and stores, one tile of 16 x 4 cells at a time
+        // 4. products and stores, one tile of 16 x 4 cells at a time.  The product is
+        //    formed transposed (the B fragments as the left operand, the pixel
+        //    fragments as the right one), so that lane (g4, mm) receives the four
+        //    pixels of cell (4 ty + g4, 16 tx + mm): element i = 2 rx + ry.
         T *yb = static_cast<T *>(a.y) + ((size_t)n0 * a.C + c) * HW;
         const float bias = smem[a.wt + (4 * L + 1) * KK];
-        const int rp = mm >> 2, ry = mm & 1, rx = (mm >> 1) & 1;
         const int smode = opaque(a.store_mode), pw1 = opaque(a.Pw1), W1 = opaque(a.W1);
-        // deep patterns of levels 2..L at level-1 resolution: Q_l of cell (row, col)
-        // at (row >> (l - 2), col >> (l - 2)); the offsets and strides held uniform
-        int qo[kMaxLevels - 1], qs[kMaxLevels - 1];
+        // deep patterns: Q_l of cell (row, col) at (row >> j, col >> j), j = l - 2,
+        // split into a wave-uniform part (tile origin) and the lane's part; a level
+        // past L reads canvas row 0, which is zero padding throughout
+        int qo[kMaxLevels - 1], qs[kMaxLevels - 1], ql[3];
 #pragma unroll
         for (int k = 0; k < kMaxLevels - 1; ++k) {
-            qo[k] = opaque(a.offq[k]);
-            qs[k] = opaque(a.sq[k]);
+            const bool on = k + 2 <= L;
+            qo[k] = on ? opaque(a.offq[k]) : 0;
+            qs[k] = on ? opaque(a.sq[k]) : 0;
         }
-        // Two tiles per iteration (t and t + NT / kWave; the second may repeat the
-        // first, then it stores nothing): their products and LDS reads are
-        // independent, which hides the latency of each.
-        auto products = [&](int t, wtc_f32x4 &dh, wtc_f32x4 &dl) {
-            const int ty = udiv16(t, a.m_tx), tx = t - ty * a.TX;
-            // canvas row 2 ci0 is window row 0; this lane's A row is cell column cj0 + mm
-            const uint32_t *wp = cv + (8 * ty) * S + (kMmaCL - G::COL0) / 2 + 16 * tx + mm;
+#pragma unroll
+        for (int j = 0; j < 3; ++j) ql[j] = (g4 >> j) * qs[j] + (mm >> j);
+        // the lane's A reads: row g4 of the window's step, cell column mm
+        const int la = (kMmaCL - G::COL0) / 2 + g4 * S + mm;
+        constexpr int NW = NT / kWave;
+        // two tiles per iteration (t and t + NW; the second may repeat the first, then
+        // it stores nothing): their MFMA chains and LDS reads are independent
+        for (int t = wave; t < a.tiles; t += 2 * NW) {
+            const int t2 = t + NW < a.tiles ? t + NW : t;
+            int ty[2], tx[2];
+            ty[0] = udiv16(t, a.m_tx);
+            tx[0] = t - ty[0] * a.TX;
+            ty[1] = udiv16(t2, a.m_tx);
+            tx[1] = t2 - ty[1] * a.TX;
+            wtc_f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
+            const uint32_t *wp[2] = {cv + la + (8 * ty[0]) * S + 16 * tx[0], cv + la + (8 * ty[1]) * S + 16 * tx[1]};
 #pragma unroll
             for (int s = 0; s < G::NSF; ++s) {
-                const int q = 4 * s + g4;
-                const uint32_t *p = wp + q * S;
-                union { wtc_bf16x8 v; uint32_t w[4]; } A;
-                A.w[0] = p[0];
-                A.w[1] = p[1];
-                A.w[2] = p[2];
-                A.w[3] = p[3];
-                dh = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A.v, bh[s], dh, 0, 0, 0);
-                dl = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A.v, bl[s], dl, 0, 0, 0);
-            }
-            if constexpr (G::TAIL) {
-                union { wtc_bf16x8 v; uint32_t w[4]; } A;
+                union { wtc_bf16x8 v; uint32_t w[4]; } A[2];
 #pragma unroll
-                for (int e = 0; e < 4; ++e) A.w[e] = wp[(g4 + 4 * e) * S + 4];
-                dh = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A.v, bh[G::NSF], dh, 0, 0, 0);
-                dl = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A.v, bl[G::NSF], dl, 0, 0, 0);
-            }
-        };
-        // lane: D column = pixel (ry, rx) of cell row rp, D rows r = cell columns cs0 + r
-        auto finish = [&](int t, const wtc_f32x4 &dh, const wtc_f32x4 &dl, bool store) {
-            const int ty = udiv16(t, a.m_tx), tx = t - ty * a.TX;
-            const int crow = 4 * ty + rp, cs0 = 16 * tx + 4 * g4;
-            float4 dz = make_float4(bias, bias, bias, bias);
-            if (L >= 2) {
-                // levels 2 and 3 (and 4) read unconditionally, a level past L from the
-                // level-2 array with its value discarded, so that the reads overlap
-                const float4 q2 = *reinterpret_cast<const float4 *>(smem + qo[0] + __umul24(crow, qs[0]) + cs0);
-                const bool l3 = L >= 3, l4 = L >= 4;
-                const float2 q3 = *reinterpret_cast<const float2 *>(
-                    smem + (l3 ? qo[1] + __umul24(crow >> 1, qs[1]) + (cs0 >> 1) : qo[0]));
-                const float q4 = smem[l4 ? qo[2] + __umul24(crow >> 2, qs[2]) + (cs0 >> 2) : qo[0]];
-                const float v3x = l3 ? q3.x : 0.f, v3y = l3 ? q3.y : 0.f, v4 = l4 ? q4 : 0.f;
-                dz.x += q2.x + (v3x + v4);
-                dz.y += q2.y + (v3x + v4);
-                dz.z += q2.z + (v3y + v4);
-                dz.w += q2.w + (v3y + v4);
-                for (int k = 3; k < L - 1; ++k) {  // levels 5..L: one value for the four cells
-                    const float v = smem[qo[k] + __umul24(crow >> k, qs[k]) + (cs0 >> k)];
-                    dz.x += v;
-                    dz.y += v;
-                    dz.z += v;
-                    dz.w += v;
+                for (int h = 0; h < 2; ++h) {
+                    const uint32_t *q = wp[h] + 4 * s * S;
+                    A[h].w[0] = q[0];
+                    A[h].w[1] = q[1];
+                    A[h].w[2] = q[2];
+                    A[h].w[3] = q[3];
                 }
-            }
-            float y[4] = {(dh[0] + dl[0]) + dz.x, (dh[1] + dl[1]) + dz.y, (dh[2] + dl[2]) + dz.z, (dh[3] + dl[3]) + dz.w};
-            // pair the two pixel columns (lane ^ 2 holds the other rx): rx = 0 keeps
-            // cells cs0, cs0 + 1, rx = 1 cells cs0 + 2, cs0 + 3, four pixels in a row
-            const float snd0 = rx ? y[0] : y[2], snd1 = rx ? y[1] : y[3];
-            const float rcv0 = dpp_quad<0x4E>(snd0), rcv1 = dpp_quad<0x4E>(snd1);
-            const float o0 = rx ? rcv0 : y[0], o1 = rx ? y[2] : rcv0;
-            const float o2 = rx ? rcv1 : y[1], o3 = rx ? y[3] : rcv1;
-            const int p = udiv16(cs0, a.m_pw1);
-            const int jc = cs0 - p * pw1 + 2 * rx;  // first cell of the four pixels
-            const int pr = 2 * crow + ry;
-            if (store && p < live && pr < H && jc < W1) {
-                T *dst = yb + (p * CHW + pr * W + 2 * jc);
-                if (smode == 2) {
-                    *reinterpret_cast<uint2 *>(dst) = make_uint2(Act<T>::pack(o0, o1), Act<T>::pack(o2, o3));
-                } else {
-                    const float oo[4] = {o0, o1, o2, o3};
 #pragma unroll
-                    for (int h = 0; h < 2; ++h) {
-                        const int col = 2 * (jc + h);
-                        if (jc + h >= W1) break;
-                        if (smode == 1) {
-                            *reinterpret_cast<uint32_t *>(dst + 2 * h) = Act<T>::pack(oo[2 * h], oo[2 * h + 1]);
-                        } else {
-                            act_store(dst, 2 * h, oo[2 * h]);
-                            if (col + 1 < W) act_store(dst, 2 * h + 1, oo[2 * h + 1]);
+                for (int h = 0; h < 2; ++h) acc[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bh[s], A[h].v, acc[h], 0, 0, 0);
+#pragma unroll
+                for (int h = 0; h < 2; ++h) acc[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bl[s], A[h].v, acc[h], 0, 0, 0);
+            }
+            if constexpr (G::TAIL) {  // window columns 8, 9 of rows g4 + 4 e
+                union { wtc_bf16x8 v; uint32_t w[4]; } A[2];
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) A[h].w[e] = wp[h][4 * e * S + 4];
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+                    acc[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bh[G::NSF], A[h].v, acc[h], 0, 0, 0);
+#pragma unroll
+                for (int h = 0; h < 2; ++h)
+                    acc[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bl[G::NSF], A[h].v, acc[h], 0, 0, 0);
+            }
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                if (h == 1 && t2 == t) break;
+                const int crow = 4 * ty[h] + g4, ccol = 16 * tx[h] + mm;
+                // bias and the deep patterns (they enter all four pixels of the cell)
+                float v = bias;
+                {
+                    float q[3];
+#pragma unroll
+                    for (int j = 0; j < 3; ++j) q[j] = smem[qo[j] + ((4 * ty[h]) >> j) * qs[j] + ((16 * tx[h]) >> j) + ql[j]];
+                    v += q[0] + (q[1] + q[2]);
+                    for (int k = 3; k < L - 1; ++k)  // levels 5..L
+                        v += smem[qo[k] + (crow >> k) * qs[k] + (ccol >> k)];
+                }
+                const int p = udiv16(ccol, a.m_pw1);
+                const int jc = ccol - p * pw1;
+                const int pr = 2 * crow;
+                if (p < live && jc < W1 && pr < H) {
+                    const float o0 = acc[h][0] + v, o1 = acc[h][1] + v, o2 = acc[h][2] + v, o3 = acc[h][3] + v;
+                    T *dst = yb + (p * CHW + pr * W + 2 * jc);
+                    const bool row1 = pr + 1 < H;
+                    if (smode != 0) {  // pixel pairs (W even)
+                        *reinterpret_cast<uint32_t *>(dst) = Act<T>::pack(o0, o2);
+                        if (row1) *reinterpret_cast<uint32_t *>(dst + W) = Act<T>::pack(o1, o3);
+                    } else {
+                        const bool col1 = 2 * jc + 1 < W;
+                        act_store(dst, 0, o0);
+                        if (col1) act_store(dst, 1, o2);
+                        if (row1) {
+                            act_store(dst, W, o1);
+                            if (col1) act_store(dst, W + 1, o3);
                         }
                     }
                 }
             }
-        };
-        constexpr int NW = NT / kWave;
-        for (int t = wave; t < a.tiles; t += 2 * NW) {
-            const int t2 = t + NW < a.tiles ? t + NW : t;
-            wtc_f32x4 h1 = {0.f, 0.f, 0.f, 0.f}, l1 = h1, h2 = h1, l2 = h1;
-            products(t, h1, l1);
-            products(t2, h2, l2);
-            finish(t, h1, l1, true);
-            finish(t2, h2, l2, t2 != t);
         }
     }
 }
