@@ -30,6 +30,7 @@ namespace wtc {
 constexpr size_t kLdsBudget = 64 * 1024;   // bytes of LDS per workgroup of the per-level kernels
 constexpr int kDwTargetBlocks = 2048;      // workgroups wanted for the gradient kernels
 constexpr int kPlaneMaxSide = 64;          // largest plane side of the plane-resident kernels
+constexpr int kPlanCUs = 256;              // compute units the launch plans are sized for
 #ifndef WTC_FWD_PB_CAP
 #define WTC_FWD_PB_CAP 64
 #endif
@@ -454,23 +455,26 @@ bool mma_layout(const wtconv_desc &d, int CW, int pb, MmaArgs &a) {
     return true;
 }
 
-// bfloat16 planes 27..64 pixels wide and at most 64 high, levels >= 1, k = 3 or 5.
+// bfloat16 planes 7..64 pixels on a side, levels >= 1, k = 3 or 5.
 // Chooses CW and PB; false when the shape is outside the kernel's range.
 bool plan_mma(const wtconv_desc &d, MmaArgs &a, int &CW) {
     if (!WTC_MMA || d.dtype != WTCONV_BF16) return false;
     if (d.levels < 1 || d.n <= 0 || d.c <= 0 || d.h <= 0 || d.w <= 0) return false;
     if (d.h > kPlaneMaxSide || d.w > kPlaneMaxSide || d.k > 5) return false;
-    // a tile is 16 cell columns: narrower planes (stacked side by side, more gap
-    // columns per tile, short rows of raw loads) run faster on the vector kernel,
-    // and so do planes without levels (measured: the base conv alone is too little
-    // work per pass to keep the latency of the products hidden)
-    if ((d.w + 1) / 2 < 14) return false;
+    // a tile is 16 x 4 cells: planes under 4 x 4 cells leave most of a tile empty
+    // and stay on the vector kernel, and so do planes without levels (measured: the
+    // base conv alone is too little work per pass to keep the latency of the
+    // products hidden); from 7 x 7 pixels up, planes stacked side by side fill the
+    // tiles well enough (measured faster than the vector kernel at 7 x 7 and 14 x 14)
+    if ((d.w + 1) / 2 < 4 || (d.h + 1) / 2 < 4) return false;
     CW = d.w % 8 == 0 ? 4 : (d.w % 4 == 0 ? 2 : 1);
     const int K = d.k;
     const int nfrag = K == 5 ? 5 : 3;  // B fragments (hi and lo each)
     // Workgroups per compute unit as the registers allow (~167 VGPRs: 3 waves per
     // SIMD); the LDS of a layout may allow fewer.  The kernel is latency-bound, so
-    // the choice weighs the resident passes as well as the work per pass.
+    // the choice weighs the resident passes as well as the work per pass, and the
+    // rounds of passes a workgroup runs: ceil(units / resident workgroups) (a last,
+    // partial round costs a whole one).
     const int wg_regs = 6;
     double best = -1.0;
     int best_pb = 0;
@@ -482,13 +486,16 @@ bool plan_mma(const wtconv_desc &d, MmaArgs &a, int &CW) {
         }
         const int wg = std::max(1, std::min(wg_regs, (int)((160 * 1024) / ((long long)t.lds_floats * 4))));
         // wave-instructions per pass: a tile ~8 per fragment (two 16-cycle products)
-        // plus ~40 others; deep items as in the vector kernel; commit ~20 per item;
+        // plus ~20 others; deep items as in the vector kernel; commit ~20 per item;
         // ~300 fixed
-        const double tiles = cdiv(t.tiles, kMmaThreads / kWave) * 2.0 * (8.0 * nfrag + 40.0);
+        const double tiles = cdiv(t.tiles, kMmaThreads / kWave) * 2.0 * (8.0 * nfrag + 20.0);
         const int deep_items = d.levels >= 2 ? t.dend[d.levels - 2] : 0;
         const double deep = cdiv(deep_items, kMmaThreads) * 2.0 * (4.0 * kPlaneRHd * K * K + 60.0);
         const double misc = cdiv(t.commit_items, kMmaThreads) * 2.0 * 20.0 + 300.0;
-        const double score = (double)pb * wg / (tiles + deep + misc);  // planes per unit time per CU
+        const long long units = (long long)d.c * cdiv(d.n, pb);
+        const double rounds = (double)cdiv(units, (long long)kPlanCUs * wg);
+        // time per pass grows as fewer passes share a compute unit (latency-bound)
+        const double score = 1.0 / (rounds * (tiles + deep + misc) * wg_regs / wg);
         if (score > best * (1 + 1e-9)) {
             best = score;
             best_pb = pb;

@@ -82,8 +82,10 @@ __global__ __launch_bounds__(kDwcThreads, 2) void plane_dwc_kernel(PlaneDwcArgs 
     static_assert(CW == 1 || CW == 2 || CW == 4, "commit width");
     extern __shared__ float smem[];
     uint32_t *lw = reinterpret_cast<uint32_t *>(smem);
-    // neighbouring workgroups take neighbouring channels of the same images
-    const int r = blockIdx.x / a.C, c = blockIdx.x - r * a.C;
+    // neighbouring workgroups (numbered per XCD) take neighbouring channels of the
+    // same images
+    const int wb = xcd_block(blockIdx.x, gridDim.x);
+    const int r = wb / a.C, c = wb - r * a.C;
     const int g_begin = (int)((long long)r * a.NG / a.k), g_end = (int)((long long)(r + 1) * a.NG / a.k);
     const int tid = threadIdx.x, lane = tid & (kWave - 1), wave = tid / kWave, PB = a.PB;
     const int HW = a.H * a.W, CHW = a.C * HW;

@@ -144,7 +144,8 @@ __device__ __forceinline__ void mma_fwd_body(const MmaArgs &args) {
     // A unit is PB images of one channel, in channel-major order: unit u = (channel
     // u / NG, images [(u % NG) PB, ...)).  This workgroup's units are [ubeg, uend).
     const long long G0 = gridDim.x;
-    const int ubeg = (int)((long long)blockIdx.x * a0.U / G0), uend = (int)(((long long)blockIdx.x + 1) * a0.U / G0);
+    const long long wb = xcd_block(blockIdx.x, gridDim.x);
+    const int ubeg = (int)(wb * a0.U / G0), uend = (int)((wb + 1) * a0.U / G0);
     auto unit_of = [&](const auto &A, int u, int &c, int &n0) {
         c = u / A.NG;
         n0 = (u - c * A.NG) * A.PB;

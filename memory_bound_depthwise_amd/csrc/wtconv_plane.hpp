@@ -183,6 +183,17 @@ __device__ __forceinline__ void commit_patch(float4 *s4, int sy1, int pw1,
     }
 }
 
+// Workgroup index with the workgroups of one XCD numbered consecutively.  The
+// command processor deals the workgroups of a launch to the eight XCDs in turn
+// (workgroup w to XCD w mod 8), and each XCD has an L2 of its own; numbered this
+// way, the workgroups that take neighbouring units (neighbouring channels, whose
+// planes share cache lines at their ends) sit behind the same L2.  A bijection of
+// [0, G) for any G.
+__device__ __forceinline__ int xcd_block(int w, int G) {
+    const int x = w & 7, q = G >> 3, r = G & 7;
+    return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + (w >> 3);
+}
+
 // Wave-uniform value made opaque to the optimizer: what is computed from it is
 // computed after this point, inside the current phase, instead of being held in
 // scalar registers from the top of the kernel.
@@ -390,9 +401,10 @@ __device__ __forceinline__ void plane_fwd_body(const PlaneArgs &args) {
 #pragma unroll
         for (int k = 0; k < WSLOTS; ++k) weight_factors(A, c, min(tid + k * NT, (4 * A.L + 1) * KK), wf0[k], wf1[k]);
     };
-    if ((int)blockIdx.x < a0.U) prefetch(args, blockIdx.x);
+    const int wb = xcd_block(blockIdx.x, gridDim.x);
+    if (wb < a0.U) prefetch(args, wb);
 
-    for (int u = blockIdx.x; u < a0.U; u += gridDim.x) {
+    for (int u = wb; u < a0.U; u += gridDim.x) {
         // Every argument below is read through a pointer made opaque per pass, so
         // that nothing derived from the arguments is held in registers across passes.
         // (The argument block is the kernel's only argument: offset 0 of its segment.)

@@ -67,8 +67,10 @@ __global__ __launch_bounds__(kDwbThreads, 2) void plane_dwb_kernel(PlaneDwbArgs 
     constexpr int SLOTS = kPlaneMaxWords / (2 * IO::kWords) > 0 ? kPlaneMaxWords / (2 * IO::kWords) : 1;
     extern __shared__ float smem[];
     float4 *s4 = reinterpret_cast<float4 *>(smem);
-    // neighbouring workgroups take neighbouring channels of the same images
-    const int r = blockIdx.x / a.C, c = blockIdx.x - r * a.C;
+    // neighbouring workgroups (numbered per XCD) take neighbouring channels of the
+    // same images
+    const int wb = xcd_block(blockIdx.x, gridDim.x);
+    const int r = wb / a.C, c = wb - r * a.C;
     const int g_begin = (int)((long long)r * a.NG / a.k), g_end = (int)((long long)(r + 1) * a.NG / a.k);
     const int tid = threadIdx.x, PB = a.PB;
     const int HW = a.H * a.W, CHW = a.C * HW;
@@ -276,8 +278,10 @@ __device__ __forceinline__ void plane_dwl_body(const PlaneDwlArgs &a) {
     using IO = PatchIO<T, CW>;
     constexpr int SLOTS = kPlaneMaxWords / (2 * IO::kWords) > 0 ? kPlaneMaxWords / (2 * IO::kWords) : 1;
     extern __shared__ float smem[];
-    // neighbouring workgroups take neighbouring channels of the same images
-    const int r = blockIdx.x / a.C, c = blockIdx.x - r * a.C;
+    // neighbouring workgroups (numbered per XCD) take neighbouring channels of the
+    // same images
+    const int wb = xcd_block(blockIdx.x, gridDim.x);
+    const int r = wb / a.C, c = wb - r * a.C;
     const int g_begin = (int)((long long)r * a.NG / a.k), g_end = (int)((long long)(r + 1) * a.NG / a.k);
     const int tid = threadIdx.x, PB = a.PB, L = a.L;
     const int HW = a.H * a.W, CHW = a.C * HW;

@@ -51,7 +51,7 @@ def variant_shapes():
                     h = he if i % 2 == 0 else ho
                     out.append((3, 2, h, w, k, L))
                     i += 1
-    # bfloat16 planes 27..64 wide with levels run the matrix-core kernel, k = 3 or 5:
+    # bfloat16 planes 7..64 on a side with levels run the matrix-core kernel, k = 3 or 5:
     # one shape per commit width CW (w % 8 == 0, w % 4 == 0, odd w), levels 1..3,
     # even and odd heights, three images per channel
     mma = {4: 32, 2: 28, 1: 29}
@@ -60,6 +60,11 @@ def variant_shapes():
             h = (30, 33, 40)[i % 3]
             out.append((3, 2, h, w, k, 1 + i % 3))
             i += 1
+    # planes under 7 pixels on a side stay on the vector kernel in bfloat16 too (the
+    # matrix-core kernel takes the rest): its variants for k = 3 and 5 on such planes
+    for k in (3, 5):
+        for h, w, L in ((14, 1, 1), (9, 1, 2), (1, 4, 1), (14, 4, 2), (9, 4, 3), (1, 8, 1), (1, 1, 1)):
+            out.append((3, 2, h, w, k, L))
     # bfloat16 weight gradients of levels 2..L beside the correlation kernel, for the
     # kernel sizes the rows above leave out at CW = 4
     for k in (3, 7):

@@ -182,7 +182,9 @@ def test_launch_plan_query():
     d = wt.make_desc(64, 96, 56, 56, 5, 3, wt.F16)        # ... on the vector units for the other dtypes
     assert plan(d, wt.OP_FORWARD) == ["plane_fwd<5,f16>"]
     assert plan(d, wt.OP_BACKWARD_WEIGHT) == ["plane_dwl<5,f16>", "plane_dwb<5,f16>", "dw_finalize<5,f16>"]
-    d = wt.make_desc(64, 384, 14, 14, 5, 1, wt.BF16)      # ... and for narrow planes
+    d = wt.make_desc(64, 384, 14, 14, 5, 1, wt.BF16)      # narrow planes side by side on the matrix cores
+    assert plan(d, wt.OP_FORWARD) == ["mma_fwd<5,bf16>"]
+    d = wt.make_desc(64, 384, 5, 14, 5, 1, wt.BF16)       # ... but under 4 cell rows on the vector units
     assert plan(d, wt.OP_FORWARD) == ["plane_fwd<5,bf16>"]
     d = wt.make_desc(64, 96, 56, 56, 7, 0, wt.BF16)       # levels = 0: the same kernel, base only
     assert plan(d, wt.OP_FORWARD) == ["plane_fwd<7,bf16>"]
