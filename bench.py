@@ -384,7 +384,7 @@ def main():
     kernels.sort(key=lambda k: -k["ms_per_step"])
     dom = kernels[0]
     t_hbm = dom["bytes_per_launch"] / (HBM_PEAK_GBS * 1e9)
-    on_mfma = dom["kernel"].startswith("mma_fwd")  # level-1 and base products on the matrix cores
+    on_mfma = dom["kernel"].startswith(("mma_fwd", "mma_tile"))  # level-1 and base products on the matrix cores
     t_alu = dom["flops_per_launch"] / ((MFMA_BF16_TFLOPS if on_mfma else VALU_PEAK_TFLOPS) * 1e12)
     digest = source_digest()
     if t_hbm >= t_alu:

@@ -509,6 +509,51 @@ bool plan_mma(const wtconv_desc &d, MmaArgs &a, int &CW) {
     return true;
 }
 
+// The tiled matrix-core forward for planes past the plane-resident range: bfloat16,
+// levels >= 1, k = 3 or 5.  A pass is a tile of UR x UC level-1 cells (at most
+// 16 x 64, narrower planes take fewer), its canvas the tile's pixels and the 2R
+// halo pixels on each side, staged in chunks of 8 pixels.
+bool plan_mma_tile(const wtconv_desc &d, MmaTileArgs &a) {
+    if (!WTC_MMA || d.dtype != WTCONV_BF16) return false;
+    if (d.levels < 1 || d.n <= 0 || d.c <= 0 || d.h <= 0 || d.w <= 0 || d.k > 5) return false;
+    const int R = (d.k - 1) / 2, KK = d.k * d.k;
+    a = MmaTileArgs{};
+    a.n = d.n;
+    a.C = d.c;
+    a.H = d.h;
+    a.W = d.w;
+    a.L = d.levels;
+    const int H1 = (d.h + 1) / 2, W1 = (d.w + 1) / 2;
+    a.UR = std::min(16, 4 * cdiv(H1, 4));
+    a.UC = std::min(64, 16 * cdiv(W1, 16));
+    a.TYu = cdiv(H1, a.UR);
+    a.TXu = cdiv(W1, a.UC);
+    a.rows = 2 * a.UR + 4 * R;
+    a.chunks = 2 + a.UC / 4;  // canvas columns X0 - 8 .. X0 + 2 UC + 7
+    a.items = a.rows * a.chunks;
+    if (a.items > kTileSlots * kTileThreads) return false;
+    int S = 4 * a.chunks;  // dwords; 16 mod 32, as in the plane-resident canvas
+    while (S % 32 != 16) ++S;
+    a.S = S;
+    // the block of D (the deeper levels' patterns summed on the level-1 grid) after
+    // the canvas: UR rows of UC cells, as pairs
+    a.qbase = a.rows * S;
+    a.qitems = d.levels >= 2 ? a.UR * (a.UC / 2) : 0;
+    if (a.qitems > kTileQSlots * kTileThreads) return false;
+    const LevelDims ld = level_dims(d);
+    a.hq = d.levels >= 2 ? 2 * ld.H[2] : 0;
+    a.wq = d.levels >= 2 ? 2 * ld.W[2] : 0;
+    a.wt = (a.qbase + a.qitems + 3) & ~3;
+    a.lds_floats = (a.wt + 5 * KK + 1 + 3) & ~3;
+    const long long units = (long long)d.c * d.n * a.TYu * a.TXu;
+    if (units >= (1LL << 31)) return false;
+    a.U = (int)units;
+    a.m_chunks = magic31_of(a.chunks);
+    a.m_tx = magic31_of(a.UC / 16);
+    a.m_qp = magic31_of(a.UC / 2);
+    return true;
+}
+
 // ---------------------------------------------------------------------------
 // Plane-resident base weight gradient (polyphase cells of x and dy)
 // ---------------------------------------------------------------------------
@@ -845,12 +890,14 @@ bool plan_dwc(const wtconv_desc &d, PlaneDwcArgs &a, int &CW, bool lev) {
     return (long long)d.c * a.k < (1LL << 31);
 }
 
-FwdPlan build_forward_plan(const wtconv_desc &d) {
+// Workspace of the per-level path: the sign patterns Q_l of every level and the
+// carriers of levels 1..L-1 (with the tiled matrix-core kernel, level 1 has no Q).
+FwdPlan build_forward_plan(const wtconv_desc &d, bool tile) {
     FwdPlan p{};
     p.ld = level_dims(d);
     const size_t es = elem_size(d.dtype), planes = (size_t)d.n * d.c;
     size_t off = 0;
-    for (int l = 1; l <= d.levels; ++l) {
+    for (int l = tile ? 2 : 1; l <= d.levels; ++l) {
         p.q_off[l - 1] = off;
         off = align_up(off + planes * 4 * p.ld.H[l] * p.ld.W[l] * es);
     }
@@ -935,10 +982,11 @@ std::shared_ptr<const PlanSet> plans_for(const wtconv_desc &d) {
     }
     auto ps = std::make_shared<PlanSet>();
     ps->d = d;
-    ps->fp = build_forward_plan(d);
-    ps->dp = build_backward_weight_plan(d);
     ps->plane = plan_plane(d, ps->pa, ps->pcfg);
     ps->mma = plan_mma(d, ps->ma, ps->mcw);
+    ps->mtile = !ps->plane && !ps->mma && plan_mma_tile(d, ps->ta);
+    ps->fp = build_forward_plan(d, ps->mtile);
+    ps->dp = build_backward_weight_plan(d);
     std::lock_guard<std::mutex> lock(mu);
     if (cache.size() >= 64) cache.erase(cache.begin());
     cache.push_back(ps);
@@ -997,6 +1045,7 @@ int check_desc(const wtconv_desc *d) {
 
 int plane_grid_for(const PlanSet &ps) { WTC_DISPATCH(ps.d.k, ps.d.dtype, plane_grid, ps); }
 int mma_grid_for(const PlanSet &ps) { WTC_DISPATCH(ps.d.k, ps.d.dtype, mma_grid, ps); }
+int tile_grid_for(const PlanSet &ps) { WTC_DISPATCH(ps.d.k, ps.d.dtype, tile_grid, ps); }
 
 int fwd_common(const wtconv_desc *desc, const void *in, const float *w0, const float *b0, const float *s0,
                const float *wl, const float *sl, void *out, void *workspace, size_t workspace_bytes, void *stream,
@@ -1192,6 +1241,16 @@ WTCONV_API int wtconv_plan_launches(const wtconv_desc *desc, int op, wtconv_laun
             } else if (ps->plane) {
                 add("plane_fwd", 0, plane_grid_for(*ps), kFwdThreads, (size_t)ps->pa.lds_floats * sizeof(float),
                     16 * ps->pcfg.CW + ps->pcfg.RH + (d.levels == 0 ? 256 : 0));
+            } else if (ps->mtile) {
+                const FwdPlan &p = ps->fp;
+                for (int l = 1; l < d.levels; ++l)
+                    add("carrier", l,
+                        (long long)cdiv((long long)p.ld.H[l] * cdiv(p.ld.W[l], 4), kThreads) *
+                            std::min<long long>((long long)d.n * d.c, 65535),
+                        kThreads, 0);
+                for (int l = d.levels; l >= 2; --l)
+                    add("level_acc", l, grid_of(p.lvl[l - 1], d.c), kThreads, lds_bytes(Kind::LevelFwd, d.k, p.lvl[l - 1]));
+                add("mma_tile", 0, tile_grid_for(*ps), kTileThreads, (size_t)ps->ta.lds_floats * sizeof(float));
             } else {
                 const FwdPlan &p = ps->fp;
                 for (int l = 1; l <= d.levels; ++l)

@@ -8,7 +8,9 @@
 //     gradient launches and the finalize;
 //   * per-level kernels (larger planes): one analysis + filter launch per level
 //     and one closed-form synthesis launch per forward-shaped pass (§4.1-4.4), one
-//     gradient launch per level, the base gradient and the finalize.
+//     gradient launch per level, the base gradient and the finalize; for bfloat16
+//     the level-1 carrier, the levels 2..L and one tiled matrix-core launch that
+//     takes level 1, the base conv and the synthesis per forward-shaped pass.
 // Plans (layouts, tilings, launch sizes) depend on the descriptor only and are
 // built once per descriptor in wtconv_api.hip.
 
@@ -27,6 +29,7 @@
 #include "wtconv_plane_dw.hpp"
 #include "wtconv_mma.hpp"
 #include "wtconv_dwc.hpp"
+#include "wtconv_mma_tile.hpp"
 
 namespace wtc {
 
@@ -124,6 +127,8 @@ struct PlanSet {
     bool mma = false;  // ... by the plane-resident kernel on the matrix cores (bfloat16)
     MmaArgs ma{};
     int mcw = 1;       // its commit width (cells per item)
+    bool mtile = false;  // per-level path: levels 2..L by the level kernels, the rest by
+    MmaTileArgs ta{};    // the tiled matrix-core kernel (bfloat16)
 };
 
 // ---- Profiling hooks (wtconv_api.hip) ------------------------------------
@@ -147,5 +152,8 @@ int plane_grid(const PlanSet &ps);
 // ... of the matrix-core forward kernel (one contiguous range of units each).
 template <int K, typename T>
 int mma_grid(const PlanSet &ps);
+// ... of the tiled matrix-core forward kernel.
+template <int K, typename T>
+int tile_grid(const PlanSet &ps);
 
 }  // namespace wtc

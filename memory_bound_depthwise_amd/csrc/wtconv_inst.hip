@@ -23,5 +23,6 @@ template int run_backward_weight<WTC_K, WTC_T>(const PlanSet &, const void *, co
                                                float *, float *, float *, float *, float *, char *, hipStream_t);
 template int plane_grid<WTC_K, WTC_T>(const PlanSet &);
 template int mma_grid<WTC_K, WTC_T>(const PlanSet &);
+template int tile_grid<WTC_K, WTC_T>(const PlanSet &);
 
 }  // namespace wtc

@@ -237,6 +237,10 @@ struct LevelArgs {
     float wscale;     // 2^-(l+1): synthesis weight 2^-l times the analysis 1/2
     int rotate;       // 1: kernels turned by 180 degrees (input gradient)
     int pairs;        // 1: Wi even and the input aligned for two-element loads
+    // the deeper levels' patterns summed on this level's grid, [n][C][2 Ho'][2 Wo']
+    // for the next level's Ho' x Wo' (its value at cell (i, j) enters all four
+    // patterns of block (i, j)), or NULL
+    const void *deeper;
     Tiling t;
 };
 
@@ -691,13 +695,91 @@ __global__ __launch_bounds__(256) void level_fwd_kernel(LevelArgs a) {
         const int rows = min(kRH, min(a.Ho, bp.ty0 + t.TY) - gi0);
         if (nn >= a.n || gj >= a.Wo || rows <= 0) continue;
         T *qp = q + ((size_t)nn * a.C + c) * q_plane + (size_t)(2 * gi0) * Wq + 2 * gj;
+        float dz[kRH];
+#pragma unroll
+        for (int i = 0; i < kRH; ++i) dz[i] = 0.f;
+        if (a.deeper) {
+            // the deeper grid is 2 Ho' x 2 Wo' with Ho' = ceil(Ho / 2): rows of this
+            // level's grid are all inside it
+            const int Wd = 2 * ((a.Wo + 1) / 2), Hd = 2 * ((a.Ho + 1) / 2);
+            const T *dp = static_cast<const T *>(a.deeper) + ((size_t)nn * a.C + c) * Hd * Wd + (size_t)gi0 * Wd + gj;
+#pragma unroll
+            for (int i = 0; i < kRH; ++i)
+                if (i < rows) dz[i] = act_load(dp, (size_t)i * Wd);
+        }
 #pragma unroll
         for (int i = 0; i < kRH; ++i) {
             if (i >= rows) break;
             const float a0 = z[0][i] + z[1][i], a1 = z[0][i] - z[1][i];
             const float b0 = z[2][i] + z[3][i], b1 = z[2][i] - z[3][i];
-            act_store2(qp + 2 * i * Wq, 0, a0 + b0, a0 - b0);
-            act_store2(qp + (2 * i + 1) * Wq, 0, a1 + b1, a1 - b1);
+            act_store2(qp + 2 * i * Wq, 0, (a0 + b0) + dz[i], (a0 - b0) + dz[i]);
+            act_store2(qp + (2 * i + 1) * Wq, 0, (a1 + b1) + dz[i], (a1 - b1) + dz[i]);
+        }
+    }
+}
+
+// ---------------------------------------------------------------------------
+// Level-1 carrier alone: the normalised low-pass band 1/2 (x00 + x01 + x10 + x11)
+// of every 2 x 2 block (Eq. 5), the input of the level-2 kernel when the level-1
+// filter and synthesis run elsewhere (the tiled matrix-core forward).  The same
+// sums, in the same order and with the same rounding, as the carrier the level
+// kernel writes.  Thread: four consecutive blocks of one block row; grid.y walks
+// the planes.
+// ---------------------------------------------------------------------------
+
+struct CarrierArgs {
+    const void *in;  // [planes][Hi][Wi]
+    void *out;       // [planes][Ho][Wo]
+    int planes, Hi, Wi, Ho, Wo;
+    int groups;      // ceil(Wo / 4) groups of four blocks per row
+    int vec;         // Wi % 8 == 0 and the input 16-byte aligned: one 8-pixel load per row
+};
+
+template <typename T>
+__global__ __launch_bounds__(256) void carrier_kernel(CarrierArgs a) {
+    const int idx = blockIdx.x * blockDim.x + threadIdx.x;
+    if (idx >= a.Ho * a.groups) return;
+    const int i = idx / a.groups, g = idx - i * a.groups;
+    const bool r1 = 2 * i + 1 < a.Hi;
+    for (int p = blockIdx.y; p < a.planes; p += gridDim.y) {
+        const T *src = static_cast<const T *>(a.in) + (size_t)p * a.Hi * a.Wi + (size_t)(2 * i) * a.Wi + 8 * g;
+        T *dst = static_cast<T *>(a.out) + (size_t)p * a.Ho * a.Wo + (size_t)i * a.Wo + 4 * g;
+        float x[2][8];
+        if constexpr (kHalf<T>) {
+            if (a.vec) {
+                const uint4 v0 = *reinterpret_cast<const uint4 *>(src);
+                const uint4 v1 = r1 ? *reinterpret_cast<const uint4 *>(src + a.Wi) : make_uint4(0u, 0u, 0u, 0u);
+                const uint32_t w[2][4] = {{v0.x, v0.y, v0.z, v0.w}, {v1.x, v1.y, v1.z, v1.w}};
+#pragma unroll
+                for (int r = 0; r < 2; ++r)
+#pragma unroll
+                    for (int e = 0; e < 4; ++e) {
+                        x[r][2 * e] = Act<T>::lo(w[r][e]);
+                        x[r][2 * e + 1] = Act<T>::hi(w[r][e]);
+                    }
+            } else {
+#pragma unroll
+                for (int r = 0; r < 2; ++r)
+#pragma unroll
+                    for (int e = 0; e < 8; ++e) {
+                        const bool in = 8 * g + e < a.Wi && (r == 0 || r1);
+                        x[r][e] = in ? act_load(src, (size_t)r * a.Wi + e) : 0.f;
+                    }
+            }
+        } else {
+#pragma unroll
+            for (int r = 0; r < 2; ++r)
+#pragma unroll
+                for (int e = 0; e < 8; ++e) {
+                    const bool in = 8 * g + e < a.Wi && (r == 0 || r1);
+                    x[r][e] = in ? act_load(src, (size_t)r * a.Wi + e) : 0.f;
+                }
+        }
+#pragma unroll
+        for (int b = 0; b < 4; ++b) {
+            if (4 * g + b >= a.Wo) break;
+            const float s0 = x[0][2 * b] + x[0][2 * b + 1], s1 = x[1][2 * b] + x[1][2 * b + 1];
+            act_store(dst, b, 0.5f * (s0 + s1));
         }
     }
 }

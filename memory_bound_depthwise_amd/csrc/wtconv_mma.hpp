@@ -109,6 +109,113 @@ struct MmaArgs {
     uint32_t m_wls[kMaxLevels];
 };
 
+// B fragments (hi and lo halves) of one channel from the LDS weight table: the
+// level-1 band weights as float4 over the bands at wt + 4 (v K + u), the base
+// weights at base + v K + u (columns of taps, as the table stores them).  Column n
+// = 4 rp + 2 rx + ry of B (held by lane n mod 16) belongs to output pixel (ry, rx)
+// of cell row rp; its entry at window pixel (rho, kap) is the level-1 tap of that
+// window pixel with the Haar sign product folded in, plus the base tap.
+template <int K>
+__device__ __forceinline__ void mma_b_fragments(const float *smem, int wt, int base, int lane,
+                                                wtc_bf16x8 (&bh)[MmaGeom<K>::NS], wtc_bf16x8 (&bl)[MmaGeom<K>::NS]) {
+    using G = MmaGeom<K>;
+    constexpr int R = (K - 1) / 2;
+    const float4 *s4 = reinterpret_cast<const float4 *>(smem);
+    // the lane's coordinates made opaque here, so that nothing of this block is
+    // hoisted out of a caller's loop (it would stay in registers throughout)
+    int ln = lane;
+    asm volatile("" : "+v"(ln));
+    const int g4 = ln >> 4, mm = ln & 15;
+    const int rp = mm >> 2, ry = mm & 1, rx = (mm >> 1) & 1;
+#pragma unroll
+    for (int s = 0; s < G::NS; ++s) {
+        union { wtc_bf16x8 v; uint32_t w[4]; } fh, fl;
+#pragma unroll
+        for (int j = 0; j < 8; j += 2) {
+            uint32_t h2[2], l2[2];
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                // window pixel (rho, kap) of K element 8 g4 + j + e of step s
+                int rho, kap;
+                if (G::TAIL && s == G::NSF) {
+                    rho = g4 + 4 * ((j + e) >> 1);
+                    kap = 8 + ((j + e) & 1);
+                } else {
+                    const int q = 4 * s + g4;
+                    rho = q;
+                    kap = j + e;
+                }
+                float w;
+                {  // level-1 tap (uu, vv) at window pixel (py, px)
+                    const int py = rho & 1, px = kap & 1, uu = (rho >> 1) - rp, vv = kap >> 1;
+                    const bool ok = rho < G::WR && uu >= 0 && uu < K && vv < K;
+                    const float4 wb = s4[(wt >> 2) + (ok ? vv * K + uu : 0)];
+                    const int sy = ry ^ py, sx = rx ^ px;
+                    const float t = (wb.x + (sy ? -wb.y : wb.y)) + ((sx ? -wb.z : wb.z) + ((sy ^ sx) ? -wb.w : wb.w));
+                    w = ok ? t : 0.f;
+                }
+                if (!G::TAIL || s < G::NSF) {  // base tap of output pixel (2 rp + ry, rx)
+                    const int uu = rho - 2 * rp - ry + R - G::ROW0, vv = kap - rx + R - G::COL0;
+                    const bool ok = rho < G::WR && uu >= 0 && uu < K && vv >= 0 && vv < K;
+                    const float t = smem[base + (ok ? vv * K + uu : 0)];
+                    w += ok ? t : 0.f;
+                }
+                const uint16_t h = Act<uint16_t>::one(w);
+                h2[e] = h;
+                l2[e] = Act<uint16_t>::one(w - __uint_as_float((uint32_t)h << 16));
+            }
+            fh.w[j >> 1] = h2[0] | (h2[1] << 16);
+            fl.w[j >> 1] = l2[0] | (l2[1] << 16);
+        }
+        bh[s] = fh.v;
+        bl[s] = fl.v;
+        // one step at a time: the table reads of all steps at once would take more
+        // registers than the rest of the kernel
+        __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+// The transposed products of two tiles (their MFMA chains and LDS reads are
+// independent, which hides the latency of each): wp[h] points at the canvas dword
+// of window row g4, cell column mm of tile h (S: canvas row stride in dwords).
+// acc[h] receives the four pixels of cell (g4, mm) of tile h, i = 2 rx + ry.
+template <int K>
+__device__ __forceinline__ void mma_products2(const uint32_t *wp0, const uint32_t *wp1, int S,
+                                              const wtc_bf16x8 (&bh)[MmaGeom<K>::NS],
+                                              const wtc_bf16x8 (&bl)[MmaGeom<K>::NS], wtc_f32x4 (&acc)[2]) {
+    using G = MmaGeom<K>;
+    const uint32_t *wp[2] = {wp0, wp1};
+    acc[0] = wtc_f32x4{0.f, 0.f, 0.f, 0.f};
+    acc[1] = acc[0];
+#pragma unroll
+    for (int s = 0; s < G::NSF; ++s) {
+        union { wtc_bf16x8 v; uint32_t w[4]; } A[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) {
+            const uint32_t *q = wp[h] + 4 * s * S;
+            A[h].w[0] = q[0];
+            A[h].w[1] = q[1];
+            A[h].w[2] = q[2];
+            A[h].w[3] = q[3];
+        }
+#pragma unroll
+        for (int h = 0; h < 2; ++h) acc[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bh[s], A[h].v, acc[h], 0, 0, 0);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) acc[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bl[s], A[h].v, acc[h], 0, 0, 0);
+    }
+    if constexpr (G::TAIL) {  // window columns 8, 9 of rows g4 + 4 e
+        union { wtc_bf16x8 v; uint32_t w[4]; } A[2];
+#pragma unroll
+        for (int h = 0; h < 2; ++h)
+#pragma unroll
+            for (int e = 0; e < 4; ++e) A[h].w[e] = wp[h][4 * e * S + 4];
+#pragma unroll
+        for (int h = 0; h < 2; ++h) acc[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bh[G::NSF], A[h].v, acc[h], 0, 0, 0);
+#pragma unroll
+        for (int h = 0; h < 2; ++h) acc[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bl[G::NSF], A[h].v, acc[h], 0, 0, 0);
+    }
+}
+
 template <int K, int CW>
 __device__ __forceinline__ void mma_fwd_body(const MmaArgs &args) {
     using G = MmaGeom<K>;
@@ -373,58 +480,7 @@ __device__ __forceinline__ void mma_fwd_body(const MmaArgs &args) {
         if (c != cur_c) {
             cur_c = c;
             const int wt = opaque(a.wt);
-            // the lane's coordinates made opaque here, so that nothing of this block
-            // is hoisted out of the unit loop (it would stay in registers throughout)
-            int ln = lane;
-            asm volatile("" : "+v"(ln));
-            const int g4 = ln >> 4, mm = ln & 15;
-            const int rp = mm >> 2, ry = mm & 1, rx = (mm >> 1) & 1;
-#pragma unroll
-            for (int s = 0; s < G::NS; ++s) {
-                union { wtc_bf16x8 v; uint32_t w[4]; } fh, fl;
-#pragma unroll
-                for (int j = 0; j < 8; j += 2) {
-                    uint32_t h2[2], l2[2];
-#pragma unroll
-                    for (int e = 0; e < 2; ++e) {
-                        // window pixel (rho, kap) of K element 8 g4 + j + e of step s
-                        int rho, kap;
-                        if (G::TAIL && s == G::NSF) {
-                            rho = g4 + 4 * ((j + e) >> 1);
-                            kap = 8 + ((j + e) & 1);
-                        } else {
-                            const int q = 4 * s + g4;
-                            rho = q;
-                            kap = j + e;
-                        }
-                        float w;
-                        {  // level-1 tap (uu, vv) at window pixel (py, px)
-                            const int py = rho & 1, px = kap & 1, uu = (rho >> 1) - rp, vv = kap >> 1;
-                            const bool ok = rho < G::WR && uu >= 0 && uu < K && vv < K;
-                            const float4 wb = s4[(wt >> 2) + (ok ? vv * K + uu : 0)];
-                            const int sy = ry ^ py, sx = rx ^ px;
-                            const float t = (wb.x + (sy ? -wb.y : wb.y)) + ((sx ? -wb.z : wb.z) + ((sy ^ sx) ? -wb.w : wb.w));
-                            w = ok ? t : 0.f;
-                        }
-                        if (!G::TAIL || s < G::NSF) {  // base tap of output pixel (2 rp + ry, rx)
-                            const int uu = rho - 2 * rp - ry + R - G::ROW0, vv = kap - rx + R - G::COL0;
-                            const bool ok = rho < G::WR && uu >= 0 && uu < K && vv >= 0 && vv < K;
-                            const float t = smem[wt + 4 * L * KK + (ok ? vv * K + uu : 0)];
-                            w += ok ? t : 0.f;
-                        }
-                        const uint16_t h = Act<T>::one(w);
-                        h2[e] = h;
-                        l2[e] = Act<T>::one(w - __uint_as_float((uint32_t)h << 16));
-                    }
-                    fh.w[j >> 1] = h2[0] | (h2[1] << 16);
-                    fl.w[j >> 1] = l2[0] | (l2[1] << 16);
-                }
-                bh[s] = fh.v;
-                bl[s] = fl.v;
-                // one step at a time: the table reads of all steps at once would take
-                // more registers than the rest of the kernel
-                __builtin_amdgcn_sched_barrier(0);
-            }
+            mma_b_fragments<K>(smem, wt, wt + 4 * L * KK, lane, bh, bl);
         }
 
         // 4. products and stores, one tile of 16 x 4 cells at a time.  The product is
@@ -458,37 +514,9 @@ __device__ __forceinline__ void mma_fwd_body(const MmaArgs &args) {
             tx[0] = t - ty[0] * a.TX;
             ty[1] = udiv16(t2, a.m_tx);
             tx[1] = t2 - ty[1] * a.TX;
-            wtc_f32x4 acc[2] = {{0.f, 0.f, 0.f, 0.f}, {0.f, 0.f, 0.f, 0.f}};
-            const uint32_t *wp[2] = {cv + la + (8 * ty[0]) * S + 16 * tx[0], cv + la + (8 * ty[1]) * S + 16 * tx[1]};
-#pragma unroll
-            for (int s = 0; s < G::NSF; ++s) {
-                union { wtc_bf16x8 v; uint32_t w[4]; } A[2];
-#pragma unroll
-                for (int h = 0; h < 2; ++h) {
-                    const uint32_t *q = wp[h] + 4 * s * S;
-                    A[h].w[0] = q[0];
-                    A[h].w[1] = q[1];
-                    A[h].w[2] = q[2];
-                    A[h].w[3] = q[3];
-                }
-#pragma unroll
-                for (int h = 0; h < 2; ++h) acc[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bh[s], A[h].v, acc[h], 0, 0, 0);
-#pragma unroll
-                for (int h = 0; h < 2; ++h) acc[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bl[s], A[h].v, acc[h], 0, 0, 0);
-            }
-            if constexpr (G::TAIL) {  // window columns 8, 9 of rows g4 + 4 e
-                union { wtc_bf16x8 v; uint32_t w[4]; } A[2];
-#pragma unroll
-                for (int h = 0; h < 2; ++h)
-#pragma unroll
-                    for (int e = 0; e < 4; ++e) A[h].w[e] = wp[h][4 * e * S + 4];
-#pragma unroll
-                for (int h = 0; h < 2; ++h)
-                    acc[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bh[G::NSF], A[h].v, acc[h], 0, 0, 0);
-#pragma unroll
-                for (int h = 0; h < 2; ++h)
-                    acc[h] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(bl[G::NSF], A[h].v, acc[h], 0, 0, 0);
-            }
+            wtc_f32x4 acc[2];
+            mma_products2<K>(cv + la + (8 * ty[0]) * S + 16 * tx[0], cv + la + (8 * ty[1]) * S + 16 * tx[1], S, bh, bl,
+                             acc);
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 if (h == 1 && t2 == t) break;

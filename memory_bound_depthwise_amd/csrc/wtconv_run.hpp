@@ -288,37 +288,117 @@ int run_mma_forward(const PlanSet &ps, const void *x, const float *w0, const flo
     }
 }
 
+// Level kernel of level l: analysis of the carrier `in` of the level above, the
+// four-band conv and the sign patterns Q_l, and (with `carry`) the carrier of
+// level l for the next; with `deeper`, the deeper levels' summed patterns are added.
+template <int K, typename T>
+int run_level_fwd(const PlanSet &ps, const char *family, int l, const void *in, const void *deeper, bool carry,
+                  const float *wl, const float *sl, char *ws, hipStream_t st, int rotate) {
+    const wtconv_desc &d = ps.d;
+    const FwdPlan &p = ps.fp;
+    LevelArgs a{};
+    a.in = in;
+    a.deeper = deeper;
+    a.qout = ws + p.q_off[l - 1];
+    a.cout = carry && l < d.levels ? (void *)(ws + p.c_off[l - 1]) : nullptr;
+    a.wl = wl + (size_t)(l - 1) * d.c * 4 * K * K;
+    a.sl = sl + (size_t)(l - 1) * d.c * 4;
+    a.n = d.n;
+    a.C = d.c;
+    a.Hi = p.ld.H[l - 1];
+    a.Wi = p.ld.W[l - 1];
+    a.Ho = p.ld.H[l];
+    a.Wo = p.ld.W[l];
+    a.wscale = std::ldexp(1.0f, -(l + 1));
+    a.rotate = rotate;
+    a.pairs = (a.Wi % 2 == 0) && ((uintptr_t)a.in % (2 * sizeof(T)) == 0);
+    a.t = p.lvl[l - 1];
+    const size_t shm = lds_bytes(Kind::LevelFwd, K, a.t);
+    return launch(family, K, dtype_of<T>(), l, level_fwd_kernel<K, T>, dim3((unsigned)grid_of(a.t, d.c)),
+                  dim3(kThreads), shm, st, a);
+}
+
+template <int K, typename T>
+int tile_grid(const PlanSet &ps) {
+    if constexpr (K > 5) {
+        return 0;  // not planned: the matrix-core kernels take K = 3 or 5
+    } else {
+        const MmaTileArgs &a = ps.ta;
+        const size_t shm = (size_t)a.lds_floats * sizeof(float);
+        return (int)std::min<long long>(
+            a.U, resident_slots(reinterpret_cast<const void *>(mma_tile_kernel<K>), kTileThreads, shm));
+    }
+}
+
+// The per-level path with the tiled matrix-core kernel: the carriers of levels
+// 1..L-1, then the level kernels from the deepest level up, each adding the summed
+// patterns of the levels below it to its own (level 2 leaves sum_{l >= 2} Q_l on
+// the level-1 grid), then the tiles.
+template <int K, typename T>
+int run_tile_forward(const PlanSet &ps, const void *x, const float *w0, const float *b0, const float *s0,
+                     const float *wl, const float *sl, void *y, char *ws, hipStream_t st, int rotate) {
+    if constexpr (!std::is_same<T, uint16_t>::value || K > 5) {
+        return WTCONV_ERR_DTYPE;  // not planned: bfloat16 with K = 3 or 5 only
+    } else {
+        const wtconv_desc &d = ps.d;
+        const FwdPlan &p = ps.fp;
+        const int bf = dtype_of<T>();
+        const int L = d.levels;
+        for (int l = 1; l < L; ++l) {
+            CarrierArgs c{};
+            c.in = l == 1 ? x : (const void *)(ws + p.c_off[l - 2]);
+            c.out = ws + p.c_off[l - 1];
+            c.planes = d.n * d.c;
+            c.Hi = p.ld.H[l - 1];
+            c.Wi = p.ld.W[l - 1];
+            c.Ho = p.ld.H[l];
+            c.Wo = p.ld.W[l];
+            c.groups = cdiv(c.Wo, 4);
+            c.vec = c.Wi % 8 == 0 && aligned(c.in, 16) ? 1 : 0;
+            const dim3 grid((unsigned)cdiv((long long)c.Ho * c.groups, kThreads),
+                            (unsigned)std::min(c.planes, 65535));
+            int rc = launch("carrier", K, bf, l, carrier_kernel<T>, grid, dim3(kThreads), 0, st, c);
+            if (rc) return rc;
+        }
+        for (int l = L; l >= 2; --l) {
+            int rc = run_level_fwd<K, T>(ps, "level_acc", l, ws + p.c_off[l - 2],
+                                         l < L ? (const void *)(ws + p.q_off[l]) : nullptr, false, wl, sl, ws, st,
+                                         rotate);
+            if (rc) return rc;
+        }
+        MmaTileArgs a = ps.ta;
+        a.x = x;
+        a.y = y;
+        a.w0 = w0;
+        a.b0 = b0;
+        a.s0 = s0;
+        a.wl = wl;
+        a.sl = sl;
+        a.rotate = rotate;
+        a.q = L >= 2 ? (const void *)(ws + p.q_off[1]) : nullptr;
+        a.vec = d.w % 8 == 0 && aligned(x, 16) ? 1 : 0;
+        a.pairs = d.w % 2 == 0 && aligned(y, 2 * sizeof(T)) ? 1 : 0;
+        const dim3 grid((unsigned)tile_grid<K, T>(ps));
+        const size_t shm = (size_t)a.lds_floats * sizeof(float);
+        return launch("mma_tile", K, bf, 0, mma_tile_kernel<K>, grid, dim3(kTileThreads), shm, st, a);
+    }
+}
+
 template <int K, typename T>
 int run_forward(const PlanSet &ps, const void *x, const float *w0, const float *b0, const float *s0,
                 const float *wl, const float *sl, void *y, char *ws, hipStream_t st, int rotate) {
     if (ps.mma) return run_mma_forward<K, T>(ps, x, w0, b0, s0, wl, sl, y, st, rotate);
     if (ps.plane) return run_plane_forward<K, T>(ps, x, w0, b0, s0, wl, sl, y, st, rotate);
+    if (ps.mtile) return run_tile_forward<K, T>(ps, x, w0, b0, s0, wl, sl, y, ws, st, rotate);
     const wtconv_desc &d = ps.d;
     const FwdPlan &p = ps.fp;
-    const int bf = dtype_of<T>();  // dtype code, for the launch records
     const int L = d.levels;
     for (int l = 1; l <= L; ++l) {
-        LevelArgs a{};
-        a.in = l == 1 ? x : (const void *)(ws + p.c_off[l - 2]);
-        a.qout = ws + p.q_off[l - 1];
-        a.cout = l < L ? (void *)(ws + p.c_off[l - 1]) : nullptr;
-        a.wl = wl + (size_t)(l - 1) * d.c * 4 * K * K;
-        a.sl = sl + (size_t)(l - 1) * d.c * 4;
-        a.n = d.n;
-        a.C = d.c;
-        a.Hi = p.ld.H[l - 1];
-        a.Wi = p.ld.W[l - 1];
-        a.Ho = p.ld.H[l];
-        a.Wo = p.ld.W[l];
-        a.wscale = std::ldexp(1.0f, -(l + 1));
-        a.rotate = rotate;
-        a.pairs = (a.Wi % 2 == 0) && ((uintptr_t)a.in % (2 * sizeof(T)) == 0);
-        a.t = p.lvl[l - 1];
-        const size_t shm = lds_bytes(Kind::LevelFwd, K, a.t);
-        int rc = launch("level_fwd", K, bf, l, level_fwd_kernel<K, T>, dim3((unsigned)grid_of(a.t, d.c)),
-                        dim3(kThreads), shm, st, a);
+        int rc = run_level_fwd<K, T>(ps, "level_fwd", l, l == 1 ? x : (const void *)(ws + p.c_off[l - 2]), nullptr,
+                                     true, wl, sl, ws, st, rotate);
         if (rc) return rc;
     }
+    const int bf = dtype_of<T>();  // dtype code, for the launch records
     SynthArgs s{};
     s.x = x;
     s.y = y;

@@ -32,6 +32,12 @@ B_l = P*H_l*W_l coefficient blocks of level l:
   level_fwd l  : reads the carrier P*H_{l-1}*W_{l-1}; writes Q(l) 4*B_l and,
                  for l < L, the carrier B_l.  FLOPs: 2 * 4 B_l k^2.
   synth        : reads x (N) and every Q(l); writes y (N).  FLOPs: 2 N k^2.
+  carrier l    : reads the carrier of level l - 1 (x for l = 1), writes B_l.
+                 FLOPs: 0 (adds only).
+  level_acc l  : level_fwd without the carrier write, plus a read of the deeper
+                 levels' summed patterns 4 B_{l+1} for l < L.
+  mma_tile     : reads x (N) and, for L >= 2, the summed patterns 4 B_2; writes
+                 y (N).  FLOPs: 2 (N k^2 + 4 B_1 k^2) (base conv and level 1).
   dw_level l   : reads the x and dy carriers (2*P*H_{l-1}*W_{l-1}); writes both
                  next carriers for l < L.  FLOPs: 2 * 4 B_l k^2.
   dw_base,
@@ -76,6 +82,15 @@ def kernel_cost(family, level, n, c, h, w, k, levels, elem_bytes):
     if family == "synth":
         q = sum(4 * blocks[l] for l in range(1, levels + 1))
         return E * (2 * N + q), 2 * N * kk
+    if family == "carrier":
+        return E * (blocks[level - 1] + blocks[level]), 0
+    if family == "level_acc":
+        l = level
+        elems = blocks[l - 1] + 4 * blocks[l] + (4 * blocks[l + 1] if l < levels else 0)
+        return E * elems, 2 * 4 * blocks[l] * kk
+    if family == "mma_tile":
+        q = 4 * blocks[2] if levels >= 2 else 0
+        return E * (2 * N + q), 2 * N * kk + (2 * 4 * blocks[1] * kk if levels >= 1 else 0)
     if family == "dw_level":
         l = level
         elems = 2 * blocks[l - 1] + (2 * blocks[l] if l < levels else 0)

@@ -29,6 +29,8 @@ SMALL = [
     (24, 2, 14, 14, 5, 1),    # many planes side by side in one pass (arrays whose size is not a multiple of 4)
     (40, 2, 7, 7, 5, 1),      # the same for 7 x 7 planes
     (12, 2, 28, 28, 5, 2),    # several 28 x 28 planes per pass, two levels
+    (1, 2, 80, 70, 5, 0),     # levels = 0 past the plane-resident range (synthesis kernel alone)
+    (1, 2, 9, 130, 3, 0),     # ... with k = 3
 ]
 DTYPES = ["f32", "bf16", "f16"]
 
