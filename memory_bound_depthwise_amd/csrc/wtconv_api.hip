@@ -912,6 +912,55 @@ FwdPlan build_forward_plan(const wtconv_desc &d, bool tile) {
     return p;
 }
 
+// The tiled correlation kernel for planes past the plane-resident range (bfloat16):
+// tiles of UR x 32 level-1 cells (UR at most 16), the x canvas XR = UR + 4 NF - 1
+// rows of XC 4-cell chunks (cells c0 - 4 .. of the offsets' reach), the dy canvas
+// UR rows between 4 NF - 1 zero rows above and below, 16 dwords a row.
+bool plan_dwc_tile(const wtconv_desc &d, DwcTileArgs &a, bool lev) {
+    if (!WTC_MMA || d.dtype != WTCONV_BF16) return false;
+    if (d.n <= 0 || d.c <= 0 || d.h <= 0 || d.w <= 0) return false;
+    const int R = (d.k - 1) / 2;
+    const int T0 = lev ? -R : -((R + 1) / 2), T1 = lev ? R : (R + 1) / 2;
+    const int NF = (T1 - T0 + 4) / 4;
+    a = DwcTileArgs{};
+    a.n = d.n;
+    a.C = d.c;
+    a.H = d.h;
+    a.W = d.w;
+    a.Ho = (d.h + 1) / 2;
+    a.Wo = (d.w + 1) / 2;
+    a.UR = std::min(16, a.Ho);
+    a.TYu = cdiv(a.Ho, a.UR);
+    a.TXu = cdiv(a.Wo, kDwcTileCols);
+    const long long P = (long long)d.n * a.TYu * a.TXu;
+    if (P >= (1LL << 31)) return false;
+    a.P = (int)P;
+    a.XR = a.UR + 4 * NF - 1;
+    // x cells the B reads reach: up to XL + 32 + T0 + 4 NF (XL = 4), and the fifth dword
+    a.XC = cdiv(4 + kDwcTileCols + T0 + 4 * NF + 2, 4);
+    if (a.XR * a.XC > kDwcTileXSlots * kDwcThreads) return false;
+    // bank spread as in the plane-resident layout: row stride 16 mod 64 dwords and
+    // plane size 4 mod 64 for dy, plane size 8 mod 64 for x
+    a.Sd = 16;
+    long long pd = (long long)(a.UR + 8 * NF - 2) * a.Sd;
+    while (pd % 64 != 4) ++pd;
+    a.pd = (int)pd;
+    a.Sx = std::max(2 * a.XC, (4 + kDwcTileCols + T0 + 4 * NF - 5) / 2 + 5);
+    long long px = (long long)a.XR * a.Sx;
+    while (px % 64 != 8) ++px;
+    a.px = (int)px;
+    a.xo = 4 * a.pd;
+    const long long planes = 4LL * a.pd + 4LL * a.px;
+    const long long NC = (long long)NF * NF * 256;
+    const long long red = (kDwcThreads / kWave + 1) * NC + kDwcThreads / kWave;
+    a.lds_floats = (int)((std::max(planes, red) + 3) & ~3LL);
+    if ((long long)a.lds_floats * 4 > kDwcLdsBudget) return false;
+    a.m_xc = magic31_of(a.XC);
+    // workgroups per channel: about eight resident per compute unit in all
+    a.k = std::max(1, std::min(a.P, kPlanCUs * 8 / d.c));
+    return (long long)d.c * a.k < (1LL << 31);
+}
+
 DwPlan build_backward_weight_plan(const wtconv_desc &d) {
     DwPlan p{};
     p.ld = level_dims(d);
@@ -925,6 +974,7 @@ DwPlan build_backward_weight_plan(const wtconv_desc &d) {
         p.dwc_lev = false;
     }
     p.dwl = p.dwc_lev ? d.levels >= 2 : plan_dwl(d, p.la, p.lcfg, 0);
+    p.dtile = !p.dwc && !p.dwl && plan_dwc_tile(d, p.ta, d.levels >= 1);
     const size_t es = elem_size(d.dtype), planes = (size_t)d.n * d.c;
     size_t off = 0;
     if (!p.dwl && !p.dwc_lev) {
@@ -943,6 +993,8 @@ DwPlan build_backward_weight_plan(const wtconv_desc &d) {
     p.region[0] = 0;
     if (p.dwc)
         p.G[0] = p.ca.k;
+    else if (p.dtile)
+        p.G[0] = p.ta.k;
     else if (p.dwb)
         p.G[0] = p.ba.k;
     else
@@ -953,6 +1005,8 @@ DwPlan build_backward_weight_plan(const wtconv_desc &d) {
         p.region[l] = floats;
         if (p.dwc_lev && l == 1)
             p.G[l] = p.ca.k;
+        else if (p.dtile && l == 1)
+            p.G[l] = p.ta.k;
         else if (p.dwl)
             p.G[l] = p.la.k;
         else
@@ -1270,14 +1324,17 @@ WTCONV_API int wtconv_plan_launches(const wtconv_desc *desc, int op, wtconv_laun
                 add("plane_dwd", 0, (long long)d.c * p.la.k, kDwlThreads, (size_t)p.la.lds_floats * sizeof(float),
                     16 * p.lcfg.CW + p.lcfg.RH);
         } else if (!empty(d)) {
+            if (p.dtile)
+                add("dwc_tile", 0, (long long)d.c * p.ta.k, kDwcThreads, (size_t)p.ta.lds_floats * sizeof(float),
+                    d.levels >= 1 ? 16 : 0);
             if (p.dwl && d.levels > 0) {
                 add("plane_dwl", 0, (long long)d.c * p.la.k, kDwlThreads, (size_t)p.la.lds_floats * sizeof(float),
                     16 * p.lcfg.CW + p.lcfg.RH);
             } else {
-                for (int l = 1; l <= d.levels; ++l)
+                for (int l = p.dtile ? 2 : 1; l <= d.levels; ++l)
                     add("dw_level", l, grid_of(p.lvl[l - 1], d.c), kThreads, lds_bytes(Kind::DwLevel, d.k, p.lvl[l - 1]));
             }
-            if (p.dwc) {
+            if (p.dwc || p.dtile) {
                 // the base ran in the correlation kernel
             } else if (p.dwb) {
                 add("plane_dwb", 0, (long long)d.c * p.ba.k, kDwbThreads, (size_t)p.ba.lds_floats * sizeof(float),

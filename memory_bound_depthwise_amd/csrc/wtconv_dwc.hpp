@@ -71,6 +71,116 @@ struct PlaneDwcArgs {
     uint32_t m_gw, m_h1, m_nch;  // udiv16 reciprocals of Gw, H1, nch
 };
 
+// Products of one item: x canvas row ci of every component, the lane's 8 cells
+// from cj on.  A row m = 4 q + i of the lane is dy component q at canvas row
+// ci + DT - ty (ty = T0 + 4 fy + i), 16 bytes at a time; B column n = 4 p + j is x
+// component p at row ci, cells cj + tx .. (tx = T0 + 4 fx + j, canvas cell XL + ..),
+// five dwords funnel-shifted by one cell when the first cell is odd.
+template <int K, bool kLev>
+__device__ __forceinline__ void dwc_item(const uint32_t *lw, int ci, int cj, int aq, int ai, int DT, int Sd, int pd,
+                                         int xo, int XL, int Sx, int pxs,
+                                         wtc_f32x4 (&acc)[DwcGeom<K, kLev>::NF][DwcGeom<K, kLev>::NF]) {
+    using Gm = DwcGeom<K, kLev>;
+    constexpr int NF = Gm::NF, T0 = Gm::T0;
+    union { wtc_bf16x8 v; uint32_t w[4]; } A[NF], Bf[NF];
+#pragma unroll
+    for (int fy = 0; fy < NF; ++fy) {
+        const uint32_t *p = lw + aq * pd + (ci + DT - (T0 + 4 * fy + ai)) * Sd + (cj >> 1);
+        const uint4 v = *reinterpret_cast<const uint4 *>(p);
+        A[fy].w[0] = v.x;
+        A[fy].w[1] = v.y;
+        A[fy].w[2] = v.z;
+        A[fy].w[3] = v.w;
+    }
+#pragma unroll
+    for (int fx = 0; fx < NF; ++fx) {
+        const int col = XL + cj + T0 + 4 * fx + ai;  // first x cell of this lane's column
+        const uint32_t *p = lw + xo + aq * pxs + ci * Sx + (col >> 1);
+        uint32_t d5[5];
+#pragma unroll
+        for (int e = 0; e < 5; ++e) d5[e] = p[e];
+        const uint32_t sh = (col & 1) * 16;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) Bf[fx].w[e] = __builtin_amdgcn_alignbit(d5[e + 1], d5[e], sh);
+    }
+#pragma unroll
+    for (int fy = 0; fy < NF; ++fy)
+#pragma unroll
+        for (int fx = 0; fx < NF; ++fx)
+            acc[fy][fx] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[fy].v, Bf[fx].v, acc[fy][fx], 0, 0, 0);
+}
+
+// Fixed-order reduction of a 128-thread workgroup's products (the wavefronts' D
+// tiles through LDS) and of its dy sums, then the sign-combinations: the raw base
+// sums and sum dy go to partial row `row` of pbase ([rows][K*K + 1]), the level-1
+// sums (with kLev) to row `row` of plev ([rows][4 K*K]).  Bitwise repeatable.
+template <int K, bool kLev>
+__device__ __forceinline__ void dwc_reduce_write(float *smem,
+                                                 const wtc_f32x4 (&acc)[DwcGeom<K, kLev>::NF][DwcGeom<K, kLev>::NF],
+                                                 float bsum, int tid, size_t row, float *pbase, float *plev) {
+    using Gm = DwcGeom<K, kLev>;
+    constexpr int R = (K - 1) / 2, KK = K * K, NF = Gm::NF, T0 = Gm::T0;
+    constexpr int NT = kDwcThreads;
+    const int lane = tid & (kWave - 1), wave = tid / kWave, g4 = lane >> 4, mm = lane & 15;
+    // fixed-order reduction: the wavefronts' D tiles through LDS, then the sums
+    constexpr int NC = NF * NF * 256;  // C[fy][fx][m][n]
+    __syncthreads();                   // the planes are no longer read
+#pragma unroll
+    for (int fy = 0; fy < NF; ++fy)
+#pragma unroll
+        for (int fx = 0; fx < NF; ++fx)
+#pragma unroll
+            for (int i = 0; i < 4; ++i) smem[wave * NC + ((fy * NF + fx) * 16 + 4 * g4 + i) * 16 + mm] = acc[fy][fx][i];
+    {
+        const float v = wave_sum(bsum);
+        if (lane == 0) smem[(NT / kWave) * NC + wave] = v;
+    }
+    __syncthreads();
+    float *Cs = smem + (NT / kWave) * NC + NT / kWave;
+    for (int i = tid; i < NC; i += NT) {
+        float s = smem[i];
+#pragma unroll
+        for (int w = 1; w < NT / kWave; ++w) s += smem[w * NC + i];
+        Cs[i] = s;
+    }
+    __syncthreads();
+    // C[q][p][(ty, tx)], q = 2 qy + qx and p = 2 py + px
+    auto Cv = [&](int q, int p, int ty, int tx) {
+        const int fy = (ty - T0) >> 2, iy = (ty - T0) & 3, fx = (tx - T0) >> 2, ix = (tx - T0) & 3;
+        return Cs[((fy * NF + fx) * 16 + 4 * q + iy) * 16 + 4 * p + ix];
+    };
+    for (int o = tid; o < KK + 1; o += NT) {
+        float s = 0.f;
+        if (o < KK) {
+            const int dy_ = o / K - R, dx_ = o % K - R;
+#pragma unroll
+            for (int q = 0; q < 4; ++q) {
+                const int sy = (q >> 1) + dy_, sx = (q & 1) + dx_;
+                s += Cv(q, 2 * (sy & 1) + (sx & 1), sy >> 1, sx >> 1);
+            }
+        } else {
+            for (int w = 0; w < NT / kWave; ++w) s += smem[(NT / kWave) * NC + w];
+        }
+        pbase[row * (KK + 1) + o] = s;
+    }
+    if constexpr (kLev) {
+        for (int o = tid; o < 4 * KK; o += NT) {
+            const int b = o / KK, tap = o - b * KK, ty = tap / K - R, tx = tap % K - R;
+            float s = 0.f;
+#pragma unroll
+            for (int q = 0; q < 4; ++q)
+#pragma unroll
+                for (int p = 0; p < 4; ++p) {
+                    // h_b(q) h_b(p): band 1 flips on odd rows, band 2 on odd columns
+                    const int fl = ((b & 1) & ((q >> 1) ^ (p >> 1))) ^ (((b >> 1) & 1) & ((q & 1) ^ (p & 1)));
+                    const float v = Cv(q, p, ty, tx);
+                    s += fl ? -v : v;
+                }
+            plev[row * 4 * KK + o] = 0.25f * s;
+        }
+    }
+}
+
 template <int K, int CW, bool kLev>
 __global__ __launch_bounds__(kDwcThreads, 2) void plane_dwc_kernel(PlaneDwcArgs a) {
     using Gm = DwcGeom<K, kLev>;
@@ -190,93 +300,11 @@ __global__ __launch_bounds__(kDwcThreads, 2) void plane_dwc_kernel(PlaneDwcArgs 
         const int xo = opaque(a.xo), XL = opaque(a.XL), DT = opaque(a.DT);
         for (int it = wave; it < a.items; it += NT / kWave) {
             const int ci = udiv16(it, a.m_nch), cj = 32 * (it - ci * a.nch) + 8 * g4;
-            union { wtc_bf16x8 v; uint32_t w[4]; } A[NF], Bf[NF];
-#pragma unroll
-            for (int fy = 0; fy < NF; ++fy) {
-                const uint32_t *p = lw + aq * pd + (ci + DT - (T0 + 4 * fy + ai)) * Sd + (cj >> 1);
-                const uint4 v = *reinterpret_cast<const uint4 *>(p);
-                A[fy].w[0] = v.x;
-                A[fy].w[1] = v.y;
-                A[fy].w[2] = v.z;
-                A[fy].w[3] = v.w;
-            }
-#pragma unroll
-            for (int fx = 0; fx < NF; ++fx) {
-                const int col = XL + cj + T0 + 4 * fx + ai;  // first x cell of this lane's column
-                const uint32_t *p = lw + xo + aq * pxs + ci * Sx + (col >> 1);
-                uint32_t d5[5];
-#pragma unroll
-                for (int e = 0; e < 5; ++e) d5[e] = p[e];
-                const uint32_t sh = (col & 1) * 16;
-#pragma unroll
-                for (int e = 0; e < 4; ++e) Bf[fx].w[e] = __builtin_amdgcn_alignbit(d5[e + 1], d5[e], sh);
-            }
-#pragma unroll
-            for (int fy = 0; fy < NF; ++fy)
-#pragma unroll
-                for (int fx = 0; fx < NF; ++fx)
-                    acc[fy][fx] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(A[fy].v, Bf[fx].v, acc[fy][fx], 0, 0, 0);
+            dwc_item<K, kLev>(lw, ci, cj, aq, ai, DT, Sd, pd, xo, XL, Sx, pxs, acc);
         }
     }
 
-    // fixed-order reduction: the wavefronts' D tiles through LDS, then the sums
-    constexpr int NC = NF * NF * 256;  // C[fy][fx][m][n]
-    __syncthreads();                   // the planes are no longer read
-#pragma unroll
-    for (int fy = 0; fy < NF; ++fy)
-#pragma unroll
-        for (int fx = 0; fx < NF; ++fx)
-#pragma unroll
-            for (int i = 0; i < 4; ++i) smem[wave * NC + ((fy * NF + fx) * 16 + 4 * g4 + i) * 16 + mm] = acc[fy][fx][i];
-    {
-        const float v = wave_sum(bsum);
-        if (lane == 0) smem[(NT / kWave) * NC + wave] = v;
-    }
-    __syncthreads();
-    float *Cs = smem + (NT / kWave) * NC + NT / kWave;
-    for (int i = tid; i < NC; i += NT) {
-        float s = smem[i];
-#pragma unroll
-        for (int w = 1; w < NT / kWave; ++w) s += smem[w * NC + i];
-        Cs[i] = s;
-    }
-    __syncthreads();
-    // C[q][p][(ty, tx)], q = 2 qy + qx and p = 2 py + px
-    auto Cv = [&](int q, int p, int ty, int tx) {
-        const int fy = (ty - T0) >> 2, iy = (ty - T0) & 3, fx = (tx - T0) >> 2, ix = (tx - T0) & 3;
-        return Cs[((fy * NF + fx) * 16 + 4 * q + iy) * 16 + 4 * p + ix];
-    };
-    const size_t row = (size_t)c * a.k + r;
-    for (int o = tid; o < KK + 1; o += NT) {
-        float s = 0.f;
-        if (o < KK) {
-            const int dy_ = o / K - R, dx_ = o % K - R;
-#pragma unroll
-            for (int q = 0; q < 4; ++q) {
-                const int sy = (q >> 1) + dy_, sx = (q & 1) + dx_;
-                s += Cv(q, 2 * (sy & 1) + (sx & 1), sy >> 1, sx >> 1);
-            }
-        } else {
-            for (int w = 0; w < NT / kWave; ++w) s += smem[(NT / kWave) * NC + w];
-        }
-        a.pbase[row * (KK + 1) + o] = s;
-    }
-    if constexpr (kLev) {
-        for (int o = tid; o < 4 * KK; o += NT) {
-            const int b = o / KK, tap = o - b * KK, ty = tap / K - R, tx = tap % K - R;
-            float s = 0.f;
-#pragma unroll
-            for (int q = 0; q < 4; ++q)
-#pragma unroll
-                for (int p = 0; p < 4; ++p) {
-                    // h_b(q) h_b(p): band 1 flips on odd rows, band 2 on odd columns
-                    const int fl = ((b & 1) & ((q >> 1) ^ (p >> 1))) ^ (((b >> 1) & 1) & ((q & 1) ^ (p & 1)));
-                    const float v = Cv(q, p, ty, tx);
-                    s += fl ? -v : v;
-                }
-            a.plev[row * 4 * KK + o] = 0.25f * s;
-        }
-    }
+    dwc_reduce_write<K, kLev>(smem, acc, bsum, tid, (size_t)c * a.k + r, a.pbase, a.plev);
 }
 
 }  // namespace wtc

@@ -30,6 +30,7 @@
 #include "wtconv_mma.hpp"
 #include "wtconv_dwc.hpp"
 #include "wtconv_mma_tile.hpp"
+#include "wtconv_dwc_tile.hpp"
 
 namespace wtc {
 
@@ -104,6 +105,8 @@ struct DwPlan {
     bool dwb;            // base by the plane-resident kernel
     PlaneDwbArgs ba;
     PlaneCfg bcfg;
+    bool dtile;          // base and level 1 by the tiled correlation kernel (bfloat16, planes
+    DwcTileArgs ta;      // past the plane-resident range), levels 2..L by the per-level kernels
     bool dwl;            // levels by the plane-resident kernel
     PlaneDwlArgs la;
     PlaneCfg lcfg;

@@ -423,6 +423,32 @@ int run_forward(const PlanSet &ps, const void *x, const float *w0, const float *
                   s);
 }
 
+// Base and level-1 weight gradients by the tiled correlation kernel; with levels
+// >= 2 it also writes the level-1 carriers of x and dy.
+template <int K, typename T>
+int run_dwc_tile(const PlanSet &ps, const void *x, const void *dy, float *partial, char *ws, hipStream_t st) {
+    if constexpr (!std::is_same<T, uint16_t>::value) {
+        return WTCONV_ERR_DTYPE;  // not planned: bfloat16 only
+    } else {
+        const wtconv_desc &d = ps.d;
+        const DwPlan &p = ps.dp;
+        DwcTileArgs a = p.ta;
+        a.x = x;
+        a.dy = dy;
+        a.pbase = partial + p.region[0];
+        a.plev = d.levels >= 1 ? partial + p.region[1] : nullptr;
+        a.xc = d.levels >= 2 ? (void *)(ws + p.xc_off[0]) : nullptr;
+        a.gc = d.levels >= 2 ? (void *)(ws + p.gc_off[0]) : nullptr;
+        a.vec = d.w % 8 == 0 && aligned(x, 16) && aligned(dy, 16) ? 1 : 0;
+        const dim3 grid((unsigned)((long long)d.c * a.k));
+        const size_t shm = (size_t)a.lds_floats * sizeof(float);
+        const int bf = dtype_of<T>();
+        if (d.levels >= 1)
+            return launch("dwc_tile", K, bf, 0, dwc_tile_kernel<K, true>, grid, dim3(kDwcThreads), shm, st, a);
+        return launch("dwc_tile", K, bf, 0, dwc_tile_kernel<K, false>, grid, dim3(kDwcThreads), shm, st, a);
+    }
+}
+
 template <int K, typename T>
 int run_backward_weight(const PlanSet &ps, const void *x, const void *dy, const float *w0, const float *b0,
                         const float *s0, const float *wl, const float *sl, float *dw0, float *db0, float *ds0,
@@ -446,7 +472,11 @@ int run_backward_weight(const PlanSet &ps, const void *x, const void *dy, const 
             int rc = run_plane_dwl<K, T>(ps, x, dy, partial, st);
             if (rc) return rc;
         }
-        for (int l = 1; l <= L && !p.dwl; ++l) {
+        if (p.dtile) {
+            int rc = run_dwc_tile<K, T>(ps, x, dy, partial, ws, st);
+            if (rc) return rc;
+        }
+        for (int l = p.dtile ? 2 : 1; l <= L && !p.dwl; ++l) {
             DwLevelArgs a{};
             a.xin = l == 1 ? x : (const void *)(ws + p.xc_off[l - 2]);
             a.gin = l == 1 ? dy : (const void *)(ws + p.gc_off[l - 2]);
@@ -467,7 +497,7 @@ int run_backward_weight(const PlanSet &ps, const void *x, const void *dy, const 
                             dim3(kThreads), shm, st, a);
             if (rc) return rc;
         }
-        if (p.dwc) {
+        if (p.dwc || p.dtile) {
             // the base ran in the correlation kernel
         } else if (p.dwb) {
             int rc = run_plane_dwb<K, T>(ps, x, dy, partial + p.region[0], st);

@@ -36,6 +36,8 @@ B_l = P*H_l*W_l coefficient blocks of level l:
                  FLOPs: 0 (adds only).
   level_acc l  : level_fwd without the carrier write, plus a read of the deeper
                  levels' summed patterns 4 B_{l+1} for l < L.
+  dwc_tile     : reads x and dy (2N); for L >= 2 writes both level-1 carriers
+                 (2 B_1).  FLOPs: 2 (N k^2 + 4 B_1 k^2) (base and level 1).
   mma_tile     : reads x (N) and, for L >= 2, the summed patterns 4 B_2; writes
                  y (N).  FLOPs: 2 (N k^2 + 4 B_1 k^2) (base conv and level 1).
   dw_level l   : reads the x and dy carriers (2*P*H_{l-1}*W_{l-1}); writes both
@@ -88,6 +90,9 @@ def kernel_cost(family, level, n, c, h, w, k, levels, elem_bytes):
         l = level
         elems = blocks[l - 1] + 4 * blocks[l] + (4 * blocks[l + 1] if l < levels else 0)
         return E * elems, 2 * 4 * blocks[l] * kk
+    if family == "dwc_tile":
+        return E * (2 * N + (2 * blocks[1] if levels >= 2 else 0)), \
+            2 * N * kk + (2 * 4 * blocks[1] * kk if levels >= 1 else 0)
     if family == "mma_tile":
         q = 4 * blocks[2] if levels >= 2 else 0
         return E * (2 * N + q), 2 * N * kk + (2 * 4 * blocks[1] * kk if levels >= 1 else 0)

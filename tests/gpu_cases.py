@@ -31,6 +31,7 @@ SMALL = [
     (12, 2, 28, 28, 5, 2),    # several 28 x 28 planes per pass, two levels
     (1, 2, 80, 70, 5, 0),     # levels = 0 past the plane-resident range (synthesis kernel alone)
     (1, 2, 9, 130, 3, 0),     # ... with k = 3
+    (1, 2, 70, 9, 7, 0),      # ... and k = 7
 ]
 DTYPES = ["f32", "bf16", "f16"]
 
