@@ -929,7 +929,7 @@ bool plan_dwc_tile(const wtconv_desc &d, DwcTileArgs &a, bool lev) {
     a.W = d.w;
     a.Ho = (d.h + 1) / 2;
     a.Wo = (d.w + 1) / 2;
-    a.UR = std::min(16, a.Ho);
+    a.UR = std::min(kDwcTileRows, a.Ho);
     a.TYu = cdiv(a.Ho, a.UR);
     a.TXu = cdiv(a.Wo, kDwcTileCols);
     const long long P = (long long)d.n * a.TYu * a.TXu;
@@ -938,7 +938,8 @@ bool plan_dwc_tile(const wtconv_desc &d, DwcTileArgs &a, bool lev) {
     a.XR = a.UR + 4 * NF - 1;
     // x cells the B reads reach: up to XL + 32 + T0 + 4 NF (XL = 4), and the fifth dword
     a.XC = cdiv(4 + kDwcTileCols + T0 + 4 * NF + 2, 4);
-    if (a.XR * a.XC > kDwcTileXSlots * kDwcThreads) return false;
+    if (a.XR * a.XC > kDwcTileXSlots * kDwcThreads || a.UR * kDwcTileCols / 4 > kDwcTileDySlots * kDwcThreads)
+        return false;
     // bank spread as in the plane-resident layout: row stride 16 mod 64 dwords and
     // plane size 4 mod 64 for dy, plane size 8 mod 64 for x
     a.Sd = 16;

@@ -28,7 +28,11 @@
 namespace wtc {
 
 constexpr int kDwcTileCols = 32;  // tile width in cells (one item covers it)
-constexpr int kDwcTileXSlots = 2; // x staging items per thread held in registers
+// tile rows at most: 32-row tiles (less x halo per dy cell) measured slower, their
+// registers and LDS leave fewer workgroups resident
+constexpr int kDwcTileRows = 16;
+constexpr int kDwcTileDySlots = kDwcTileRows * kDwcTileCols / 4 / 128;  // dy staging items per thread
+constexpr int kDwcTileXSlots = 2;                                       // x staging items per thread
 
 struct DwcTileArgs {
     const void *x, *dy;
@@ -38,7 +42,7 @@ struct DwcTileArgs {
     int n, C, H, W;
     int Ho, Wo;        // level-1 grid
     int vec;           // W % 8 == 0, x and dy 16-byte aligned: 8-pixel loads
-    int UR;            // tile rows (cells), at most 16
+    int UR;            // tile rows (cells), at most kDwcTileRows
     int TYu, TXu;      // tiles per plane
     int P;             // passes per channel: n TYu TXu
     int k;             // workgroups per channel
@@ -108,15 +112,16 @@ __global__ __launch_bounds__(kDwcThreads, 2) void dwc_tile_kernel(DwcTileArgs a)
             }
         }
     };
-    uint4 dr[2], xr[kDwcTileXSlots][2];
+    uint4 dr[kDwcTileDySlots][2], xr[kDwcTileXSlots][2];
     auto prefetch = [&](int p) {
         int nn, r0, c0;
         pass_of(p, nn, r0, c0);
         const size_t pl = ((size_t)nn * a.C + c) * HW;
         const T *xp = static_cast<const T *>(a.x) + pl, *dp = static_cast<const T *>(a.dy) + pl;
-        {
-            const int e = min(tid, dy_items - 1), ar = e >> 3, j = e & 7;
-            load8(dp, r0 + ar, 2 * c0 + 8 * j, dr);
+#pragma unroll
+        for (int s = 0; s < kDwcTileDySlots; ++s) {
+            const int e = min(tid + s * NT, dy_items - 1), ar = e >> 3, j = e & 7;
+            load8(dp, r0 + ar, 2 * c0 + 8 * j, dr[s]);
         }
 #pragma unroll
         for (int s = 0; s < kDwcTileXSlots; ++s) {
@@ -163,17 +168,22 @@ __global__ __launch_bounds__(kDwcThreads, 2) void dwc_tile_kernel(DwcTileArgs a)
         __syncthreads();  // the previous pass is done with the canvases
         // dy cells of the tile: components into canvas rows DZ .. DZ + UR - 1, sum dy,
         // and the dy carrier
-        if (tid < dy_items) {
-            const int ar = tid >> 3, j = tid & 7;
+#pragma unroll
+        for (int s = 0; s < kDwcTileDySlots; ++s) {
+            const int e = tid + s * NT;
+            if (e >= dy_items) continue;
+            const int ar = e >> 3, j = e & 7;
             uint2 comp[4];
-            dwc_split(dr, comp);
+            dwc_split(dr[s], comp);
 #pragma unroll
             for (int q = 0; q < 4; ++q)
                 *reinterpret_cast<uint2 *>(lw + q * a.pd + (ar + DZ) * a.Sd + 2 * j) = comp[q];
 #pragma unroll
             for (int h = 0; h < 2; ++h)
-                bsum += ((Act<T>::lo(dr[h].x) + Act<T>::hi(dr[h].x)) + (Act<T>::lo(dr[h].y) + Act<T>::hi(dr[h].y))) +
-                        ((Act<T>::lo(dr[h].z) + Act<T>::hi(dr[h].z)) + (Act<T>::lo(dr[h].w) + Act<T>::hi(dr[h].w)));
+                bsum += ((Act<T>::lo(dr[s][h].x) + Act<T>::hi(dr[s][h].x)) +
+                         (Act<T>::lo(dr[s][h].y) + Act<T>::hi(dr[s][h].y))) +
+                        ((Act<T>::lo(dr[s][h].z) + Act<T>::hi(dr[s][h].z)) +
+                         (Act<T>::lo(dr[s][h].w) + Act<T>::hi(dr[s][h].w)));
             if (a.gc) carry(static_cast<T *>(a.gc) + cpl, r0 + ar, c0 + 4 * j, comp);
         }
         // x cells: canvas rows 0 .. XR - 1, and the x carrier of the tile's own cells
