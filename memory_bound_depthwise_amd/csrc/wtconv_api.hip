@@ -395,7 +395,12 @@ bool mma_layout(const wtconv_desc &d, int CW, int pb, MmaArgs &a) {
     if (a.Pw1 < a.Gw * CW) return false;
     const int Wc = pb == 1 ? a.W1 : (pb - 1) * a.Pw1 + a.W1;  // cells of the side-by-side strip
     const int TY = cdiv(a.H1, 4);
-    a.TX = cdiv(Wc, 16);
+    // planes at most 8 cells wide take MW (4 or 8) M rows each, 16 / MW planes per
+    // tile and no gap columns; wider ones the 16 consecutive strip columns
+    a.MW = pb > 1 && a.W1 <= 4 ? 4 : (pb > 1 && a.W1 <= 8 ? 8 : 16);
+    a.TX = a.MW == 16 ? cdiv(Wc, 16) : cdiv(pb, 16 / a.MW);
+    // last strip column a tile reads
+    const long long cmax = a.MW == 16 ? 16LL * a.TX - 1 : (long long)(a.TX * (16 / a.MW) - 1) * a.Pw1 + a.MW - 1;
     a.tiles = TY * a.TX;
     a.commit_items = pb * a.H1 * a.Gw;
     a.H2 = (a.H1 + 1) / 2;
@@ -406,7 +411,7 @@ bool mma_layout(const wtconv_desc &d, int CW, int pb, MmaArgs &a) {
     // kMmaCL + x; the row stride (dwords) is 16 mod 32, so that the four lane
     // groups of an A read (four consecutive rows) fall on four distinct bank ranges
     const long long s_min = std::max<long long>(kMmaCL / 2 + (long long)pb * a.Pw1,
-                                                (kMmaCL - COL0) / 2 + 16LL * a.TX + 4 + (TAIL ? 1 : 0));
+                                                (kMmaCL - COL0) / 2 + cmax + 1 + 4 + (TAIL ? 1 : 0));
     long long S = s_min;
     while (S % 32 != 16) ++S;
     a.S = (int)S;
@@ -441,7 +446,7 @@ bool mma_layout(const wtconv_desc &d, int CW, int pb, MmaArgs &a) {
     // the tiles read the deep patterns of every tile cell, also past the plane
     for (int l = 2; l <= L; ++l) {
         const int li = l - 2;
-        const long long end = a.offq[li] + (long long)((4 * TY - 1) >> li) * a.sq[li] + ((16 * a.TX - 1) >> li) + 1;
+        const long long end = a.offq[li] + (long long)((4 * TY - 1) >> li) * a.sq[li] + (cmax >> li) + 1;
         fl = std::max(fl, (end + 3) & ~3LL);
     }
     a.lds_floats = (int)fl;

@@ -94,6 +94,8 @@ struct MmaArgs {
     int H2, pair_items;  // level-2 rows ceil(H1 / 2); commit items of two stacked patches (PB H2 Gw)
     int S;           // canvas row stride (dwords)
     int TX, tiles;   // product tiles per tile row, in all
+    int MW;          // M rows per plane: 16 (a tile takes 16 consecutive strip columns) or,
+                     // for planes at most MW cells wide, 4 or 8 (16 / MW whole planes a tile)
     int sy1;         // (unused: level 2 is analysed from the canvas)
     // deep levels l = 2..L at index l - 2 (as in PlaneArgs)
     int hl[kMaxLevels], wls[kMaxLevels];
@@ -486,13 +488,17 @@ __device__ __forceinline__ void mma_fwd_body(const MmaArgs &args) {
         // 4. products and stores, one tile of 16 x 4 cells at a time.  The product is
         //    formed transposed (the B fragments as the left operand, the pixel
         //    fragments as the right one), so that lane (g4, mm) receives the four
-        //    pixels of cell (4 ty + g4, 16 tx + mm): element i = 2 rx + ry.
+        //    pixels of cell (4 ty + g4, tile column lcol): element i = 2 rx + ry.
         T *yb = static_cast<T *>(a.y) + ((size_t)n0 * a.C + c) * HW;
         const float bias = smem[a.wt + (4 * L + 1) * KK];
         const int smode = opaque(a.store_mode), pw1 = opaque(a.Pw1), W1 = opaque(a.W1);
+        // the lane's strip column within a tile, and the tile's first strip column
+        const int MW = opaque(a.MW);
+        const int lcol = MW == 16 ? mm : (mm / MW) * pw1 + (mm & (MW - 1));
+        const int tstep = MW == 16 ? 16 : (16 / MW) * pw1;
         // deep patterns: Q_l of cell (row, col) at (row >> j, col >> j), j = l - 2,
-        // split into a wave-uniform part (tile origin) and the lane's part; a level
-        // past L reads canvas row 0, which is zero padding throughout
+        // split into a wave-uniform part (tile origin, a multiple of 4 columns) and the
+        // lane's part; a level past L reads canvas row 0, which is zero padding throughout
         int qo[kMaxLevels - 1], qs[kMaxLevels - 1], ql[3];
 #pragma unroll
         for (int k = 0; k < kMaxLevels - 1; ++k) {
@@ -501,9 +507,9 @@ __device__ __forceinline__ void mma_fwd_body(const MmaArgs &args) {
             qs[k] = on ? opaque(a.sq[k]) : 0;
         }
 #pragma unroll
-        for (int j = 0; j < 3; ++j) ql[j] = (g4 >> j) * qs[j] + (mm >> j);
-        // the lane's A reads: row g4 of the window's step, cell column mm
-        const int la = (kMmaCL - G::COL0) / 2 + g4 * S + mm;
+        for (int j = 0; j < 3; ++j) ql[j] = (g4 >> j) * qs[j] + (lcol >> j);
+        // the lane's A reads: row g4 of the window's step, strip column lcol
+        const int la = (kMmaCL - G::COL0) / 2 + g4 * S + lcol;
         constexpr int NW = NT / kWave;
         // two tiles per iteration (t and t + NW; the second may repeat the first, then
         // it stores nothing): their MFMA chains and LDS reads are independent
@@ -515,18 +521,19 @@ __device__ __forceinline__ void mma_fwd_body(const MmaArgs &args) {
             ty[1] = udiv16(t2, a.m_tx);
             tx[1] = t2 - ty[1] * a.TX;
             wtc_f32x4 acc[2];
-            mma_products2<K>(cv + la + (8 * ty[0]) * S + 16 * tx[0], cv + la + (8 * ty[1]) * S + 16 * tx[1], S, bh, bl,
-                             acc);
+            mma_products2<K>(cv + la + (8 * ty[0]) * S + tstep * tx[0], cv + la + (8 * ty[1]) * S + tstep * tx[1], S, bh,
+                             bl, acc);
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 if (h == 1 && t2 == t) break;
-                const int crow = 4 * ty[h] + g4, ccol = 16 * tx[h] + mm;
+                const int crow = 4 * ty[h] + g4, ccol = tstep * tx[h] + lcol;
                 // bias and the deep patterns (they enter all four pixels of the cell)
                 float v = bias;
                 {
                     float q[3];
 #pragma unroll
-                    for (int j = 0; j < 3; ++j) q[j] = smem[qo[j] + ((4 * ty[h]) >> j) * qs[j] + ((16 * tx[h]) >> j) + ql[j]];
+                    for (int j = 0; j < 3; ++j)
+                        q[j] = smem[qo[j] + ((4 * ty[h]) >> j) * qs[j] + ((tstep * tx[h]) >> j) + ql[j]];
                     v += q[0] + (q[1] + q[2]);
                     for (int k = 3; k < L - 1; ++k)  // levels 5..L
                         v += smem[qo[k] + (crow >> k) * qs[k] + (ccol >> k)];
