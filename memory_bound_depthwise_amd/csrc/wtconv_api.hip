@@ -879,10 +879,13 @@ bool plan_dwc(const wtconv_desc &d, PlaneDwcArgs &a, int &CW, bool lev) {
         // wave-instructions per pass: an item ~8 per product (16 cycles) plus ~10
         // per operand read and ~20 others; commit ~40 per item; ~300 fixed.  Eight
         // workgroups per compute unit as the registers allow, fewer as the LDS does.
+        // A workgroup's passes run one after another (latency-bound), so the time is
+        // the passes of the busiest workgroup, ceil(NG / k), times the cost of one.
         const int wg = std::max(1, std::min(8, (int)((160 * 1024) / ((long long)t.lds_floats * 4))));
         const double cost = cdiv(t.items, kDwcThreads / kWave) * 2.0 * (8.0 * NF * NF + 20.0 * NF + 20.0) +
                             cdiv(t.commit_items, kDwcThreads) * 2.0 * 40.0 + 300.0;
-        const double score = (double)pb * wg / cost;
+        const int ng = cdiv(d.n, pb), k = std::max(1, std::min(ng, kPlanCUs * wg / d.c));
+        const double score = 1.0 / (cdiv(ng, k) * cost);
         if (score > best * (1 + 1e-9)) {
             best = score;
             best_pb = pb;
@@ -891,7 +894,7 @@ bool plan_dwc(const wtconv_desc &d, PlaneDwcArgs &a, int &CW, bool lev) {
     if (!dwc_layout(d, CW, best_pb, a, lev)) return false;
     a.NG = cdiv(d.n, a.PB);
     const int wg = std::max(1, std::min(8, (int)((160 * 1024) / ((long long)a.lds_floats * 4))));
-    a.k = std::max(1, std::min(a.NG, 256 * wg / d.c));
+    a.k = std::max(1, std::min(a.NG, kPlanCUs * wg / d.c));
     return (long long)d.c * a.k < (1LL << 31);
 }
 
