@@ -395,12 +395,16 @@ bool mma_layout(const wtconv_desc &d, int CW, int pb, MmaArgs &a) {
     if (a.Pw1 < a.Gw * CW) return false;
     const int Wc = pb == 1 ? a.W1 : (pb - 1) * a.Pw1 + a.W1;  // cells of the side-by-side strip
     const int TY = cdiv(a.H1, 4);
-    // planes at most 8 cells wide take MW (4 or 8) M rows each, 16 / MW planes per
-    // tile and no gap columns; wider ones the 16 consecutive strip columns
-    a.MW = pb > 1 && a.W1 <= 4 ? 4 : (pb > 1 && a.W1 <= 8 ? 8 : 16);
-    a.TX = a.MW == 16 ? cdiv(Wc, 16) : cdiv(pb, 16 / a.MW);
+    // A tile's 16 M rows are 16 consecutive strip columns, or (planes at most 16
+    // cells wide) whole planes: MW = 4, 8 or 16 rows each, 16 / MW planes a tile and no
+    // gap columns; whichever needs fewer tiles
+    const int mw = a.W1 <= 4 ? 4 : (a.W1 <= 8 ? 8 : 16);
+    const int tx_strip = cdiv(Wc, 16), tx_planes = cdiv(pb, 16 / mw);
+    a.aligned = pb > 1 && a.W1 <= 16 && tx_planes < tx_strip ? 1 : 0;
+    a.MW = a.aligned ? mw : 16;
+    a.TX = a.aligned ? tx_planes : tx_strip;
     // last strip column a tile reads
-    const long long cmax = a.MW == 16 ? 16LL * a.TX - 1 : (long long)(a.TX * (16 / a.MW) - 1) * a.Pw1 + a.MW - 1;
+    const long long cmax = a.aligned ? (long long)(a.TX * (16 / a.MW) - 1) * a.Pw1 + a.MW - 1 : 16LL * a.TX - 1;
     a.tiles = TY * a.TX;
     a.commit_items = pb * a.H1 * a.Gw;
     a.H2 = (a.H1 + 1) / 2;

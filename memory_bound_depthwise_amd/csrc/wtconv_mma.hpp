@@ -94,8 +94,8 @@ struct MmaArgs {
     int H2, pair_items;  // level-2 rows ceil(H1 / 2); commit items of two stacked patches (PB H2 Gw)
     int S;           // canvas row stride (dwords)
     int TX, tiles;   // product tiles per tile row, in all
-    int MW;          // M rows per plane: 16 (a tile takes 16 consecutive strip columns) or,
-                     // for planes at most MW cells wide, 4 or 8 (16 / MW whole planes a tile)
+    int aligned;     // 0: a tile takes 16 consecutive strip columns; 1: 16 / MW whole planes
+    int MW;          // ... of at most MW = 4, 8 or 16 cells, MW M rows each
     int sy1;         // (unused: level 2 is analysed from the canvas)
     // deep levels l = 2..L at index l - 2 (as in PlaneArgs)
     int hl[kMaxLevels], wls[kMaxLevels];
@@ -493,9 +493,9 @@ __device__ __forceinline__ void mma_fwd_body(const MmaArgs &args) {
         const float bias = smem[a.wt + (4 * L + 1) * KK];
         const int smode = opaque(a.store_mode), pw1 = opaque(a.Pw1), W1 = opaque(a.W1);
         // the lane's strip column within a tile, and the tile's first strip column
-        const int MW = opaque(a.MW);
-        const int lcol = MW == 16 ? mm : (mm / MW) * pw1 + (mm & (MW - 1));
-        const int tstep = MW == 16 ? 16 : (16 / MW) * pw1;
+        const int MW = opaque(a.MW), aligned = opaque(a.aligned);
+        const int lcol = aligned ? (mm / MW) * pw1 + (mm & (MW - 1)) : mm;
+        const int tstep = aligned ? (16 / MW) * pw1 : 16;
         // deep patterns: Q_l of cell (row, col) at (row >> j, col >> j), j = l - 2,
         // split into a wave-uniform part (tile origin, a multiple of 4 columns) and the
         // lane's part; a level past L reads canvas row 0, which is zero padding throughout
