@@ -41,12 +41,16 @@ def trace(db: str):
     return out
 
 
-def _counter(db: str):
+def _counter(db: str, with_counts: bool = False):
+    """Mean reading per (kernel, counter, grid) over its dispatches (and, with
+    with_counts, the number of dispatches)."""
     cur = sqlite3.connect(db).cursor()
     rows = cur.execute("select kernel_name, counter_name, value, grid_size from counters_collection").fetchall()
     agg = collections.defaultdict(list)
     for k, c, v, g in rows:
         agg[(_short(k), c, g)].append(v)
+    if with_counts:
+        return {key: (sum(v) / len(v), len(v)) for key, v in agg.items()}
     return {key: sum(v) / len(v) for key, v in agg.items()}
 
 
@@ -58,12 +62,12 @@ def counters(fetch_db, write_db, copy_fetch_db, copy_write_db, copy_bytes):
     write_ref = max(v for (k, c, g), v in cw.items() if c == "WRITE_SIZE")
     fetch_scale = copy_bytes / (fetch_ref * 1024.0)
     write_scale = copy_bytes / (write_ref * 1024.0)
-    f = _counter(fetch_db)
+    f = _counter(fetch_db, with_counts=True)
     w = _counter(write_db)
     kernels = []
-    for (k, c, g), v in sorted(f.items()):
+    for (k, c, g), (v, n) in sorted(f.items()):
         wv = w.get((k, "WRITE_SIZE", g))
-        kernels.append({"kernel": k, "grid": g, "fetch_kib": round(v, 1),
+        kernels.append({"kernel": k, "grid": g, "dispatches": n, "fetch_kib": round(v, 1),
                         "write_kib": None if wv is None else round(wv, 1),
                         "fetch_bytes": round(v * 1024 * fetch_scale),
                         "write_bytes": None if wv is None else round(wv * 1024 * write_scale)})
@@ -119,12 +123,14 @@ def traffic(workload, fetch_db, write_db, copy_fetch_db, copy_write_db, copy_byt
                 continue
             for r in match:  # every compiled variant the launch matched (one per layer shape)
                 got[e["name"]][r["kernel"]] = r
-    # a name's record is the mean over its launches' rows (the layers of a stack that
-    # run the same kernel family, as bench.py averages their times)
+    # a name's record is the mean over its launches (the layers of a stack that run
+    # the same kernel family, as bench.py averages their times): the rows weighted by
+    # their dispatch counts (layers that run one compiled variant share its row)
     for name, rs in got.items():
         rs = list(rs.values())
-        fb = round(sum(r["fetch_bytes"] for r in rs) / len(rs))
-        wb = round(sum(r["write_bytes"] for r in rs) / len(rs))
+        nd = sum(r["dispatches"] for r in rs)
+        fb = round(sum(r["fetch_bytes"] * r["dispatches"] for r in rs) / nd)
+        wb = round(sum(r["write_bytes"] * r["dispatches"] for r in rs) / nd)
         out[name] = {"fetch_bytes": fb, "write_bytes": wb, "bytes": fb + wb, "variants": len(rs)}
     return {"workload": workload, "source_digest": bench.source_digest(),
             "fetch_scale": rec["fetch_scale"], "write_scale": rec["write_scale"], "kernels": out}
