@@ -694,17 +694,20 @@ bool dwl_layout(const wtconv_desc &d, const PlaneCfg &cfg, int pb, PlaneDwlArgs 
         a.pw[li] = pb == 1 ? ws[l] : a.Pw1 >> (l - 1);
         const int items = a.ns[li] * pb * a.wr[li];
         if (items >= 32768 || 2LL * hs[l] * a.wl[li] >= 32768) return false;
+        // without level-1 items (lfirst = 1) only level 1's low-pass bands are kept:
+        // the level-2 analysis reads nothing else of level 1
+        const int nb = li < lfirst ? 1 : 4;
         a.xs[li] = column_stride(std::max((a.ns[li] - 1) * RHD + 4 * WQ, a.ns[li] * RHD + 2 * R));
         a.xb[li] = a.xs[li] * (a.wl[li] + 2 * R);
         a.xo[li] = (int)fl;
-        fl += 4LL * a.xb[li];
+        fl += (long long)nb * a.xb[li];
         // dy columns: ns RHD >= hl rows (a multiple of 4, so the pad row an odd hl
         // needs for the next level's butterflies is inside), one pad column if wl
         // is odd
         a.gs[li] = column_stride(a.ns[li] * RHD);
         a.gb[li] = a.gs[li] * (a.wl[li] + (a.wl[li] & 1));
         a.go[li] = (int)fl;
-        fl += 4LL * a.gb[li];
+        fl += (long long)nb * a.gb[li];
         a.m_wl[li] = magic31_of(a.wl[li]);
         a.m_row[li] = magic31_of(pb * a.wr[li]);
         a.m_wr[li] = magic31_of(a.wr[li]);
