@@ -14,7 +14,14 @@ stack at batch 128 (forward of layers 1..4, then the backward of layers 4..1).
   only their inputs and outputs) are reported next to it.
 * `ms_per_step`: one forward + backward of the workload's layers; the per-step
   event times also give `ms_per_step_median`, and each pass is timed on its own
-  (`per_pass_ms`).  Launches are eager: the host enqueues the step's kernels
+  (`per_pass_ms`).  Every launch goes to one stream, in order.  With
+  `--two-stream` the layers are scheduled as a chain instead: each layer's weight
+  gradients run on a second stream as soon as its dy is in place (the input
+  gradient of the layer after it), beside the rest of the input-gradient chain.
+  That overlaps only the kernels' tails (every launch fills the GPU), and measured
+  slower than one stream: the kernels raise the priority of workgroups with many
+  passes left, so a kernel that starts on one stream holds back the tail of the
+  one ending on the other.  Launches are eager: the host enqueues the step's kernels
   faster than they run, so the gaps between them are a few microseconds.  With
   `--graph` the step is captured once per buffer set as a HIP graph
   (torch.cuda.graph around the same library calls) and the replays are timed;
@@ -90,7 +97,7 @@ class Layer:
     """Device tensors of one layer: `rotate` sets of (x, dy, y, dx) plus parameters,
     gradient outputs and one workspace, all allocated before timing."""
 
-    def __init__(self, case, rotate, torch, wt):
+    def __init__(self, case, rotate, torch, wt, two_stream=False):
         from synthetic import normal
         self.case = case
         dt = {"bf16": torch.bfloat16, "f16": torch.float16}.get(case.dtype, torch.float32)
@@ -116,6 +123,12 @@ class Layer:
         desc = wt.make_desc(case.n, case.c, case.h, case.w, k, L, DTYPE_CODE[case.dtype])
         nbytes = max(wt.wtconv_workspace_size(desc, op) for op in range(3))
         self.ws = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
+        # the weight-gradient pass's own workspace, for when it runs beside the
+        # input-gradient pass on a second stream
+        self.ws_w = None
+        if two_stream:
+            nbytes = wt.wtconv_workspace_size(desc, wt.OP_BACKWARD_WEIGHT)
+            self.ws_w = torch.empty(max(nbytes, 256), dtype=torch.uint8, device=dev)
 
     def forward(self, i, wt):
         x, _, y, _ = self.sets[i % len(self.sets)]
@@ -127,11 +140,11 @@ class Layer:
         p, L = self.p, self.case.levels
         wt.wtconv_backward_input(dy, p["w0"], p["s0"], p["wl"], p["sl"], L, out=dx, workspace=self.ws)
 
-    def backward_weight(self, i, wt):
+    def backward_weight(self, i, wt, own_workspace=False):
         x, dy, _, _ = self.sets[i % len(self.sets)]
         p, L = self.p, self.case.levels
         wt.wtconv_backward_weight(x, dy, p["w0"], p["b0"], p["s0"], p["wl"], p["sl"], L, out=self.grads,
-                                  workspace=self.ws)
+                                  workspace=self.ws_w if own_workspace else self.ws)
 
     def backward(self, i, wt):
         self.backward_input(i, wt)
@@ -148,18 +161,50 @@ def memory_report(layers, torch):
     step = 0
     for layer in layers:
         step += sum(nb(t) for t in layer.sets[0])
-        step += sum(nb(t) for t in layer.p.values()) + sum(nb(t) for t in layer.grads.values()) + nb(layer.ws)
+        step += sum(nb(t) for t in layer.p.values()) + sum(nb(t) for t in layer.grads.values())
+        step += nb(layer.ws) + nb(layer.ws_w)
     return {"peak_allocated_bytes": int(torch.cuda.max_memory_allocated()),
             "step_footprint_bytes": int(step),
-            "workspace_bytes": int(sum(nb(layer.ws) for layer in layers)),
+            "workspace_bytes": int(sum(nb(layer.ws) + nb(layer.ws_w) for layer in layers)),
             "rotate_buffer_sets": len(layers[0].sets)}
 
 
 def run_step(layers, i, wt):
+    """One step on the current stream: forward of every layer, then the input and
+    weight gradients of each layer, last layer first."""
     for layer in layers:
         layer.forward(i, wt)
     for layer in reversed(layers):
         layer.backward(i, wt)
+
+
+class TwoStreamStep:
+    """One step with the weight gradients on a second stream.  The layers are taken
+    as a chain, as in a network: layer l's dy is the input gradient of layer l + 1,
+    so the weight gradients of layer l wait for that input gradient (the last layer's
+    for the end of the forward pass) and then run beside the rest of the input-
+    gradient chain; the step ends when both streams have finished.  Each layer's
+    weight-gradient pass has a workspace of its own."""
+
+    def __init__(self, layers, torch):
+        self.layers = layers
+        self.torch = torch
+        self.side = torch.cuda.Stream()  # default priority
+        self.events = [torch.cuda.Event() for _ in range(len(layers))]
+
+    def __call__(self, i, wt):
+        torch = self.torch
+        main = torch.cuda.current_stream()
+        for layer in self.layers:
+            layer.forward(i, wt)
+        for j, layer in enumerate(reversed(self.layers)):
+            ready = self.events[j]
+            ready.record(main)  # this layer's dy and x are in place
+            self.side.wait_event(ready)
+            with torch.cuda.stream(self.side):
+                layer.backward_weight(i, wt, own_workspace=True)
+            layer.backward_input(i, wt)
+        main.wait_stream(self.side)
 
 
 def cpu_baseline(cases, budget_s):
@@ -259,6 +304,8 @@ def main():
     ap.add_argument("--warmup", type=int, default=5)
     ap.add_argument("--workload", default="stack", choices=sorted(WORKLOADS))
     ap.add_argument("--rotate", type=int, default=3)
+    ap.add_argument("--two-stream", action="store_true",
+                    help="run each layer's weight gradients on a second stream, beside the input-gradient chain")
     ap.add_argument("--graph", action="store_true",
                     help="time replays of the step captured as a HIP graph instead of eager launches")
     ap.add_argument("--no-cpu-baseline", action="store_true")
@@ -295,7 +342,7 @@ def main():
     allc = baseline_cases()
     cases = [allc[name] for name in WORKLOADS[args.workload]]
     print(f"# bench: {args.workload}: {describe(cases)}", file=sys.stderr, flush=True)
-    layers = [Layer(c, args.rotate, torch, wt) for c in cases]
+    layers = [Layer(c, args.rotate, torch, wt, args.two_stream) for c in cases]
     es = lambda c: 4 if c.dtype == "f32" else 2
 
     def case_launches(c):
@@ -311,9 +358,10 @@ def main():
     model = {p: sum(traffic.model_bytes(c.n, c.c, c.h, c.w, c.levels, es(c))[p] for c in cases)
              for p in PASSES + ("step",)}
 
+    step = TwoStreamStep(layers, torch) if args.two_stream else (lambda i, wt: run_step(layers, i, wt))
     torch.cuda.reset_peak_memory_stats()
     for i in range(args.warmup):
-        run_step(layers, i, wt)
+        step(i, wt)
     torch.cuda.synchronize()
 
     # one HIP graph per rotating buffer set, each holding a whole step (every launch
@@ -323,12 +371,12 @@ def main():
         for r in range(args.rotate):
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g):
-                run_step(layers, r, wt)
+                step(r, wt)
             graphs.append(g)
         for i in range(args.warmup):
             graphs[i % len(graphs)].replay()
         torch.cuda.synchronize()
-    step_fn = (lambda i: graphs[i % len(graphs)].replay()) if graphs else (lambda i: run_step(layers, i, wt))
+    step_fn = (lambda i: graphs[i % len(graphs)].replay()) if graphs else (lambda i: step(i, wt))
 
     # timed region: exactly `steps` steps, synchronised on both sides
     wall_ms, step_ms = timed(step_fn, args.steps, torch)
@@ -339,7 +387,7 @@ def main():
     eager_ms = None
     if graphs:
         # the same steps as eager launches, for comparison
-        ew, es_ms = timed(lambda i: run_step(layers, i, wt), args.steps, torch)
+        ew, es_ms = timed(lambda i: step(i, wt), args.steps, torch)
         eager_ms = max(ew, sum(es_ms)) / args.steps
 
     # each pass on its own (forward of every layer, then input gradients, then weight gradients)
@@ -352,7 +400,8 @@ def main():
         per_pass[name] = {"mean_ms": round(statistics.mean(ms), 5), "median_ms": round(statistics.median(ms), 5),
                           "model_gbs": round(model[name] / (statistics.mean(ms) * 1e-3) / 1e9, 1)}
 
-    # per-kernel durations: the same steps again with the library's event pairs
+    # per-kernel durations: the same steps again with the library's event pairs, on one
+    # stream (each launch's pair then times that launch alone)
     wt.profile_begin()
     for i in range(args.steps):
         run_step(layers, i, wt)
@@ -427,6 +476,7 @@ def main():
         "data": "synthetic",
         "config": {"workload": args.workload, "shapes": describe(cases), "pass": "forward + dx + dW",
                    "rotate_buffer_sets": args.rotate, "launch": "hip_graph" if graphs else "eager",
+                   "streams": 2 if args.two_stream else 1,
                    "model_step_bytes": model["step"],
                    "moved_step_bytes": moved_bytes, "step_flops": step_flops},
         "hbm_frac": round(value / HBM_PEAK_GBS, 4),

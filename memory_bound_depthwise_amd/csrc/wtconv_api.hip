@@ -453,6 +453,17 @@ bool mma_layout(const wtconv_desc &d, int CW, int pb, MmaArgs &a) {
         const long long end = a.offq[li] + (long long)((4 * TY - 1) >> li) * a.sq[li] + (cmax >> li) + 1;
         fl = std::max(fl, (end + 3) & ~3LL);
     }
+    // the B table: in the level-2 pattern region when it fits there (the table is
+    // read before the deep phase writes the patterns), else after everything
+    const int bwords = 4 * (2 * K) * (K == 5 ? 12 : 8);
+    if (L >= 2 && 2LL * hs[2] * a.sq[0] >= bwords) {
+        a.btab = a.offq[0];
+        a.btab_alias = 1;
+    } else {
+        a.btab = (int)fl;
+        a.btab_alias = 0;
+        fl += bwords;
+    }
     a.lds_floats = (int)fl;
     if (fl * 4 > kMmaLdsBudget) return false;
     a.m_gw = magic31_of(a.Gw);

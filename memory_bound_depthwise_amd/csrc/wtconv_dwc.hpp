@@ -263,6 +263,7 @@ __global__ __launch_bounds__(kDwcThreads, 2) void plane_dwc_kernel(PlaneDwcArgs 
     const int aq = mm >> 2, ai = mm & 3;
 
     for (int g = g_begin; g < g_end; ++g) {
+        balance_priority(g_end - g, g_end - g_begin);
         const int n0 = g * PB, live = min(PB, a.n - n0);
         const bool full = live == PB && !(a.H & 1);
         __syncthreads();  // the previous pass is done with the planes

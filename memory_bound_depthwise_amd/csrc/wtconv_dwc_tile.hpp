@@ -162,6 +162,7 @@ __global__ __launch_bounds__(kDwcThreads, 2) void dwc_tile_kernel(DwcTileArgs a)
     const int g4 = lane >> 4, mm = lane & 15, aq = mm >> 2, ai = mm & 3;
 
     for (int p = p_begin; p < p_end; ++p) {
+        balance_priority(p_end - p, p_end - p_begin);
         int nn, r0, c0;
         pass_of(p, nn, r0, c0);
         const size_t cpl = ((size_t)nn * a.C + c) * a.Ho * a.Wo;

@@ -104,6 +104,8 @@ struct MmaArgs {
     int sq[kMaxLevels], offq[kMaxLevels];
     int dend[kMaxLevels];
     int wt;           // weight table (floats)
+    int btab;         // B table (MmaBTab words), 16-byte aligned
+    int btab_alias;   // 1: the B table lies in the level-2 pattern region
     int zero_floats;  // floats cleared at the start (canvas, bands, patterns, weights)
     int tab;          // deep-level geometry table
     int lds_floats;
@@ -174,6 +176,96 @@ __device__ __forceinline__ void mma_b_fragments(const float *smem, int wt, int b
         // one step at a time: the table reads of all steps at once would take more
         // registers than the rest of the kernel
         __builtin_amdgcn_sched_barrier(0);
+    }
+}
+
+// The B entries of a channel as a table shared by the workgroup.  The entry of B
+// column n = (rp, ry, rx) at window pixel (rho, kap) depends on rp and rho only
+// through dy = rho - 2 rp: the level-1 tap is (dy >> 1, kap >> 1) with window-pixel
+// parities (dy & 1, kap & 1), the base tap (dy - ry - R, kap - rx - R).  Entry
+// (2 ry + rx, dy, kap), dy < 2K, holds that value split as hi | lo << 16 (bfloat16
+// halves); window pixels with dy outside [0, 2K) carry no weight.  Rows are FC words
+// (a multiple of 4: the lanes read window columns 0..7 as two 16-byte words, and
+// columns 8, 9 for K = 5).
+template <int K>
+struct MmaBTab {
+    static constexpr int FR = 2 * K;
+    static constexpr int FC = K == 5 ? 12 : 8;
+    static constexpr int kWords = 4 * FR * FC;
+};
+
+template <int K>
+__device__ __forceinline__ void mma_btab_build(const float *smem, int wt, int base, uint32_t *ft, int tid, int NT) {
+    using BT = MmaBTab<K>;
+    constexpr int R = (K - 1) / 2;
+    const float4 *s4 = reinterpret_cast<const float4 *>(smem);
+    for (int e = tid; e < BT::kWords; e += NT) {
+        const int q = e / (BT::FR * BT::FC), r = e - q * (BT::FR * BT::FC);
+        const int dy = r / BT::FC, kap = r - dy * BT::FC;
+        const int ry = q >> 1, rx = q & 1;
+        float w = 0.f;
+        {  // level-1 tap (dy >> 1, kap >> 1), the Haar sign product folded in
+            const int uu = dy >> 1, vv = kap >> 1;
+            const bool ok = vv < K;
+            const float4 wb = s4[(wt >> 2) + (ok ? vv * K + uu : 0)];
+            const int sy = ry ^ (dy & 1), sx = rx ^ (kap & 1);
+            const float t = (wb.x + (sy ? -wb.y : wb.y)) + ((sx ? -wb.z : wb.z) + ((sy ^ sx) ? -wb.w : wb.w));
+            w = ok ? t : 0.f;
+        }
+        {  // base tap of output pixel (ry, rx)
+            const int uu = dy - ry - R, vv = kap - rx - R;
+            const bool ok = uu >= 0 && uu < K && vv >= 0 && vv < K;
+            const float t = smem[base + (ok ? vv * K + uu : 0)];
+            w += ok ? t : 0.f;
+        }
+        const uint32_t h = Act<uint16_t>::one(w);
+        const uint32_t l = Act<uint16_t>::one(w - __uint_as_float(h << 16));
+        ft[e] = h | (l << 16);
+    }
+}
+
+// A lane's B fragments (hi and lo halves) from the B table: lane (g4, mm) holds
+// column mm = 4 rp + 2 rx + ry and, in step s, window row 4 s + g4, columns 0..7;
+// in the tail step (K = 5), columns 8, 9 of window rows g4, g4 + 4, g4 + 8, g4 + 12.
+template <int K>
+__device__ __forceinline__ void mma_b_from_table(const uint32_t *ft, int lane, wtc_bf16x8 (&bh)[MmaGeom<K>::NS],
+                                                 wtc_bf16x8 (&bl)[MmaGeom<K>::NS]) {
+    using G = MmaGeom<K>;
+    using BT = MmaBTab<K>;
+    const int g4 = lane >> 4, mm = lane & 15;
+    const int rp = mm >> 2, ry = mm & 1, rx = (mm >> 1) & 1;
+    const uint32_t *fq = ft + (2 * ry + rx) * (BT::FR * BT::FC);
+    // hi halves of two entries as one bfloat16 pair, and the lo halves
+    auto split = [](uint32_t p0, uint32_t p1, uint32_t &h, uint32_t &l) {
+        h = __builtin_amdgcn_perm(p1, p0, 0x05040100u);
+        l = __builtin_amdgcn_perm(p1, p0, 0x07060302u);
+    };
+#pragma unroll
+    for (int s = 0; s < G::NSF; ++s) {
+        const int dy = 4 * s + g4 - 2 * rp;
+        const bool ok = dy >= 0 && dy < BT::FR;
+        const uint4 *src = reinterpret_cast<const uint4 *>(fq + (ok ? dy : 0) * BT::FC);
+        const uint4 v0 = src[0], v1 = src[1];
+        const uint32_t p[8] = {v0.x, v0.y, v0.z, v0.w, v1.x, v1.y, v1.z, v1.w};
+        union { wtc_bf16x8 v; uint32_t w[4]; } fh, fl;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            split(ok ? p[2 * i] : 0u, ok ? p[2 * i + 1] : 0u, fh.w[i], fl.w[i]);
+        }
+        bh[s] = fh.v;
+        bl[s] = fl.v;
+    }
+    if constexpr (G::TAIL) {
+        union { wtc_bf16x8 v; uint32_t w[4]; } fh, fl;
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int dy = g4 + 4 * i - 2 * rp;
+            const bool ok = dy >= 0 && dy < BT::FR;
+            const uint2 v = *reinterpret_cast<const uint2 *>(fq + (ok ? dy : 0) * BT::FC + 8);
+            split(ok ? v.x : 0u, ok ? v.y : 0u, fh.w[i], fl.w[i]);
+        }
+        bh[G::NSF] = fh.v;
+        bl[G::NSF] = fl.v;
     }
 }
 
@@ -318,9 +410,13 @@ __device__ __forceinline__ void mma_fwd_body(const MmaArgs &args) {
     };
     uint32_t raw[SLOTS][2][IO::kWords];
     float wf0[WSLOTS], wf1[WSLOTS];
+    // The weight table stays in LDS while consecutive units share a channel: its
+    // factors are fetched (and the table rewritten) only for a unit that starts a
+    // channel in this workgroup.
     auto prefetch = [&](const auto &A, int u) {
         int c, n0;
         unit_of(A, u, c, n0);
+        const bool new_c = u == ubeg || c != (u - 1) / A.NG;
         const int live = min(A.PB, A.n - n0);
         const T *xb = static_cast<const T *>(A.x) + ((size_t)n0 * A.C + c) * HW;
         if (kPair && A.L >= 2) {
@@ -330,17 +426,22 @@ __device__ __forceinline__ void mma_fwd_body(const MmaArgs &args) {
 #pragma unroll
             for (int k = 0; k < SLOTS; ++k) load_patch(A, raw[k], xb, live, tid + k * NT);
         }
+        if (new_c) {
 #pragma unroll
-        for (int k = 0; k < WSLOTS; ++k) weight_factors(A, c, min(tid + k * NT, (4 * A.L + 1) * KK), wf0[k], wf1[k]);
+            for (int k = 0; k < WSLOTS; ++k)
+                weight_factors(A, c, min(tid + k * NT, (4 * A.L + 1) * KK), wf0[k], wf1[k]);
+        }
     };
     if (ubeg < uend) prefetch(args, ubeg);
 
-    // B fragments of the current channel (hi and lo halves)
+    // B fragments of the current channel (hi and lo halves); the channel whose weight
+    // table is in LDS
     wtc_bf16x8 bh[G::NS], bl[G::NS];
-    int cur_c = -1;
+    int cur_c = -1, tbl_c = -1;
     const int g4 = lane >> 4, mm = lane & 15;  // lane group (K octet) and A row / D column
 
     for (int u = ubeg; u < uend; ++u) {
+        balance_priority(uend - u, uend - ubeg);
         const __attribute__((address_space(4))) MmaArgs *ap =
             (const __attribute__((address_space(4))) MmaArgs *)__builtin_amdgcn_kernarg_segment_ptr();
         asm volatile("" : "+s"(ap));
@@ -351,18 +452,22 @@ __device__ __forceinline__ void mma_fwd_body(const MmaArgs &args) {
         const int H = a.H, W = a.W, L = a.L, S = opaque(a.S);
         const bool full = live == a.PB && !(H & 1);
         __syncthreads();  // the previous pass is done with every array
-        // 1. commit: the weight table and the raw pixels (canvas rows ROW0 + y)
+        // 1. commit: the weight table (for a new channel) and the raw pixels (canvas
+        //    rows ROW0 + y)
         {
-            const int nw = (4 * L + 1) * KK + 1;
+            if (c != tbl_c) {
+                tbl_c = c;
+                const int nw = (4 * L + 1) * KK + 1;
 #pragma unroll
-            for (int k = 0; k < WSLOTS; ++k) {
-                const int e = tid + k * NT;
-                if (e < nw) smem[weight_slot(a, e)] = fold_weight(a, e, wf0[k], wf1[k]);
-            }
-            for (int e = tid + WSLOTS * NT; e < nw; e += NT) {
-                float f0, f1;
-                weight_factors(a, c, e, f0, f1);
-                smem[weight_slot(a, e)] = fold_weight(a, e, f0, f1);
+                for (int k = 0; k < WSLOTS; ++k) {
+                    const int e = tid + k * NT;
+                    if (e < nw) smem[weight_slot(a, e)] = fold_weight(a, e, wf0[k], wf1[k]);
+                }
+                for (int e = tid + WSLOTS * NT; e < nw; e += NT) {
+                    float f0, f1;
+                    weight_factors(a, c, e, f0, f1);
+                    smem[weight_slot(a, e)] = fold_weight(a, e, f0, f1);
+                }
             }
             const int pw1 = opaque(a.Pw1);
             auto put = [&](const uint32_t (&r)[2][IO::kWords], int p, int i, int m) {
@@ -447,6 +552,20 @@ __device__ __forceinline__ void mma_fwd_body(const MmaArgs &args) {
         // and nothing in it waits for vector-memory loads.
         if (u + 1 < uend) prefetch(a, u + 1);
 
+        // B fragments of a new channel (the condition is uniform over the workgroup):
+        // the workgroup builds the B table, each lane reads its fragments.  Where the
+        // table lies in the level-2 pattern region, the reads finish before the deep
+        // phase writes the patterns.
+        if (c != cur_c) {
+            cur_c = c;
+            uint32_t *ft = reinterpret_cast<uint32_t *>(smem + opaque(a.btab));
+            const int wt = opaque(a.wt);
+            mma_btab_build<K>(smem, wt, wt + 4 * L * KK, ft, tid, NT);
+            __syncthreads();
+            mma_b_from_table<K>(ft, lane, bh, bl);
+            if (a.btab_alias) __syncthreads();
+        }
+
         {
             // 2. level 2 from the pixels (a level-2 cell is a 4 x 4 pixel block: the
             //    butterflies of the low-pass sums of its four level-1 cells; formed at
@@ -476,13 +595,6 @@ __device__ __forceinline__ void mma_fwd_body(const MmaArgs &args) {
                 haar_levels<K>(a, s4, 3, tid, NT);
                 deep_patterns<K>(a, s4, smem, tab, tid, NT);
             }
-        }
-
-        // B fragments, when the channel changes (wave-uniform)
-        if (c != cur_c) {
-            cur_c = c;
-            const int wt = opaque(a.wt);
-            mma_b_fragments<K>(smem, wt, wt + 4 * L * KK, lane, bh, bl);
         }
 
         // 4. products and stores, one tile of 16 x 4 cells at a time.  The product is
@@ -529,7 +641,7 @@ __device__ __forceinline__ void mma_fwd_body(const MmaArgs &args) {
                 const int crow = 4 * ty[h] + g4, ccol = tstep * tx[h] + lcol;
                 // bias and the deep patterns (they enter all four pixels of the cell)
                 float v = bias;
-                {
+                if (L >= 2) {
                     float q[3];
 #pragma unroll
                     for (int j = 0; j < 3; ++j)
@@ -564,7 +676,7 @@ __device__ __forceinline__ void mma_fwd_body(const MmaArgs &args) {
 }
 
 template <int K, int CW>
-__global__ __launch_bounds__(kMmaThreads, 2) void mma_fwd_kernel(MmaArgs a) {
+__global__ __launch_bounds__(kMmaThreads, 3) void mma_fwd_kernel(MmaArgs a) {
     mma_fwd_body<K, CW>(a);
 }
 

@@ -149,6 +149,7 @@ __global__ __launch_bounds__(kTileThreads, 3) void mma_tile_kernel(MmaTileArgs a
     int cur_c = -1;
 
     for (int u = ubeg; u < uend; ++u) {
+        balance_priority(uend - u, uend - ubeg);
         const __attribute__((address_space(4))) MmaTileArgs *ap =
             (const __attribute__((address_space(4))) MmaTileArgs *)__builtin_amdgcn_kernarg_segment_ptr();
         asm volatile("" : "+s"(ap));

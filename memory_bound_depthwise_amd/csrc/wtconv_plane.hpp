@@ -194,6 +194,26 @@ __device__ __forceinline__ int xcd_block(int w, int G) {
     return (x < r ? x * (q + 1) : r * (q + 1) + (x - r) * q) + (w >> 3);
 }
 
+// Wave priority of a workgroup that walks a fixed range of passes, from the passes
+// it has left (rem of total; wave-uniform).  The instruction arbiter favours older
+// waves, so of the workgroups that share a compute unit the last dispatched fall
+// behind and finish last, with equal work.  Lowering the priority of workgroups as
+// they near the end of their range lets the others catch up, and the launch ends
+// sooner (measured with per-workgroup timestamps: the finish times of the six
+// workgroups of a compute unit moved from 61..79 us to 66..75 us).
+__device__ __forceinline__ void balance_priority(int rem, int total) {
+    const int p = total >= 8 ? rem >> 1 : rem - 1;
+    if (p >= 3) {
+        __builtin_amdgcn_s_setprio(3);
+    } else if (p == 2) {
+        __builtin_amdgcn_s_setprio(2);
+    } else if (p == 1) {
+        __builtin_amdgcn_s_setprio(1);
+    } else {
+        __builtin_amdgcn_s_setprio(0);
+    }
+}
+
 // Wave-uniform value made opaque to the optimizer: what is computed from it is
 // computed after this point, inside the current phase, instead of being held in
 // scalar registers from the top of the kernel.
@@ -406,7 +426,9 @@ __device__ __forceinline__ void plane_fwd_body(const PlaneArgs &args) {
     const int wb = blockIdx.x;
     if (wb < a0.U) prefetch(args, wb);
 
+    const int own = wb < a0.U ? (a0.U - 1 - wb) / (int)gridDim.x + 1 : 0;
     for (int u = wb; u < a0.U; u += gridDim.x) {
+        balance_priority(own - (u - wb) / (int)gridDim.x, own);
         // Every argument below is read through a pointer made opaque per pass, so
         // that nothing derived from the arguments is held in registers across passes.
         // (The argument block is the kernel's only argument: offset 0 of its segment.)

@@ -120,6 +120,7 @@ __global__ __launch_bounds__(kDwbThreads, 2) void plane_dwb_kernel(PlaneDwbArgs 
     if (g_begin < g_end) prefetch(g_begin);
 
     for (int g = g_begin; g < g_end; ++g) {
+        balance_priority(g_end - g, g_end - g_begin);
         const int n0 = g * PB, live = min(PB, a.n - n0);
         const bool full = live == PB && !(a.H & 1);  // nothing of the pass's patches needs masking
         __syncthreads();  // the previous pass is done with the cells
@@ -353,6 +354,7 @@ __device__ __forceinline__ void plane_dwl_body(const PlaneDwlArgs &a) {
     if (g_begin < g_end) prefetch(g_begin);
 
     for (int g = g_begin; g < g_end; ++g) {
+        balance_priority(g_end - g, g_end - g_begin);
         const int n0 = g * PB, live = min(PB, a.n - n0);
         const bool full = live == PB && !(a.H & 1);  // nothing of the pass's patches needs masking
         __syncthreads();  // the previous pass is done with the bands
