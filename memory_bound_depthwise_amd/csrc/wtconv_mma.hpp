@@ -272,15 +272,17 @@ __device__ __forceinline__ void mma_b_from_table(const uint32_t *ft, int lane, w
 // The transposed products of two tiles (their MFMA chains and LDS reads are
 // independent, which hides the latency of each): wp[h] points at the canvas dword
 // of window row g4, cell column mm of tile h (S: canvas row stride in dwords).
-// acc[h] receives the four pixels of cell (g4, mm) of tile h, i = 2 rx + ry.
+// acc[h] receives the four pixels of cell (g4, mm) of tile h, i = 2 rx + ry, added
+// to v[h] (the value every pixel of the cell starts from).
 template <int K>
 __device__ __forceinline__ void mma_products2(const uint32_t *wp0, const uint32_t *wp1, int S,
                                               const wtc_bf16x8 (&bh)[MmaGeom<K>::NS],
-                                              const wtc_bf16x8 (&bl)[MmaGeom<K>::NS], wtc_f32x4 (&acc)[2]) {
+                                              const wtc_bf16x8 (&bl)[MmaGeom<K>::NS], const float (&v)[2],
+                                              wtc_f32x4 (&acc)[2]) {
     using G = MmaGeom<K>;
     const uint32_t *wp[2] = {wp0, wp1};
-    acc[0] = wtc_f32x4{0.f, 0.f, 0.f, 0.f};
-    acc[1] = acc[0];
+    acc[0] = wtc_f32x4{v[0], v[0], v[0], v[0]};
+    acc[1] = wtc_f32x4{v[1], v[1], v[1], v[1]};
 #pragma unroll
     for (int s = 0; s < G::NSF; ++s) {
         union { wtc_bf16x8 v; uint32_t w[4]; } A[2];
@@ -632,29 +634,35 @@ __device__ __forceinline__ void mma_fwd_body(const MmaArgs &args) {
             tx[0] = t - ty[0] * a.TX;
             ty[1] = udiv16(t2, a.m_tx);
             tx[1] = t2 - ty[1] * a.TX;
-            wtc_f32x4 acc[2];
-            mma_products2<K>(cv + la + (8 * ty[0]) * S + tstep * tx[0], cv + la + (8 * ty[1]) * S + tstep * tx[1], S, bh,
-                             bl, acc);
+            // bias and the deep patterns (they enter all four pixels of the cell): the
+            // products accumulate onto them
+            float v[2];
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
-                if (h == 1 && t2 == t) break;
                 const int crow = 4 * ty[h] + g4, ccol = tstep * tx[h] + lcol;
-                // bias and the deep patterns (they enter all four pixels of the cell)
-                float v = bias;
+                v[h] = bias;
                 if (L >= 2) {
                     float q[3];
 #pragma unroll
                     for (int j = 0; j < 3; ++j)
                         q[j] = smem[qo[j] + ((4 * ty[h]) >> j) * qs[j] + ((tstep * tx[h]) >> j) + ql[j]];
-                    v += q[0] + (q[1] + q[2]);
+                    v[h] += q[0] + (q[1] + q[2]);
                     for (int k = 3; k < L - 1; ++k)  // levels 5..L
-                        v += smem[qo[k] + (crow >> k) * qs[k] + (ccol >> k)];
+                        v[h] += smem[qo[k] + (crow >> k) * qs[k] + (ccol >> k)];
                 }
+            }
+            wtc_f32x4 acc[2];
+            mma_products2<K>(cv + la + (8 * ty[0]) * S + tstep * tx[0], cv + la + (8 * ty[1]) * S + tstep * tx[1], S, bh,
+                             bl, v, acc);
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                if (h == 1 && t2 == t) break;
+                const int crow = 4 * ty[h] + g4, ccol = tstep * tx[h] + lcol;
                 const int p = udiv16(ccol, a.m_pw1);
                 const int jc = ccol - p * pw1;
                 const int pr = 2 * crow;
                 if (p < live && jc < W1 && pr < H) {
-                    const float o0 = acc[h][0] + v, o1 = acc[h][1] + v, o2 = acc[h][2] + v, o3 = acc[h][3] + v;
+                    const float o0 = acc[h][0], o1 = acc[h][1], o2 = acc[h][2], o3 = acc[h][3];
                     T *dst = yb + (p * CHW + pr * W + 2 * jc);
                     const bool row1 = pr + 1 < H;
                     if (smode != 0) {  // pixel pairs (W even)

@@ -233,18 +233,24 @@ __global__ __launch_bounds__(kTileThreads, 3) void mma_tile_kernel(MmaTileArgs a
             tx[0] = t - ty[0] * ntx;
             ty[1] = udiv16(t2, a.m_tx);
             tx[1] = t2 - ty[1] * ntx;
+            // bias and the deep patterns of the cell, from the staged block of D: the
+            // products accumulate onto them
+            float v[2];
+#pragma unroll
+            for (int h = 0; h < 2; ++h) {
+                const int lr = 4 * ty[h] + g4, lc = 16 * tx[h] + mm;
+                v[h] = bias + (deep ? Act<T>::lo(qs16[2 * a.qbase + lr * a.UC + lc]) : 0.f);
+            }
             wtc_f32x4 acc[2];
             mma_products2<K>(cv + la + (8 * ty[0]) * S + 16 * tx[0], cv + la + (8 * ty[1]) * S + 16 * tx[1], S, bh, bl,
-                             acc);
+                             v, acc);
 #pragma unroll
             for (int h = 0; h < 2; ++h) {
                 if (h == 1 && t2 == t) break;
-                // bias and the deep patterns of the cell, from the staged block of D
                 const int lr = 4 * ty[h] + g4, lc = 16 * tx[h] + mm;
-                const float v = bias + (deep ? Act<T>::lo(qs16[2 * a.qbase + lr * a.UC + lc]) : 0.f);
                 const int pr = 2 * (cr0 + lr), pc = 2 * (cc0 + lc);
                 if (pr < H && pc < W) {
-                    const float o0 = acc[h][0] + v, o1 = acc[h][1] + v, o2 = acc[h][2] + v, o3 = acc[h][3] + v;
+                    const float o0 = acc[h][0], o1 = acc[h][1], o2 = acc[h][2], o3 = acc[h][3];
                     T *dst = yp + ((size_t)pr * W + pc);
                     const bool row1 = pr + 1 < H;
                     if (pairs) {
