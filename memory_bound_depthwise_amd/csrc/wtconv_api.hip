@@ -664,6 +664,103 @@ int column_stride(int lo) {
     return s;
 }
 
+// Trips of the busiest wavefront of a lane table (the most items a lane runs: the
+// item phase of a pass ends with it).
+int dwl_wave_trips(const PlaneDwlArgs &a) {
+    int total = 0;
+    for (int w = 0; w < kDwlThreads / kWave; ++w) {
+        int worst = 0;
+        for (int t = w * kWave; t < (w + 1) * kWave; ++t) {
+            const uint32_t in = a.lane[t];
+            const int M = (in >> 16) & 255, l = (int)(in & 15) - 1;
+            if (M) worst = std::max(worst, cdiv(a.ns[l] * a.PB * a.wr[l], M));
+        }
+        total = std::max(total, worst);
+    }
+    return total;
+}
+
+// Lanes per band of each level lfirst .. L - 1 (0-based) with items: M[l] lanes run
+// ceil(items / M[l]) trips each.  For three levels or fewer the trips of each level
+// are searched from the fewest its lanes allow (at most 64 lanes a band) to seven
+// more, for the table (levels with more trips first) whose busiest wavefront has the
+// fewest trips (a pass ends at a barrier), then the fewest wavefront trips in all
+// (the issue work), then the fewest lane trips; with more levels, greedily (the
+// largest item count of a lane made smallest).
+bool dwl_lanes(const PlaneDwlArgs &a, int lfirst, int (&M)[kMaxLevels]) {
+    const int L = a.L, nl = L - lfirst;
+    constexpr int NWv = kDwlThreads / kWave;
+    int items[kMaxLevels];
+    for (int l = 0; l < L; ++l) {
+        M[l] = 0;
+        items[l] = l < lfirst ? 0 : a.ns[l] * a.PB * a.wr[l];
+    }
+    if (nl <= 0) return true;
+    if (nl <= 3) {
+        long long best = -1;
+        int bestM[3] = {0, 0, 0}, t0[3] = {1, 1, 1}, span[3] = {1, 1, 1};
+        for (int k = 0; k < nl; ++k) {
+            t0[k] = std::max(1, cdiv(items[lfirst + k], kDwlThreads / 4));
+            span[k] = 8;
+        }
+        int T[3];
+        for (T[0] = t0[0]; T[0] < t0[0] + span[0]; ++T[0])
+            for (T[1] = t0[1]; T[1] < t0[1] + span[1]; ++T[1])
+                for (T[2] = t0[2]; T[2] < t0[2] + span[2]; ++T[2]) {
+                    int m[3] = {0, 0, 0}, tr[3] = {0, 0, 0}, lanes = 0;
+                    bool ok = true;
+                    for (int k = 0; k < nl; ++k) {
+                        m[k] = cdiv(items[lfirst + k], T[k]);
+                        tr[k] = cdiv(items[lfirst + k], m[k]);
+                        ok = ok && m[k] <= 255 && tr[k] == T[k];
+                        lanes += 4 * m[k];
+                    }
+                    if (!ok || lanes > kDwlThreads) continue;
+                    // groups by trips, most first: a wavefront's most trips is that of
+                    // the group holding its first lane
+                    int idx[3] = {0, 1, 2};
+                    std::stable_sort(idx, idx + nl, [&](int x, int y) { return tr[x] > tr[y]; });
+                    long long waves = 0, sum = 0, most = 0;
+                    for (int w = 0; w < NWv; ++w) {
+                        int first = w * kWave, c = 0;
+                        for (int k = 0; k < nl; ++k) {
+                            c += 4 * m[idx[k]];
+                            if (first < c) {
+                                waves += tr[idx[k]];
+                                most = std::max<long long>(most, tr[idx[k]]);
+                                break;
+                            }
+                        }
+                    }
+                    for (int k = 0; k < nl; ++k) sum += 4LL * m[k] * tr[k];
+                    const long long cst = (most * 1000 + waves) * 1000000 + sum;
+                    if (best < 0 || cst < best) {
+                        best = cst;
+                        for (int k = 0; k < nl; ++k) bestM[k] = m[k];
+                    }
+                }
+        if (best < 0) return false;
+        for (int k = 0; k < nl; ++k) M[lfirst + k] = bestM[k];
+        return true;
+    }
+    for (int l = lfirst; l < L; ++l) M[l] = 1;
+    int used = 4 * nl;
+    while (used + 4 <= kDwlThreads) {
+        int worst = -1, wl_items = 0;
+        for (int l = lfirst; l < L; ++l) {
+            const int per = cdiv(items[l], M[l]);
+            if (M[l] < std::min(items[l], 255) && per > wl_items) {
+                wl_items = per;
+                worst = l;
+            }
+        }
+        if (worst < 0) break;
+        ++M[worst];
+        used += 4;
+    }
+    return true;
+}
+
 bool dwl_layout(const wtconv_desc &d, const PlaneCfg &cfg, int pb, PlaneDwlArgs &a, int lfirst) {
     const int K = d.k, KK = K * K, R = (K - 1) / 2, L = d.levels, RHD = cfg.RH, CW = cfg.CW;
     a = PlaneDwlArgs{};
@@ -728,27 +825,19 @@ bool dwl_layout(const wtconv_desc &d, const PlaneCfg &cfg, int pb, PlaneDwlArgs 
     fl = std::max<long long>(fl, (long long)kDwlThreads * (TC + 1));
     a.lds_floats = (int)((fl + 3) & ~3LL);
     if ((long long)a.lds_floats * 4 > kDwlLdsBudget) return false;
-    // lanes per (level, band) of levels lfirst + 1 .. L: greedy, to minimise the
-    // largest item count of a lane
+    // lanes per (level, band) of levels lfirst + 1 .. L
     int M[kMaxLevels];
-    for (int l = 0; l < L; ++l) M[l] = l < lfirst ? 0 : 1;
     if (4 * (L - lfirst) > kDwlThreads) return false;
-    int used = 4 * (L - lfirst);
-    while (used + 4 <= kDwlThreads) {
-        int worst = -1, wl_items = 0;
-        for (int l = lfirst; l < L; ++l) {
-            const int items = a.ns[l] * a.PB * a.wr[l], per = cdiv(items, M[l]);
-            if (M[l] < std::min(items, 255) && per > wl_items) {
-                wl_items = per;
-                worst = l;
-            }
-        }
-        if (worst < 0) break;
-        ++M[worst];
-        used += 4;
-    }
+    if (!dwl_lanes(a, lfirst, M)) return false;
+    // the table: levels by trips per lane, most first, so that the lanes with the
+    // most trips share wavefronts; each level's lanes band by band
+    int order[kMaxLevels], no = 0;
+    for (int l = lfirst; l < L; ++l) order[no++] = l;
+    auto trips = [&](int l) { return cdiv(a.ns[l] * a.PB * a.wr[l], M[l]); };
+    std::stable_sort(order, order + no, [&](int x, int y) { return trips(x) > trips(y); });
     int t = 0;
-    for (int l = lfirst; l < L; ++l) {
+    for (int k = 0; k < no; ++k) {
+        const int l = order[k];
         a.lane0[l] = t;
         a.lanes[l] = M[l];
         for (int b = 0; b < 4; ++b)
@@ -761,17 +850,6 @@ bool dwl_layout(const wtconv_desc &d, const PlaneCfg &cfg, int pb, PlaneDwlArgs 
     a.m_gw = magic31_of(a.Gw);
     a.m_h1 = magic31_of(a.H1);
     return true;
-}
-
-// Largest item count of a lane (the pass time) for a layout.
-int dwl_lane_items(const PlaneDwlArgs &a) {
-    int worst = 0;
-    for (int t = 0; t < kDwlThreads; ++t) {
-        const uint32_t in = a.lane[t];
-        const int M = (in >> 16) & 255, l = (int)(in & 15) - 1;
-        if (M) worst = std::max(worst, cdiv(a.ns[l] * a.PB * a.wr[l], M));
-    }
-    return worst;
 }
 
 // lfirst = 1: levels 2..L only (level 1 runs in the correlation kernel)
@@ -788,9 +866,9 @@ bool plan_dwl(const wtconv_desc &d, PlaneDwlArgs &a, PlaneCfg &cfg, int lfirst) 
             if (pb == 1) return false;
             break;
         }
-        // wave-instructions per pass: a lane's items of RHD K^2 FMAs + 30 others;
-        // commit and Haar ~60 per item; ~300 fixed
-        const double cost = (2.0 * dwl_lane_items(t) * (cfg.RH * d.k * d.k + 30.0) +
+        // wave-instructions per pass: the item trips of the busiest wavefront, of
+        // RHD K^2 FMAs + 30 others each; commit and Haar ~60 per item; ~300 fixed
+        const double cost = (2.0 * dwl_wave_trips(t) * (cfg.RH * d.k * d.k + 30.0) +
                              cdiv(t.commit_items, kDwlThreads) * 120.0 + 300.0) / pb;
         if (cost < best - 1e-9) {
             best = cost;

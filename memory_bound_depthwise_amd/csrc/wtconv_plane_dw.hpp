@@ -337,7 +337,10 @@ __device__ __forceinline__ void plane_dwl_body(const PlaneDwlArgs &a) {
         }
     };
 
-    const uint32_t info = a.lane[tid];
+    // the lane table, rotated by whole wavefronts per workgroup (so that the
+    // wavefronts with the most items fall on different SIMDs); entry pos is this lane's
+    const int pos = (tid + kWave * (int)(blockIdx.x & (NT / kWave - 1))) & (NT - 1);
+    const uint32_t info = a.lane[pos];
     const int lv = info & 15, band = (info >> 4) & 3, gm = (info >> 8) & 255, gM = (info >> 16) & 255;
     // the lane's item geometry, fixed for the kernel (the level differs between
     // lanes of a wavefront, so it is looked up once, not per item)
@@ -464,7 +467,7 @@ __device__ __forceinline__ void plane_dwl_body(const PlaneDwlArgs &a) {
         __syncthreads();
 #pragma unroll
         for (int t = 0; t < TC; ++t)
-            if (t0 + t < KK) smem[tid * (TC + 1) + t] = acc[t0 + t];
+            if (t0 + t < KK) smem[pos * (TC + 1) + t] = acc[t0 + t];
         __syncthreads();
         const int nt = min(TC, KK - t0);
         for (int q = tid; q < a.groups * nt; q += NT) {
