@@ -1039,9 +1039,12 @@ bool plan_dwc_tile(const wtconv_desc &d, DwcTileArgs &a, bool lev) {
     const long long P = (long long)d.n * a.TYu * a.TXu;
     if (P >= (1LL << 31)) return false;
     a.P = (int)P;
-    a.XR = a.UR + 4 * NF - 1;
-    // x cells the B reads reach: up to XL + 32 + T0 + 4 NF (XL = 4), and the fifth dword
-    a.XC = cdiv(4 + kDwcTileCols + T0 + 4 * NF + 2, 4);
+    // x canvas rows and 4-cell chunks that the used offsets T0..T1 reach (the
+    // products of a family's offsets past T1 land in accumulators nothing reads, so
+    // what their lanes read there does not matter): rows T0 .. UR - 1 + T1, and the
+    // cells of a lane's five-dword B read at XL + 24 + T1 (XL = 4)
+    a.XR = a.UR + T1 - T0;
+    a.XC = cdiv(2 * ((kDwcTileCols - 4 + T1) >> 1) + 10, 4);
     if (a.XR * a.XC > kDwcTileXSlots * kDwcThreads || a.UR * kDwcTileCols / 4 > kDwcTileDySlots * kDwcThreads)
         return false;
     // bank spread as in the plane-resident layout: row stride 16 mod 64 dwords and
