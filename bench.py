@@ -300,8 +300,8 @@ def timed(fn, steps, torch):
 def main():
     ap = argparse.ArgumentParser(description=__doc__)
     ap.add_argument("--gpus", type=int, default=1)
-    ap.add_argument("--steps", type=int, default=20)
-    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=20)
     ap.add_argument("--workload", default="stack", choices=sorted(WORKLOADS))
     ap.add_argument("--rotate", type=int, default=3)
     ap.add_argument("--two-stream", action="store_true",
