@@ -1083,6 +1083,13 @@ DwPlan build_backward_weight_plan(const wtconv_desc &d) {
     }
     p.dwl = p.dwc_lev ? d.levels >= 2 : plan_dwl(d, p.la, p.lcfg, 0);
     p.dtile = !p.dwc && !p.dwl && plan_dwc_tile(d, p.ta, d.levels >= 1);
+    for (int l = 2; l <= d.levels; ++l) {
+        wtconv_desc dl = d;
+        dl.h = p.ld.H[l - 1];
+        dl.w = p.ld.W[l - 1];
+        dl.levels = l < d.levels ? 2 : 1;  // 2: it also writes the carriers for level l + 1
+        p.dtl[l - 1] = p.dtile && plan_dwc_tile(dl, p.tal[l - 1], true);
+    }
     const size_t es = elem_size(d.dtype), planes = (size_t)d.n * d.c;
     size_t off = 0;
     if (!p.dwl && !p.dwc_lev) {
@@ -1115,12 +1122,19 @@ DwPlan build_backward_weight_plan(const wtconv_desc &d) {
             p.G[l] = p.ca.k;
         else if (p.dtile && l == 1)
             p.G[l] = p.ta.k;
+        else if (p.dtl[l - 1])
+            p.G[l] = p.tal[l - 1].k;
         else if (p.dwl)
             p.G[l] = p.la.k;
         else
             p.G[l] = (d.n > 0 && d.h > 0 && d.w > 0) ? p.lvl[l - 1].nblk * p.lvl[l - 1].tiles : 0;
         floats += (long long)d.c * p.G[l] * 4 * KK;
     }
+    p.trash = floats;
+    long long trash_rows = 0;
+    for (int l = 2; l <= d.levels; ++l)
+        if (p.dtl[l - 1]) trash_rows = std::max<long long>(trash_rows, p.tal[l - 1].k);
+    floats += (long long)d.c * trash_rows * (KK + 1);
     p.bytes = align_up(off + (size_t)floats * sizeof(float));
     return p;
 }
@@ -1439,8 +1453,14 @@ WTCONV_API int wtconv_plan_launches(const wtconv_desc *desc, int op, wtconv_laun
                 add("plane_dwl", 0, (long long)d.c * p.la.k, kDwlThreads, (size_t)p.la.lds_floats * sizeof(float),
                     16 * p.lcfg.CW + p.lcfg.RH);
             } else {
-                for (int l = p.dtile ? 2 : 1; l <= d.levels; ++l)
-                    add("dw_level", l, grid_of(p.lvl[l - 1], d.c), kThreads, lds_bytes(Kind::DwLevel, d.k, p.lvl[l - 1]));
+                for (int l = p.dtile ? 2 : 1; l <= d.levels; ++l) {
+                    if (p.dtl[l - 1])
+                        add("dwc_tile", l, (long long)d.c * p.tal[l - 1].k, kDwcThreads,
+                            (size_t)p.tal[l - 1].lds_floats * sizeof(float), 16);
+                    else
+                        add("dw_level", l, grid_of(p.lvl[l - 1], d.c), kThreads,
+                            lds_bytes(Kind::DwLevel, d.k, p.lvl[l - 1]));
+                }
             }
             if (p.dwc || p.dtile) {
                 // the base ran in the correlation kernel

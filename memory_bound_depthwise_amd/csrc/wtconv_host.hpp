@@ -109,6 +109,13 @@ struct DwPlan {
     DwcTileArgs ta;      // past the plane-resident range), levels 2..L by the per-level kernels
     bool dwl;            // levels by the plane-resident kernel
     PlaneDwlArgs la;
+    // with dtile, level l >= 2 (index l - 1) by the tiled correlation kernel too, on the
+    // level-(l - 1) carriers: their level-1 bands are level l's, and its level-1 raw
+    // sums are level l's (the carrier's 1/2 and the 4^-l cancel); its base sums go
+    // to a region nothing reads
+    bool dtl[kMaxLevels];
+    DwcTileArgs tal[kMaxLevels];
+    long long trash;     // float offset of that region within the partials
     PlaneCfg lcfg;
     LevelDims ld;
     size_t xc_off[kMaxLevels], gc_off[kMaxLevels];  // carriers of the per-level kernels

@@ -449,6 +449,30 @@ int run_dwc_tile(const PlanSet &ps, const void *x, const void *dy, float *partia
     }
 }
 
+// Level l >= 2 by the tiled correlation kernel on the level-(l - 1) carriers of x and
+// dy (their level-1 raw sums are level l's); it writes the level-l carriers for the
+// next level, and its base sums to a region nothing reads.
+template <int K, typename T>
+int run_dwc_tile_level(const PlanSet &ps, int l, float *partial, char *ws, hipStream_t st) {
+    if constexpr (!std::is_same<T, uint16_t>::value) {
+        return WTCONV_ERR_DTYPE;  // not planned: bfloat16 only
+    } else {
+        const wtconv_desc &d = ps.d;
+        const DwPlan &p = ps.dp;
+        DwcTileArgs a = p.tal[l - 1];
+        a.x = ws + p.xc_off[l - 2];
+        a.dy = ws + p.gc_off[l - 2];
+        a.pbase = partial + p.trash;
+        a.plev = partial + p.region[l];
+        a.xc = l < d.levels ? (void *)(ws + p.xc_off[l - 1]) : nullptr;
+        a.gc = l < d.levels ? (void *)(ws + p.gc_off[l - 1]) : nullptr;
+        a.vec = a.W % 8 == 0 && aligned(a.x, 16) && aligned(a.dy, 16) ? 1 : 0;
+        const dim3 grid((unsigned)((long long)d.c * a.k));
+        const size_t shm = (size_t)a.lds_floats * sizeof(float);
+        return launch("dwc_tile", K, dtype_of<T>(), l, dwc_tile_kernel<K, true>, grid, dim3(kDwcThreads), shm, st, a);
+    }
+}
+
 template <int K, typename T>
 int run_backward_weight(const PlanSet &ps, const void *x, const void *dy, const float *w0, const float *b0,
                         const float *s0, const float *wl, const float *sl, float *dw0, float *db0, float *ds0,
@@ -477,6 +501,11 @@ int run_backward_weight(const PlanSet &ps, const void *x, const void *dy, const 
             if (rc) return rc;
         }
         for (int l = p.dtile ? 2 : 1; l <= L && !p.dwl; ++l) {
+            if (p.dtl[l - 1]) {
+                int rc = run_dwc_tile_level<K, T>(ps, l, partial, ws, st);
+                if (rc) return rc;
+                continue;
+            }
             DwLevelArgs a{};
             a.xin = l == 1 ? x : (const void *)(ws + p.xc_off[l - 2]);
             a.gin = l == 1 ? dy : (const void *)(ws + p.gc_off[l - 2]);

@@ -90,6 +90,10 @@ def kernel_cost(family, level, n, c, h, w, k, levels, elem_bytes):
         l = level
         elems = blocks[l - 1] + 4 * blocks[l] + (4 * blocks[l + 1] if l < levels else 0)
         return E * elems, 2 * 4 * blocks[l] * kk
+    if family == "dwc_tile" and level >= 2:  # level l from the level-(l - 1) carriers
+        l = level
+        elems = 2 * blocks[l - 1] + (2 * blocks[l] if l < levels else 0)
+        return E * elems, 2 * 4 * blocks[l] * kk
     if family == "dwc_tile":
         return E * (2 * N + (2 * blocks[1] if levels >= 2 else 0)), \
             2 * N * kk + (2 * 4 * blocks[1] * kk if levels >= 1 else 0)

@@ -64,12 +64,15 @@ def path_of(case):
     import memory_bound_depthwise_amd as wt
     names = plan_names(case)
     fwd = "plane" if any(n.startswith(("plane_fwd", "mma_fwd")) for n in names[wt.OP_FORWARD]) else "level"
-    # weight gradients: the per-level kernels (dw_level, dw_base) pass carriers
-    # through the workspace; the plane-resident ones (plane_dwb, plane_dwl, and for
-    # bfloat16 the correlation kernel plane_dwc, whose products of bfloat16 values are
-    # exact, beside plane_dwd for levels 2..L) keep everything in float32
+    # weight gradients: the per-level kernels (dw_level, dw_base, and the tiled
+    # correlation kernel of a level l >= 2, 'dwc_tile...#l', which reads the level-(l-1)
+    # carriers) pass carriers through the workspace; the plane-resident ones
+    # (plane_dwb, plane_dwl, and for bfloat16 the correlation kernel plane_dwc, whose
+    # products of bfloat16 values are exact, beside plane_dwd for levels 2..L) keep
+    # everything in float32
     dw = names[wt.OP_BACKWARD_WEIGHT]
-    dwp = "level" if any(n.startswith(("dw_level", "dw_base")) for n in dw) else "plane"
+    dwp = "level" if any(n.startswith(("dw_level", "dw_base")) or (n.startswith("dwc_tile") and "#" in n)
+                         for n in dw) else "plane"
     return fwd, dwp
 
 
