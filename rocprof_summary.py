@@ -79,6 +79,32 @@ def _family(short: str) -> str:
     return short.split("<")[0].split("::")[-1].removesuffix("_kernel")
 
 
+# launch names whose kernel symbol has another family name (the level pass that also
+# adds the deeper levels' patterns runs the level kernel)
+_SYMBOL_FAMILY = {"level_acc": "level_fwd"}
+
+
+def _sequence(db: str, counter: str, fam: str, grid):
+    """The readings of one counter for the dispatches of one kernel family (of one
+    grid size, unless grid is None), in dispatch order."""
+    cur = sqlite3.connect(db).cursor()
+    rows = cur.execute("select kernel_name, grid_size, value from counters_collection "
+                       "where counter_name = ? order by dispatch_id", (counter,)).fetchall()
+    return [v for k, g, v in rows if _family(_short(k)) == fam and (grid is None or g == grid)]
+
+
+def _by_order(seq, cycle):
+    """Mean reading per launch name when several planned launches share one kernel
+    family and grid: a layer runs its launches in plan order every time, so the j-th
+    dispatch belongs to cycle[j % len(cycle)].  None when the count does not fit."""
+    if not seq or len(seq) % len(cycle):
+        return None
+    acc = collections.defaultdict(list)
+    for j, v in enumerate(seq):
+        acc[cycle[j % len(cycle)]].append(v)
+    return {n: sum(v) / len(v) for n, v in acc.items()}
+
+
 def traffic(workload, fetch_db, write_db, copy_fetch_db, copy_write_db, copy_bytes):
     """Measured HBM bytes per launch for every kernel of the workload's launch plan:
     a counter row matches a planned launch by kernel family and grid size (by family
@@ -97,21 +123,25 @@ def traffic(workload, fetch_db, write_db, copy_fetch_db, copy_write_db, copy_byt
     out = {}
     got = collections.defaultdict(dict)
     allc = baseline_cases()
+    # launches of one family with one grid size (two levels' kernels) share a counter
+    # row, which averages them: they are told apart by dispatch order below
+    shared = collections.defaultdict(list)
     for name in bench.WORKLOADS[workload]:
         c = allc[name]
         desc = wt.make_desc(c.n, c.c, c.h, c.w, c.k, c.levels, bench.DTYPE_CODE[c.dtype])
         plan = [e for op in (wt.OP_FORWARD, wt.OP_BACKWARD_INPUT, wt.OP_BACKWARD_WEIGHT)
                 for e in wt.wtconv_plan_launches(desc, op)]
-        # launches of one family with one grid size (two levels' kernels) share a
-        # counter row, which averages them: such launches get no record
         names_at = collections.defaultdict(set)
         for e in plan:
             names_at[(e["name"].split("<")[0], e["workgroups"] * e["threads"])].add(e["name"])
         for e in plan:
             fam = e["name"].split("<")[0]
-            if len(names_at[(fam, e["workgroups"] * e["threads"])]) > 1:
+            fam = _SYMBOL_FAMILY.get(fam, fam)
+            grid = e["workgroups"] * e["threads"]
+            if len(names_at[(e["name"].split("<")[0], grid)]) > 1:
+                shared[(fam, grid)].append((name, e["name"]))
                 continue
-            match = rows.get((fam, e["workgroups"] * e["threads"]))
+            match = rows.get((fam, grid))
             if not match:
                 # A persistent kernel's grid follows the device's occupancy, which
                 # the host-side plan does not know: take the family's rows when
@@ -132,6 +162,27 @@ def traffic(workload, fetch_db, write_db, copy_fetch_db, copy_write_db, copy_byt
         fb = round(sum(r["fetch_bytes"] * r["dispatches"] for r in rs) / nd)
         wb = round(sum(r["write_bytes"] * r["dispatches"] for r in rs) / nd)
         out[name] = {"fetch_bytes": fb, "write_bytes": wb, "bytes": fb + wb, "variants": len(rs)}
+    for (fam, grid), launches in shared.items():
+        # only one layer's launches in the group: another layer's could interleave
+        if len({case for case, _ in launches}) > 1:
+            continue
+        if (fam, grid) not in rows:
+            # a persistent kernel (its grid follows the occupancy): the family's one
+            # grid, when no other group of the family claims it
+            grids = {g for (f, g) in rows if f == fam}
+            if len(grids) != 1 or sum(f == fam for f, _ in shared) > 1:
+                continue
+            grid = grids.pop()
+        cycle = [n for _, n in launches]
+        fr = _by_order(_sequence(fetch_db, "FETCH_SIZE", fam, grid), cycle)
+        wr = _by_order(_sequence(write_db, "WRITE_SIZE", fam, grid), cycle)
+        if fr is None or wr is None:
+            continue
+        for n in fr:
+            fb = round(fr[n] * 1024 * rec["fetch_scale"])
+            wb = round(wr[n] * 1024 * rec["write_scale"])
+            out[n] = {"fetch_bytes": fb, "write_bytes": wb, "bytes": fb + wb, "variants": 1,
+                      "matched_by": "dispatch order"}
     return {"workload": workload, "source_digest": bench.source_digest(),
             "fetch_scale": rec["fetch_scale"], "write_scale": rec["write_scale"], "kernels": out}
 
